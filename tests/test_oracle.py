@@ -1,0 +1,369 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Each test ties one part of the oracle to a library routine, a closed form, an
+invariant, 50-digit brute force, or the accuracy table printed on the pages,
+so that a dropped term, a wrong sign or index, or a transposed operand in the
+oracle fails at least one of them.
+"""
+import json
+import math
+import os
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from scipy.special import logsumexp
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _problem(seed, BT, V, weighted=False, ignore_frac=0.0, sigma=1.0, dyadic=False):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((BT, V)) * sigma
+    if dyadic:  # values that a bf16 buffer could hold, so shifts by 2^k stay exact
+        x = np.round(x * 64) / 64
+    t = rng.integers(0, V, BT).astype(np.int64)
+    if ignore_frac:
+        t[rng.permutation(BT)[: int(round(ignore_frac * BT))]] = -100
+    w = rng.uniform(0.5, 1.5, V) if weighted else None
+    return x, t, w
+
+
+# ---------------------------------------------------------------- library routines
+
+def test_unsmoothed_loss_is_logsumexp_minus_target_logit():
+    x, t, _ = _problem(1, 32, 257, sigma=3.0)
+    r = oracle.rows(x, t, want_grad=False)
+    expect = logsumexp(x, axis=1) - x[np.arange(32), t]
+    np.testing.assert_allclose(r.loss, expect, rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+@pytest.mark.parametrize("eps", [0.0, 0.1, 0.7])
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_matches_torch_cross_entropy_fp64(weighted, eps, reduction):
+    x, t, w = _problem(2, 24, 97, weighted=weighted, ignore_frac=0.25, sigma=2.0)
+    go = np.linspace(0.3, 1.7, 24) if reduction == "none" else 0.37
+    res = oracle.cross_entropy(x, t, w, -100, eps, reduction, go)
+
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    wt = None if w is None else torch.tensor(w, dtype=torch.float64)
+    lt = F.cross_entropy(xt, torch.tensor(t), weight=wt, ignore_index=-100,
+                         reduction=reduction, label_smoothing=eps)
+    lt.backward(torch.tensor(go, dtype=torch.float64) if reduction == "none"
+                else torch.tensor(go, dtype=torch.float64))
+    np.testing.assert_allclose(np.asarray(res.loss), lt.detach().numpy(), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(res.grad, xt.grad.numpy(), rtol=1e-10, atol=1e-15)
+
+
+def test_two_classes_is_the_logistic_loss():
+    x, t, _ = _problem(3, 50, 2, sigma=4.0)
+    r = oracle.rows(x, t, want_grad=False)
+    other = x[np.arange(50), 1 - t]
+    np.testing.assert_allclose(r.loss, np.logaddexp(0.0, other - x[np.arange(50), t]), rtol=1e-13)
+
+
+def test_stats_and_argmax_match_numpy():
+    x, t, w = _problem(4, 40, 301, weighted=True, sigma=2.0, dyadic=True)
+    x[5, 17] = x[5, 200] = x[5].max() + 1.0        # a tie for the max: first index wins
+    x[6, :] = 0.25                                  # every class ties
+    r = oracle.rows(x, t, w, label_smoothing=0.2, want_grad=False)
+    np.testing.assert_array_equal(r.argmax, np.argmax(x, axis=1))
+    np.testing.assert_array_equal(r.stats[:, 0], x.max(axis=1))
+    lse = logsumexp(x, axis=1)
+    np.testing.assert_allclose(r.stats[:, 1], np.exp(lse - x.max(axis=1)) - 1.0, rtol=1e-12)
+    np.testing.assert_array_equal(r.stats[:, 2], x[np.arange(40), t])
+    np.testing.assert_allclose(r.stats[:, 3], x @ w, rtol=1e-12)
+    r0 = oracle.rows(x, t, w, label_smoothing=0.0, want_grad=False)
+    assert np.all(r0.stats[:, 3] == 0.0)
+
+
+def test_token_accuracy_brute_force_with_ties():
+    x, t, _ = _problem(5, 60, 11, ignore_frac=0.2, dyadic=True)
+    x = np.floor(x * 2) / 2                         # coarse values: many ties
+    t[:10] = np.argmax(x[:10], axis=1)              # some hits for sure
+    res = oracle.cross_entropy(x, t, reduction="mean")
+    hits, valid = 0, 0
+    for n in range(60):
+        if t[n] == -100:
+            assert res.acc[n] == 0
+            continue
+        valid += 1
+        best = 0
+        for c in range(11):
+            if x[n, c] > x[n, best]:
+                best = c
+        assert res.acc[n] == (1.0 if best == t[n] else 0.0)
+        hits += best == t[n]
+    assert res.acc_mean == hits / valid
+
+
+# ---------------------------------------------------------------- brute force, 50 digits
+
+def _mp_loss(xrow, y, w, eps):
+    mpmath.mp.dps = 50
+    V = len(xrow)
+    w = [mpmath.mpf(1)] * V if w is None else [mpmath.mpf(float(v)) for v in w]
+
+    def f(*xs):
+        lse = mpmath.log(mpmath.fsum(mpmath.exp(v) for v in xs))
+        s = mpmath.fsum(w[c] * (lse - xs[c]) for c in range(V))
+        return (1 - mpmath.mpf(eps)) * w[y] * (lse - xs[y]) + mpmath.mpf(eps) / V * s
+    return f
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("weighted,eps", [(False, 0.0), (False, 0.3), (True, 0.0), (True, 0.15)])
+def test_brute_force_loss_and_derivative(V, weighted, eps):
+    x, t, w = _problem(10 + V, 3, V, weighted=weighted, sigma=3.0)
+    r = oracle.rows(x, t, w, label_smoothing=eps)
+    for n in range(3):
+        f = _mp_loss(x[n], int(t[n]), w, eps)
+        pt = [mpmath.mpf(float(v)) for v in x[n]]
+        assert float(r.loss[n]) == pytest.approx(float(f(*pt)), rel=1e-13, abs=1e-15)
+        for c in range(V):
+            d = [0] * V
+            d[c] = 1
+            g = mpmath.diff(f, pt, tuple(d))
+            assert float(r.grad[n, c]) == pytest.approx(float(g), rel=1e-11, abs=1e-14)
+
+
+def test_confident_rows_keep_d_prime_and_dxy_precision():
+    """A dominant class: d' from 1e-2 down to 1e-9 must hold ~1e-12 relative,
+    and so must dx_y = p_y - 1 (the cancellation the pages are about)."""
+    mpmath.mp.dps = 50
+    rng = np.random.default_rng(6)
+    V = 64
+    for gap in (5.0, 10.0, 15.0, 25.0):
+        x = rng.standard_normal(V)
+        y = 7
+        x[y] = x.max() + gap
+        r = oracle.rows(x[None, :], np.array([y]))
+        mx = [mpmath.mpf(float(v)) for v in x]
+        dp = mpmath.fsum(mpmath.exp(v - mx[y]) for i, v in enumerate(mx) if i != y)
+        dxy = -dp / (1 + dp)
+        assert float(r.stats[0, 1]) == pytest.approx(float(dp), rel=1e-12)
+        assert float(r.grad[0, y]) == pytest.approx(float(dxy), rel=1e-12)
+        assert float(r.loss[0]) == pytest.approx(float(mpmath.log1p(dp)), rel=1e-12)
+
+
+# ---------------------------------------------------------------- finite differences of the reduced loss
+
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+@pytest.mark.parametrize("weighted,eps", [(False, 0.0), (True, 0.2)])
+def test_scaled_gradient_is_derivative_of_reduced_loss(reduction, weighted, eps):
+    x, t, w = _problem(7, 5, 6, weighted=weighted, ignore_frac=0.2)
+    go = np.array([0.5, 1.5, -0.7, 2.0, 0.3]) if reduction == "none" else 0.37
+    res = oracle.cross_entropy(x, t, w, -100, eps, reduction, go)
+
+    def J(xx):
+        r = oracle.cross_entropy(xx, t, w, -100, eps, reduction, go, want_grad=False)
+        return float(np.dot(go, r.loss)) if reduction == "none" else go * r.loss
+    h = 1e-6
+    fd = np.zeros_like(x)
+    for n in range(5):
+        for c in range(6):
+            xp = x.copy()
+            xm = x.copy()
+            xp[n, c] += h
+            xm[n, c] -= h
+            fd[n, c] = (J(xp) - J(xm)) / (2 * h)
+    np.testing.assert_allclose(res.grad, fd, rtol=1e-7, atol=1e-9)
+
+
+# ---------------------------------------------------------------- closed forms and invariants
+
+@pytest.mark.parametrize("weighted,eps", [(False, 0.0), (False, 0.1), (True, 0.0), (True, 0.3)])
+def test_gradient_rows_sum_to_zero(weighted, eps):
+    x, t, w = _problem(8, 16, 513, weighted=weighted, sigma=2.0)
+    r = oracle.rows(x, t, w, label_smoothing=eps)
+    s = r.grad.sum(axis=1)
+    scale = np.abs(r.grad).sum(axis=1)
+    assert np.all(np.abs(s) <= 1e-13 * scale)
+
+
+@pytest.mark.parametrize("eps", [0.0, 0.1, 1.0])
+def test_uniform_logits_closed_form(eps):
+    V, BT = 1000, 8
+    x = np.full((BT, V), 0.75)
+    t = np.arange(BT) * 13
+    res = oracle.cross_entropy(x, t, label_smoothing=eps, reduction="mean")
+    assert res.loss == pytest.approx(math.log(V), rel=1e-14)
+    expect = np.full((BT, V), 1.0 / V - eps / V)
+    expect[np.arange(BT), t] -= 1.0 - eps
+    np.testing.assert_allclose(res.grad, expect / BT, rtol=1e-12, atol=1e-18)
+
+
+def test_one_class_has_zero_loss_and_gradient():
+    x = np.array([[3.0], [-2.0], [0.0]])
+    res = oracle.cross_entropy(x, np.zeros(3, np.int64), label_smoothing=0.1, reduction="none")
+    assert np.all(res.loss == 0.0)
+    assert np.all(res.grad == 0.0)
+
+
+def test_shift_by_power_of_two_changes_nothing():
+    x, t, w = _problem(9, 12, 129, weighted=True, dyadic=True)
+    a = oracle.cross_entropy(x, t, w, label_smoothing=0.1, reduction="none")
+    b = oracle.cross_entropy(x + 8.0, t, w, label_smoothing=0.1, reduction="none")
+    np.testing.assert_allclose(a.loss, b.loss, rtol=1e-13)
+    np.testing.assert_allclose(a.grad, b.grad, rtol=1e-12, atol=1e-17)
+
+
+def test_uniform_class_weights():
+    x, t, _ = _problem(10, 20, 50, ignore_frac=0.1)
+    w = np.full(50, 2.5)
+    plain_mean = oracle.cross_entropy(x, t, None, label_smoothing=0.1, reduction="mean")
+    wmean = oracle.cross_entropy(x, t, w, label_smoothing=0.1, reduction="mean")
+    plain_sum = oracle.cross_entropy(x, t, None, label_smoothing=0.1, reduction="sum")
+    wsum = oracle.cross_entropy(x, t, w, label_smoothing=0.1, reduction="sum")
+    assert wmean.loss == pytest.approx(plain_mean.loss, rel=1e-13)
+    assert wsum.loss == pytest.approx(2.5 * plain_sum.loss, rel=1e-13)
+    np.testing.assert_allclose(wmean.grad, plain_mean.grad, rtol=1e-12, atol=1e-18)
+
+
+def test_ignored_rows_and_normalizer():
+    x, t, w = _problem(11, 30, 40, weighted=True, ignore_frac=0.3)
+    t[t == -100] = 5  # ignore_index inside [0, V) still ignores
+    t[3] = 5
+    res = oracle.cross_entropy(x, t, w, ignore_index=5, label_smoothing=0.1, reduction="mean")
+    ign = t == 5
+    assert np.all(res.row_loss[ign] == 0.0) and np.all(res.grad[ign] == 0.0)
+    valid = (~ign)
+    assert res.norm.n_valid == int(valid.sum())
+    assert res.norm.W == pytest.approx(float(w[t[valid]].sum()), rel=1e-14)
+    assert res.norm.sum_w == pytest.approx(float(w.sum()), rel=1e-14)
+    assert res.loss == pytest.approx(float(res.row_loss.sum() / w[t[valid]].sum()), rel=1e-13)
+
+
+def test_all_rows_ignored_mean_is_nan_with_zero_gradient():
+    x, _, _ = _problem(12, 6, 10)
+    t = np.full(6, -100)
+    res = oracle.cross_entropy(x, t, reduction="mean")
+    assert math.isnan(res.loss)
+    assert np.all(res.grad == 0.0)
+    xt = torch.tensor(x, requires_grad=True)
+    assert math.isnan(float(F.cross_entropy(xt, torch.tensor(t), reduction="mean").detach()))
+
+
+def test_invalid_target_gives_nan_loss_zero_gradient():
+    x, t, _ = _problem(13, 5, 10)
+    t[2] = 10
+    t[4] = -3
+    res = oracle.cross_entropy(x, t, reduction="none")
+    assert math.isnan(res.row_loss[2]) and math.isnan(res.row_loss[4])
+    assert np.all(res.grad[[2, 4]] == 0.0)
+    assert res.norm.n_invalid == 2 and res.norm.n_valid == 3
+    assert math.isnan(oracle.cross_entropy(x, t, reduction="sum").loss)
+
+
+def test_nan_logit_reaches_loss_and_gradient():
+    x, t, _ = _problem(14, 3, 10)
+    x[1, 4] = np.nan
+    res = oracle.cross_entropy(x, t, reduction="none")
+    assert math.isnan(res.row_loss[1]) and np.all(np.isnan(res.grad[1]))
+    assert np.all(np.isfinite(res.row_loss[[0, 2]]))
+
+
+# ---------------------------------------------------------------- rounding to the buffer type
+
+def _exact_rne(v, p, emin, emax):
+    """Round-to-nearest-even with exact rational arithmetic (Python's round()
+    on a Fraction rounds half to even)."""
+    from fractions import Fraction
+    if v == 0 or not math.isfinite(v):
+        return v
+    f = Fraction(v)
+    e = math.floor(math.log2(abs(v)))
+    while Fraction(2) ** e > abs(f):
+        e -= 1
+    while Fraction(2) ** (e + 1) <= abs(f):
+        e += 1
+    e = max(e, emin)
+    q = Fraction(2) ** (e - p + 1)
+    r = round(f / q) * q
+    mx = (2 - Fraction(2) ** (1 - p)) * Fraction(2) ** emax
+    if abs(r) > mx:
+        return math.copysign(math.inf, v)
+    return float(r)
+
+
+def _rounding_cases(seed):
+    rng = np.random.default_rng(seed)
+    mags = np.exp2(rng.uniform(-140, 130, 4000))
+    vals = mags * rng.choice([-1.0, 1.0], 4000) * (1 + rng.uniform(0, 1, 4000))
+    # exact halfway points of bf16 and fp16 and values next to them
+    base = rng.integers(1 << 7, 1 << 8, 200).astype(np.float64) * np.exp2(rng.integers(-20, 20, 200))
+    half_bf16 = base + 0.5 * np.exp2(np.floor(np.log2(base)) - 7)
+    half_f16 = base + 0.5 * np.exp2(np.floor(np.log2(base)) - 10)
+    edge = np.array([65504.0, 65519.99, 65520.0, 3.3895313892515355e38, 3.3961775292304e38,
+                     2.0 ** -133, 2.0 ** -134, 1.5 * 2.0 ** -134, 2.0 ** -24, 2.0 ** -25,
+                     3.0 * 2.0 ** -26, 1e-45, 0.0, -0.0])
+    return np.concatenate([vals, half_bf16, half_f16, np.nextafter(half_bf16, 0), edge])
+
+
+def test_rounding_to_f32_matches_the_c_cast():
+    v = _rounding_cases(20)
+    with np.errstate(over="ignore"):
+        np.testing.assert_array_equal(oracle.round_to(v, "f32"), v.astype(np.float32).astype(np.float64))
+
+
+def test_rounding_to_f16_matches_numpy():
+    v = _rounding_cases(21)
+    with np.errstate(over="ignore"):
+        np.testing.assert_array_equal(oracle.round_to(v, "f16"), v.astype(np.float16).astype(np.float64))
+
+
+def test_rounding_to_bf16_matches_torch_and_exact_rationals():
+    v = _rounding_cases(22)
+    with np.errstate(over="ignore"):
+        f32 = v.astype(np.float32)
+    from_torch = torch.from_numpy(f32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.round_to(f32.astype(np.float64), "bf16"), from_torch)
+    exact = np.array([_exact_rne(float(a), 8, -126, 127) for a in v])
+    np.testing.assert_array_equal(oracle.round_to(v, "bf16"), exact)
+
+
+# ---------------------------------------------------------------- the pages' accuracy table
+
+def test_reproduces_the_dxy_accuracy_table():
+    """The table of maximum dx_y relative error (bf16, V=32000): an fp32
+    evaluation rounded once stays under 0.5%, while the read-modify-write of
+    the bf16 buffer reaches ~2%, ~20% and 100% at softmax(target) 0.9, 0.99,
+    0.999.  Measured against the oracle's fp64 dx_y, on the confidence
+    workload's recipe.  The row count is a power of two: the table's 1.95% at
+    0.9 is exactly half a bf16 ulp of 0.9/N over 0.1/N (2^-9 / 0.1), which
+    holds when N is a power of two; the pages do not state N."""
+    with open(os.path.join(GOLDEN, "dxy_accuracy_table.json")) as fh:
+        table = json.load(fh)
+    wl = workloads.with_rows(workloads.WORKLOADS["confidence"], 2048)
+    t = workloads.targets(wl)
+    xb = workloads.logits(wl, t)
+    x = workloads.as_f64(xb)
+    N = wl.BT
+    res = oracle.cross_entropy(x, t, reduction="mean", dtype="bf16")
+    rows = np.arange(N)
+    exact = res.grad[rows, t]
+
+    # fp32 evaluation from the live max, sum and target logit, one rounding
+    x32 = x.astype(np.float32)
+    m = x32.max(axis=1)
+    d = np.exp(x32 - m[:, None]).sum(axis=1, dtype=np.float32)
+    py = np.exp(x32[rows, t] - m) / d
+    fold = oracle.round_to((py - np.float32(1)) / np.float32(N), "bf16")
+    # read-modify-write: softmax/N rounded into the bf16 buffer, then -1/N added
+    stored = oracle.round_to((py / np.float32(N)).astype(np.float32), "bf16")
+    rmw = oracle.round_to((stored.astype(np.float32) - np.float32(1.0 / N)).astype(np.float64), "bf16")
+
+    level = np.arange(N) % 3
+    for i, (p, before, at, _torch) in enumerate(table["rows"]):
+        sel = level == i
+        e_fold = np.max(np.abs(fold[sel] - exact[sel]) / np.abs(exact[sel])) * 100
+        e_rmw = np.max(np.abs(rmw[sel] - exact[sel]) / np.abs(exact[sel])) * 100
+        assert e_fold <= 0.5, (p, e_fold)
+        assert e_fold == pytest.approx(before, abs=0.15), (p, e_fold, before)
+        assert e_rmw == pytest.approx(at, rel=0.15), (p, e_rmw, at)
