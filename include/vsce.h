@@ -1,0 +1,212 @@
+/*
+ * vsce.h -- C ABI of the fused large-vocabulary softmax cross-entropy
+ * (libvsce.so, HIP for MI355X / gfx950).
+ *
+ * For each row n of a [rows, vocab] logits matrix x with target y[n] the
+ * library computes, in one pass over the row,
+ *   m = max_c x[c], d' = sum_{c != first argmax} exp(x[c] - m), x[y], and
+ *   S = sum_c w[c] x[c] (only needed under label smoothing),
+ * from them the row loss
+ *   l = (1 - eps) w[y] (lse - x[y]) + (eps / V) sum_c w[c] (lse - x[c]),
+ *   lse = m + log1p(d'),
+ * its none / sum / mean reduction (mean divides by W = sum of w[y] over rows
+ * whose target is not ignored), the token accuracy, and the logits gradient
+ *   g[c] = sigma (p[c] ((1 - eps) w[y] + (eps / V) sum_k w[k]) - (eps / V) w[c]
+ *                 - (1 - eps) w[y] [c == y]),   p = softmax(x),
+ * computed in fp32 and rounded once to the buffer type.  The true-class term
+ * is evaluated once per row from the live m, d' and x[y] and written with a
+ * single store (no per-element compare, no read-modify-write).
+ *
+ * Sources (page titles and sections):
+ *  - Liger-Kernel PR #1268 "perf(ce): single-shot dx_y gradient correction":
+ *    the pass-2 gradient hunks, the O(1) true-class correction, and the
+ *    embedded commit message of linkedin#1329 (recompute dx_y in fp32 from
+ *    the live target logit, max and sum, one store); the embedded commit
+ *    message of linkedin#1290 ("The optimization: CE backward memory parity":
+ *    scale the saved gradient in place through a raw element-wise kernel).
+ *  - Liger-Kernel PR #1622 "perf(flce): drop host syncs that do not feed the
+ *    computation", Summary: count / target-weight sum for mean, class-weight
+ *    sum times eps = label_smoothing / V, accuracy divided by the count on the
+ *    device, grad_output == 1.0 checked on the device (SKIP_IF_ONE).
+ *  - TransformerEngine PR #2325 "change fused cross entropy backward grad to
+ *    fp32 and reduce one read/write", Greptile summary and sequence diagram:
+ *    the forward saves per-row (max, sum, target logit, scaled_x_sum) and the
+ *    backward recomputes the gradient in fp32 from them.
+ *
+ * Conventions for every entry point:
+ *  - Every pointer argument is caller-owned DEVICE memory unless stated
+ *    otherwise; the problem and output descriptors themselves are host
+ *    structs read during the call only.
+ *  - The library allocates no memory, never synchronizes the stream or the
+ *    device, and never reads device data on the host: all work is enqueued on
+ *    `stream` (NULL = the null stream) and the call returns at once.
+ *  - Return codes: VSCE_OK (work enqueued), VSCE_ERR_INVALID (an argument is
+ *    out of its documented domain; nothing was enqueued),
+ *    VSCE_ERR_UNSUPPORTED (a valid combination this build does not handle;
+ *    nothing enqueued), VSCE_ERR_LAUNCH (a kernel launch failed).
+ *  - Data-dependent errors (a target neither equal to ignore_index nor in
+ *    [0, vocab)) are not return codes: the row gets a NaN loss and a zero
+ *    gradient, is left out of W and of the valid count, and bit
+ *    VSCE_STATUS_BAD_TARGET is set in the workspace status word, which the
+ *    caller may read whenever it chooses.
+ *  - Calls are reentrant; the library keeps no mutable global state.  Two
+ *    calls that share a workspace must be ordered on one stream.
+ */
+#ifndef VSCE_H
+#define VSCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of the logits / gradient buffer. */
+typedef enum vsce_dtype { VSCE_F32 = 0, VSCE_BF16 = 1, VSCE_F16 = 2 } vsce_dtype;
+
+/* Reduction of the per-row losses (PyTorch's names). */
+typedef enum vsce_reduction {
+  VSCE_REDUCTION_NONE = 0,
+  VSCE_REDUCTION_MEAN = 1,
+  VSCE_REDUCTION_SUM = 2
+} vsce_reduction;
+
+enum {
+  VSCE_OK = 0,
+  VSCE_ERR_INVALID = -1,
+  VSCE_ERR_UNSUPPORTED = -2,
+  VSCE_ERR_LAUNCH = -3
+};
+
+/* Bits of the workspace status word. */
+#define VSCE_STATUS_BAD_TARGET 1u
+
+/* Floats per row of the saved statistics: (m, d', x[y], S); S = 0 when
+   label_smoothing == 0; d' = d - 1 (the sum with the first maximum left out). */
+#define VSCE_STATS_STRIDE 4
+
+/*
+ * Workspace: caller-allocated device memory of vsce_workspace_bytes(rows)
+ * bytes, 256-byte aligned.  Its first 256 bytes are a header the forward
+ * writes and the backward reads (so a forward and its backward must get the
+ * same workspace); its contents need no initialisation.  Header fields, at
+ * these byte offsets:
+ */
+#define VSCE_WS_W 0          /* double: W, target-weight sum over valid rows  */
+#define VSCE_WS_SUM_W 8      /* double: class-weight sum (vocab if unweighted) */
+#define VSCE_WS_N_VALID 16   /* int64: rows whose target is in [0, vocab)     */
+#define VSCE_WS_N_INVALID 24 /* int64: rows with a bad target                 */
+#define VSCE_WS_STATUS 32    /* uint32: VSCE_STATUS_* bits of the last forward */
+#define VSCE_WS_HEADER_BYTES 256
+
+/* Bytes of workspace a problem with `rows` rows needs (0 if rows < 0). */
+size_t vsce_workspace_bytes(int64_t rows);
+
+/*
+ * The problem: one [rows, vocab] matrix and its targets.
+ *  rows            BT >= 0 (0 is allowed: nothing to do but the reduction)
+ *  vocab           V >= 1
+ *  row_stride      elements between the starts of consecutive rows, >= vocab
+ *  dtype           vsce_dtype of the logits / gradient buffer
+ *  reduction       vsce_reduction
+ *  target          [rows] int64 class ids (device)
+ *  class_weight    [vocab] fp32 weights (device) or NULL for all ones
+ *  ignore_index    target value of rows to ignore (PyTorch default -100); it
+ *                  is tested before the range check, so it may lie in [0, V)
+ *  label_smoothing eps in [0, 1]
+ */
+typedef struct vsce_problem {
+  int64_t rows;
+  int64_t vocab;
+  int64_t row_stride;
+  int32_t dtype;
+  int32_t reduction;
+  const int64_t *target;
+  const float *class_weight;
+  int64_t ignore_index;
+  float label_smoothing;
+  int32_t reserved; /* must be 0 */
+} vsce_problem;
+
+/*
+ * Forward outputs (all device fp32):
+ *  loss       required; [1] for mean and sum, [rows] for none.  A mean over
+ *             zero valid rows is NaN; a bad target makes the reduced loss NaN.
+ *  row_loss   optional [rows]: the unreduced per-row loss (0 for ignored rows).
+ *  token_acc  optional [rows]: 1 where the row is valid and the first index of
+ *             its maximum equals the target, else 0.
+ *  acc_mean   optional [1]: the mean of token_acc over valid rows (NaN if none).
+ */
+typedef struct vsce_outputs {
+  float *loss;
+  float *row_loss;
+  float *token_acc;
+  float *acc_mean;
+} vsce_outputs;
+
+/*
+ * Fused forward + gradient, in place (Liger-Kernel PR #1268 pass 1 / pass 2
+ * with the linkedin#1329 fp32 true-class fold; PR #1622 device-side
+ * normalizers).  Reads every valid row once, writes the loss outputs, and
+ * overwrites `logits_inout` (a [rows, row_stride] buffer of `dtype`) with the
+ * gradient of the reduced loss for grad_output = 1: sigma = 1/W for mean, 1
+ * for sum and none.  Ignored and bad-target rows are overwritten with zeros.
+ * Columns in [vocab, row_stride) are neither read nor written.  Apply a
+ * grad_output other than 1 afterwards with ce_scale_grad.
+ */
+int ce_forward_fused_inplace(const vsce_problem *problem, void *logits_inout,
+                             const vsce_outputs *out, void *workspace,
+                             hipStream_t stream);
+
+/*
+ * Split forward (TransformerEngine PR #2325 online_softmax_kernel +
+ * cross_entropy_forward_kernel): reads the logits once and writes the loss
+ * outputs and `stats` ([rows][VSCE_STATS_STRIDE] fp32: m, d', x[y], S; rows
+ * that are not valid get zeros).  The logits are not modified.
+ */
+int ce_forward_stats(const vsce_problem *problem, const void *logits,
+                     float *stats, const vsce_outputs *out, void *workspace,
+                     hipStream_t stream);
+
+/*
+ * Split backward (TransformerEngine PR #2325 cross_entropy_backward_kernel):
+ * from the logits and the saved stats, writes grad = RN(sigma * go[n] *
+ * dl_n/dx) in fp32 with one rounding, with the true-class term folded in
+ * fp32.  `grad` (a [rows, row_stride] buffer of `dtype`) may equal `logits`
+ * (in place) but must not otherwise overlap it.  grad_output is fp32 device
+ * memory: one value read at grad_output[0] when grad_output_stride == 0 (mean,
+ * sum), or [rows] values at grad_output[n * grad_output_stride] when it is 1
+ * (none).  `workspace` must be the one the matching ce_forward_stats wrote.
+ * Ignored and bad-target rows get zeros.
+ */
+int ce_backward_from_stats(const vsce_problem *problem, const void *logits,
+                           void *grad, const float *stats,
+                           const float *grad_output, int64_t grad_output_stride,
+                           const void *workspace, hipStream_t stream);
+
+/*
+ * Scale a gradient in place by grad_output (linkedin#1290 element-wise
+ * in-place scale; PR #1622 SKIP_IF_ONE): g <- RN(g * go[n]), with go read on
+ * the device at grad_output[n * grad_output_stride] (stride 0: one scalar,
+ * stride 1: per row).  Rows whose go equals 1.0 exactly are left untouched
+ * when skip_if_one != 0, so the call costs one launch when go == 1.
+ */
+int ce_scale_grad(void *grad, int64_t rows, int64_t vocab, int64_t row_stride,
+                  int32_t dtype, const float *grad_output,
+                  int64_t grad_output_stride, int32_t skip_if_one,
+                  hipStream_t stream);
+
+/* Human-readable name of a return code (static string). */
+const char *vsce_strerror(int code);
+
+/* Library version, as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int vsce_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSCE_H */

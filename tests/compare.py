@@ -1,0 +1,96 @@
+"""Comparators of GPU results against the oracle (test infrastructure).
+
+Gradients: an element passes if it is within one unit in the last place of
+the buffer type of the oracle's exact value rounded once to that type
+(``strict``), or, where the gradient is a difference of nearly equal terms
+(label smoothing, fp32 buffers), within the error of evaluating that
+difference in fp32 (``floor``):
+    |g - g64| <= 2^-24 (|x_c - lse| + log2 V + 8) sigma (p_c |A| + eta |w_c|
+                 + (1 - eps) w_y [c == y])
+The strict fraction must be 1 for bf16/fp16 buffers without label smoothing;
+the floored fraction must be 1 everywhere.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+import oracle
+
+# (significand bits, minimum normal exponent) per buffer type
+FORMATS = {"f32": (24, -126), "bf16": (8, -126), "f16": (11, -14)}
+
+
+def ulp(v: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the buffer type at |v| (the subnormal spacing near 0)."""
+    p, emin = FORMATS[dtype]
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, emin)
+    return np.exp2(e - (p - 1))
+
+
+@dataclass
+class GradReport:
+    n: int
+    strict_fail: int
+    floor_fail: int
+    max_ulp: float
+
+    @property
+    def strict_frac(self) -> float:
+        return 1.0 - self.strict_fail / max(self.n, 1)
+
+
+def grad_report(g: np.ndarray, g64: np.ndarray, dtype: str, x: np.ndarray, target: np.ndarray,
+                stats: np.ndarray, cls: np.ndarray, scale: np.ndarray, eps: float,
+                weight=None, sum_w=None) -> GradReport:
+    """g: GPU gradient (fp64 copy), g64: oracle exact scaled gradient, rows
+    aligned; x: logits; stats: oracle (m, d', x_y, S); scale: per-row sigma."""
+    g = np.asarray(g, dtype=np.float64)
+    rn = oracle.round_to(g64, dtype)
+    u = ulp(rn, dtype)
+    diff = np.abs(g - rn)
+    # NaN where the oracle has NaN is a match
+    both_nan = np.isnan(g) & np.isnan(g64)
+    strict = (diff <= u) | both_nan
+    n, V = g.shape
+    w = np.ones(V) if weight is None else np.asarray(weight, np.float64)
+    sw = float(V) if sum_w is None else float(sum_w)
+    eta = eps / V
+    floor_ok = strict.copy()
+    bad_rows = np.where(~strict.all(axis=1))[0]
+    for r in bad_rows:
+        if cls[r] != 0:
+            continue
+        m, dp = stats[r, 0], stats[r, 1]
+        lse = m + math.log1p(dp)
+        p = np.exp(x[r] - lse)
+        y = int(target[r])
+        wy = w[y]
+        A = (1 - eps) * wy + eta * sw
+        mag = p * abs(A) + eta * np.abs(w)
+        mag[y] += (1 - eps) * wy
+        tol = 2.0 ** -24 * (np.abs(x[r] - lse) + math.log2(V) + 8) * abs(scale[r]) * mag
+        floor_ok[r] |= np.abs(g[r] - g64[r]) <= tol + u[r]
+    with np.errstate(invalid="ignore"):
+        units = np.where(u > 0, diff / u, 0.0)
+    units = np.where(both_nan, 0.0, units)
+    return GradReport(int(g.size), int((~strict).sum()), int((~floor_ok).sum()),
+                      float(np.nanmax(units)) if units.size else 0.0)
+
+
+def rel_err(a, b) -> np.ndarray:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        e = np.abs(a - b) / np.maximum(np.abs(b), 1e-30)
+    return np.where(np.isnan(a) & np.isnan(b), 0.0, e)
+
+
+def assert_loss_close(gpu, ref, rtol=1e-5, what="loss"):
+    e = rel_err(gpu, ref)
+    assert np.all(e <= rtol), f"{what}: max relative error {np.nanmax(e):.3e} > {rtol:g}"

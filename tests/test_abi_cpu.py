@@ -1,0 +1,152 @@
+"""The C ABI on the host: the library loads, exports what include/vsce.h
+declares, and rejects invalid arguments before any HIP call (CPU only: no
+call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import vocab_softmax_cross_amd._lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vsce.h")
+
+FAKE = 0x10000  # a 256-byte-aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\([^;{]*\)\s*;", text, flags=re.M)
+    return sorted(set(n for n in names if not n.startswith("__")))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("ce_forward_fused_inplace", "ce_forward_stats", "ce_backward_from_stats",
+              "ce_scale_grad", "vsce_workspace_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(declared_functions()) == set(L.EXPORTS)
+
+
+def test_version_and_workspace_size():
+    assert L.vsce_version() >= 100
+    assert L.vsce_workspace_bytes(-1) == 0
+    assert L.vsce_workspace_bytes(0) == L.WS_HEADER_BYTES
+    assert L.vsce_workspace_bytes(1) == L.WS_HEADER_BYTES + 2 * 256
+    assert L.vsce_workspace_bytes(8192) == L.WS_HEADER_BYTES + 2 * 8192 * 4
+
+
+def test_struct_layout_matches_the_header():
+    assert ctypes.sizeof(L.Problem) == 64
+    assert L.Problem.label_smoothing.offset == 56
+    assert ctypes.sizeof(L.Outputs) == 32
+
+
+def _problem(**kw):
+    p = L.Problem()
+    p.rows, p.vocab, p.row_stride = 8, 64, 64
+    p.dtype, p.reduction = L.BF16, L.REDUCTION_MEAN
+    p.target, p.class_weight = FAKE, None
+    p.ignore_index, p.label_smoothing, p.reserved = -100, 0.0, 0
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _outputs(loss=FAKE):
+    o = L.Outputs()
+    o.loss = loss
+    return o
+
+
+def _fused(p, logits=FAKE, out="default", ws=FAKE):
+    o = _outputs() if out == "default" else out
+    return L.raw_call("ce_forward_fused_inplace", None if p is None else ctypes.byref(p), logits,
+                      None if o is None else ctypes.byref(o), ws, None)
+
+
+def _stats(p, stats=FAKE, logits=FAKE, ws=FAKE):
+    return L.raw_call("ce_forward_stats", ctypes.byref(p), logits, stats,
+                      ctypes.byref(_outputs()), ws, None)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("rows", -1), ("vocab", 0), ("vocab", -3), ("row_stride", 63), ("dtype", 3), ("dtype", -1),
+    ("reduction", 3), ("reserved", 1), ("label_smoothing", -0.1), ("label_smoothing", 1.5),
+    ("label_smoothing", float("nan")), ("target", None),
+])
+def test_bad_problem_fields_are_rejected(field, value):
+    assert _fused(_problem(**{field: value})) == L.ERR_INVALID
+    assert _stats(_problem(**{field: value})) == L.ERR_INVALID
+
+
+def test_bad_pointers_are_rejected():
+    assert _fused(None) == L.ERR_INVALID
+    assert _fused(_problem(), logits=None) == L.ERR_INVALID
+    assert _fused(_problem(), logits=FAKE + 1) == L.ERR_INVALID      # bf16 needs 2-byte alignment
+    assert _fused(_problem(dtype=L.F32), logits=FAKE + 2) == L.ERR_INVALID
+    assert _fused(_problem(), out=None) == L.ERR_INVALID
+    assert _fused(_problem(), out=_outputs(loss=None)) == L.ERR_INVALID
+    assert _fused(_problem(), ws=None) == L.ERR_INVALID
+    assert _fused(_problem(), ws=FAKE + 8) == L.ERR_INVALID           # workspace: 256-byte aligned
+    assert _fused(_problem(class_weight=FAKE + 2)) == L.ERR_INVALID
+    assert _stats(_problem(), stats=None) == L.ERR_INVALID
+    assert _stats(_problem(), stats=FAKE + 4) == L.ERR_INVALID
+
+
+def test_unsupported_sizes():
+    assert _fused(_problem(vocab=1 << 30, row_stride=1 << 30)) == L.ERR_UNSUPPORTED
+    assert _fused(_problem(rows=1 << 31)) == L.ERR_UNSUPPORTED
+
+
+def _backward(p, grad=FAKE, stats=FAKE, go=FAKE, go_stride=0, ws=FAKE):
+    return L.raw_call("ce_backward_from_stats", ctypes.byref(p), FAKE, grad, stats, go, go_stride,
+                      ws, None)
+
+
+def test_backward_argument_checks():
+    assert _backward(_problem(), grad=None) == L.ERR_INVALID
+    assert _backward(_problem(), grad=FAKE + 1) == L.ERR_INVALID
+    assert _backward(_problem(), stats=None) == L.ERR_INVALID
+    assert _backward(_problem(), go=None) == L.ERR_INVALID
+    assert _backward(_problem(), go_stride=2) == L.ERR_INVALID
+    assert _backward(_problem(), ws=None) == L.ERR_INVALID
+    assert _backward(_problem(vocab=0)) == L.ERR_INVALID
+    # nothing to do for an empty batch: accepted without touching the GPU
+    assert _backward(_problem(rows=0), grad=None, stats=None, go=None) == L.OK
+
+
+def _scale(grad=FAKE, rows=4, vocab=64, stride=64, dtype=L.BF16, go=FAKE, go_stride=0):
+    return L.raw_call("ce_scale_grad", grad, rows, vocab, stride, dtype, go, go_stride, 1, None)
+
+
+def test_scale_argument_checks():
+    assert _scale(dtype=7) == L.ERR_INVALID
+    assert _scale(rows=-1) == L.ERR_INVALID
+    assert _scale(vocab=0) == L.ERR_INVALID
+    assert _scale(stride=10) == L.ERR_INVALID
+    assert _scale(go_stride=-1) == L.ERR_INVALID
+    assert _scale(grad=None) == L.ERR_INVALID
+    assert _scale(go=None) == L.ERR_INVALID
+    assert _scale(grad=FAKE + 1) == L.ERR_INVALID
+    assert _scale(rows=0, grad=None, go=None) == L.OK
+
+
+def test_strerror():
+    lib = L.load()
+    assert lib.vsce_strerror(L.ERR_INVALID) == b"invalid argument"
+    assert lib.vsce_strerror(12345) == b"unknown error"
+
+
+def test_binding_raises_on_error_codes():
+    with pytest.raises(L.VsceError) as e:
+        L.ce_forward_fused_inplace(_problem(vocab=0), FAKE, _outputs(), FAKE, 0)
+    assert e.value.code == L.ERR_INVALID

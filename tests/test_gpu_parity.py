@@ -1,0 +1,506 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on the GPU.
+
+Tolerances (from the method's stated targets):
+* losses (per row and reduced): 1e-5 relative (fp32 accumulation);
+* gradient: within 1 ulp of the oracle's value rounded once to the buffer
+  type; where label smoothing or an fp32 buffer makes the element a
+  difference of nearly equal terms, within the fp32 evaluation floor instead
+  (tests/compare.py) -- the strict fraction must be 1 for bf16 without
+  label smoothing;
+* true-class gradient in the confident regime: <= 0.5% relative;
+* split-mode statistics: m and x_y bit-equal, d' 1e-5 relative, S absolute
+  64 u sum|w x|.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.compare import assert_loss_close, grad_report, rel_err
+
+pytestmark = pytest.mark.gpu
+
+vf = pytest.importorskip("vocab_softmax_cross_amd.functional")
+
+
+def _note(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _go_tensor(go, reduction, rows, dev):
+    if reduction == "none":
+        return torch.full((rows,), go, dtype=torch.float32, device=dev)
+    return torch.tensor(go, dtype=torch.float32, device=dev)
+
+
+def run(wl, mode, reduction, go, accuracy=False, row_stride=None, check_rows=None,
+        x_host=None, tgt=None, inplace_backward=False):
+    """Runs one forward + backward through the C ABI and returns GPU results
+    (host copies) next to the oracle's."""
+    dev = _dev()
+    _note(f"{wl.name} BT={wl.BT} V={wl.V} {wl.dtype} mode={mode} red={reduction} go={go} "
+          f"stride={row_stride}")
+    tgt = W.targets(wl) if tgt is None else tgt
+    w = W.class_weights(wl)
+    x_host = W.logits(wl, tgt) if x_host is None else x_host
+    stride = row_stride or wl.V
+    buf = torch.zeros((wl.BT, stride), dtype=wl.torch_dtype, device=dev)
+    if stride > wl.V:
+        buf[:, wl.V:] = 7.0  # padding columns must survive untouched
+    x = buf[:, :wl.V]
+    x.copy_(x_host.to(dev))
+    t = torch.from_numpy(tgt).to(dev)
+    wt = None if w is None else torch.from_numpy(w).to(dev)
+    eps = wl.label_smoothing
+    go_t = _go_tensor(go, reduction, wl.BT, dev)
+    if mode == "fused":
+        res = vf.forward_fused_inplace(x, t, wt, -100, eps, reduction, row_loss=True,
+                                       accuracy=accuracy)
+        vf.scale_grad(x, go_t, reduction)
+        g = x
+        stats = None
+    else:
+        res = vf.forward_stats(x, t, wt, -100, eps, reduction, row_loss=True, accuracy=accuracy)
+        g = vf.backward_from_stats(x, t, res["stats"], go_t, res["workspace"], wt, -100, eps,
+                                   reduction, out=x if inplace_backward else None)
+        stats = res["stats"].cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    if stride > wl.V:
+        assert torch.all(buf[:, wl.V:] == 7.0), "padding columns were written"
+    out = {
+        "loss": res["loss"].cpu().numpy().astype(np.float64),
+        "row_loss": res["row_loss"].cpu().numpy().astype(np.float64),
+        "stats": stats,
+        "status": vf.status(res["workspace"]),
+        "acc": None if not accuracy else res["token_acc"].cpu().numpy().astype(np.float64),
+        "acc_mean": None if not accuracy else float(res["acc_mean"].cpu()),
+    }
+    rows = np.arange(wl.BT) if check_rows is None else np.asarray(check_rows)
+    out["grad"] = g[torch.from_numpy(rows).to(dev)].float().cpu().numpy().astype(np.float64) \
+        if len(rows) else np.zeros((0, wl.V))
+    return out, x_host, tgt, w
+
+
+def reference(wl, x_host, tgt, w, reduction, go, rows=None):
+    """Oracle over all rows (losses, stats) and the gradient of `rows`."""
+    BT = wl.BT
+    nz = oracle.normalizer(tgt, wl.V, w)
+    loss_rows = np.empty(BT)
+    stats = np.empty((BT, 4))
+    am = np.empty(BT, np.int64)
+    cls = np.empty(BT, np.int32)
+    chunk = max(1, (1 << 26) // wl.V)
+    for r0 in range(0, BT, chunk):
+        r1 = min(BT, r0 + chunk)
+        r = oracle.rows(W.as_f64(x_host[r0:r1]), tgt[r0:r1], w, -100, wl.label_smoothing,
+                        want_grad=False)
+        loss_rows[r0:r1], stats[r0:r1], am[r0:r1], cls[r0:r1] = r.loss, r.stats, r.argmax, r.cls
+    rows = np.arange(BT) if rows is None else np.asarray(rows)
+    scale = oracle.grad_scale(reduction, nz.W, go, BT)
+    g64 = np.zeros((len(rows), wl.V))
+    for i0 in range(0, len(rows), chunk):
+        sel = rows[i0:i0 + chunk]
+        r = oracle.rows(W.as_f64(x_host[torch.from_numpy(sel)]), tgt[sel], w, -100,
+                        wl.label_smoothing, want_grad=True)
+        gg = r.grad * scale[sel][:, None]
+        gg[r.cls != 0] = 0.0
+        g64[i0:i0 + len(sel)] = gg
+    acc, acc_mean = oracle.token_accuracy(am, tgt, cls)
+    return {
+        "loss": oracle.reduce_loss(loss_rows, cls, nz.W, reduction),
+        "row_loss": loss_rows, "stats": stats, "cls": cls, "norm": nz, "scale": scale,
+        "rows": rows, "grad": g64, "acc": acc, "acc_mean": acc_mean,
+    }
+
+
+def check(wl, out, ref, x_host, tgt, w, strict_bf16=None):
+    assert_loss_close(out["loss"], ref["loss"], 1e-5, "reduced loss")
+    assert_loss_close(out["row_loss"], ref["row_loss"], 1e-5, "row loss")
+    rows = ref["rows"]
+    rep = grad_report(out["grad"], ref["grad"], wl.dtype, W.as_f64(x_host[torch.from_numpy(rows)]),
+                      tgt[rows], ref["stats"][rows], ref["cls"][rows], ref["scale"][rows],
+                      wl.label_smoothing, w, ref["norm"].sum_w)
+    print(f"  grad: n={rep.n} strict_fail={rep.strict_fail} floor_fail={rep.floor_fail} "
+          f"max_ulp={rep.max_ulp:.2f}", flush=True)
+    assert rep.floor_fail == 0, rep
+    if strict_bf16 or (strict_bf16 is None and wl.dtype != "f32" and wl.label_smoothing == 0):
+        assert rep.strict_fail == 0, rep
+    if out["stats"] is not None:
+        valid = ref["cls"] == 0
+        s, r = out["stats"][valid], ref["stats"][valid]
+        np.testing.assert_array_equal(s[:, 0], r[:, 0])
+        np.testing.assert_array_equal(s[:, 2], r[:, 2])
+        assert np.all(rel_err(s[:, 1], r[:, 1]) <= 1e-5), np.max(rel_err(s[:, 1], r[:, 1]))
+        if wl.label_smoothing > 0:
+            xa = np.abs(W.as_f64(x_host[torch.from_numpy(np.where(valid)[0])]))
+            wa = np.ones(wl.V) if w is None else np.abs(w.astype(np.float64))
+            bound = 64 * 2.0 ** -24 * (xa @ wa)
+            assert np.all(np.abs(s[:, 3] - r[:, 3]) <= bound)
+        else:
+            assert np.all(s[:, 3] == 0.0)
+    if out["acc"] is not None:
+        np.testing.assert_array_equal(out["acc"], ref["acc"])
+        assert out["acc_mean"] == pytest.approx(ref["acc_mean"], rel=1e-6)
+    assert out["status"]["n_valid"] == ref["norm"].n_valid
+    assert out["status"]["n_invalid"] == ref["norm"].n_invalid
+    assert out["status"]["W"] == pytest.approx(ref["norm"].W, rel=1e-12)
+
+
+# ---------------------------------------------------------------- the workloads
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_tiny(mode):
+    wl = W.WORKLOADS["tiny"]
+    out, xh, tgt, w = run(wl, mode, "mean", 1.0, accuracy=True)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0), xh, tgt, w)
+
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_confidence_regime(mode):
+    """softmax(target) ~ 0.9 / 0.99 / 0.999 by row: dx_y within 0.5% of fp64."""
+    wl = W.WORKLOADS["confidence"]
+    rows = np.arange(0, wl.BT, 8)
+    out, xh, tgt, w = run(wl, mode, "mean", 1.0, check_rows=rows)
+    ref = reference(wl, xh, tgt, w, "mean", 1.0, rows)
+    check(wl, out, ref, xh, tgt, w)
+    gy = out["grad"][np.arange(len(rows)), tgt[rows]]
+    ry = ref["grad"][np.arange(len(rows)), tgt[rows]]
+    lvl = rows % 3
+    for i in range(3):
+        e = np.max(rel_err(gy[lvl == i], ry[lvl == i])) * 100
+        print(f"  dx_y max rel err level {i}: {e:.3f}%", flush=True)
+        assert e <= 0.5
+
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+@pytest.mark.parametrize("go", [1.0, 0.37])
+def test_llm_head_rows(mode, go):
+    """The headline row length (V = 128256, bf16, eps = 0.1, 5% ignored) on 96
+    rows, every gradient element checked."""
+    wl = W.with_rows(W.WORKLOADS["llm_head"], 96)
+    out, xh, tgt, w = run(wl, mode, "mean", go)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", go), xh, tgt, w)
+
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+@pytest.mark.parametrize("reduction", ["sum", "none"])
+def test_weighted_rows(mode, reduction):
+    wl = W.with_rows(W.WORKLOADS["weighted"], 64)
+    out, xh, tgt, w = run(wl, mode, reduction, 0.5)
+    check(wl, out, reference(wl, xh, tgt, w, reduction, 0.5), xh, tgt, w)
+
+
+@pytest.mark.parametrize("mode", ["split", "fused"])
+def test_wide_fp32_rows(mode):
+    """V = 256000 fp32 with dominant targets: the streaming kernels (the row
+    does not fit on chip), accuracy included."""
+    wl = W.with_rows(W.WORKLOADS["wide_fp32"], 40)
+    out, xh, tgt, w = run(wl, mode, "none", 1.0, accuracy=True)
+    check(wl, out, reference(wl, xh, tgt, w, "none", 1.0), xh, tgt, w)
+
+
+# ---------------------------------------------------------------- full sizes, sampled
+
+def _sample_rows(BT, k=24, seed=0):
+    r = np.random.default_rng(seed).choice(BT, size=k, replace=False)
+    return np.sort(np.concatenate([r, [0, BT - 1]]))
+
+
+@pytest.mark.parametrize("mode,go", [("fused", 1.0), ("split", 0.37)])
+def test_llm_head_full_size(mode, go):
+    """BT = 8192, V = 128256 bf16 in the launch configuration the benchmark
+    times: every row loss, the reduced loss and the statistics checked, the
+    gradient on sampled rows."""
+    wl = W.WORKLOADS["llm_head"]
+    rows = _sample_rows(wl.BT)
+    out, xh, tgt, w = run(wl, mode, "mean", go, check_rows=rows)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", go, rows), xh, tgt, w)
+
+
+@pytest.mark.parametrize("reduction", ["sum", "none"])
+def test_weighted_full_size(reduction):
+    wl = W.WORKLOADS["weighted"]
+    rows = _sample_rows(wl.BT, 16, 1)
+    out, xh, tgt, w = run(wl, "fused", reduction, 0.5, check_rows=rows)
+    check(wl, out, reference(wl, xh, tgt, w, reduction, 0.5, rows), xh, tgt, w)
+
+
+def test_wide_fp32_full_size():
+    wl = W.WORKLOADS["wide_fp32"]
+    rows = _sample_rows(wl.BT, 16, 2)
+    out, xh, tgt, w = run(wl, "split", "none", 1.0, accuracy=True, check_rows=rows)
+    check(wl, out, reference(wl, xh, tgt, w, "none", 1.0, rows), xh, tgt, w)
+
+
+# ---------------------------------------------------------------- edge cases
+
+def _small(name, BT, V, **kw):
+    base = W.WORKLOADS[name]
+    d = dict(base.__dict__)
+    d.update(BT=BT, V=V, **kw)
+    return W.Workload(**d)
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 7, 8, 9, 1001, 4097, 65541])
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_ragged_vocab_bf16(V, mode):
+    """Row lengths that do not fill 16-byte vectors take the scalar path."""
+    wl = _small("llm_head", 37, V, ignore_frac=0.1, label_smoothing=0.0)
+    out, xh, tgt, w = run(wl, mode, "mean", 1.0, accuracy=True)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0), xh, tgt, w)
+
+
+@pytest.mark.parametrize("V", [8, 64, 2048, 16384, 32768, 65536, 131072, 163840, 262144])
+def test_every_resident_shape(V):
+    """One row length per on-chip shape boundary, with a ragged last slot."""
+    wl = _small("llm_head", 9, V - 8 if V > 8 else V)
+    out, xh, tgt, w = run(wl, "fused", "mean", 1.0, accuracy=True)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0), xh, tgt, w)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_other_dtypes(dtype, mode):
+    wl = _small("llm_head", 33, 12000, dtype=dtype)
+    out, xh, tgt, w = run(wl, mode, "sum", 0.37)
+    check(wl, out, reference(wl, xh, tgt, w, "sum", 0.37), xh, tgt, w)
+
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_row_stride_wider_than_vocab(mode):
+    wl = _small("llm_head", 20, 5000)
+    out, xh, tgt, w = run(wl, mode, "mean", 1.0, row_stride=5016)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0), xh, tgt, w)
+
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_all_rows_ignored(mode):
+    wl = _small("tiny", 16, 300)
+    tgt = np.full(16, -100, np.int64)
+    out, xh, _, w = run(wl, mode, "mean", 1.0, tgt=tgt)
+    assert math.isnan(float(out["loss"]))
+    assert np.all(out["grad"] == 0.0)
+    assert np.all(out["row_loss"] == 0.0)
+
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_empty_batch(mode):
+    wl = _small("tiny", 0, 100)
+    dev = _dev()
+    x = torch.zeros((0, 100), device=dev)
+    t = torch.zeros(0, dtype=torch.int64, device=dev)
+    for red in ("mean", "sum", "none"):
+        if mode == "fused":
+            res = vf.forward_fused_inplace(x, t, reduction=red)
+        else:
+            res = vf.forward_stats(x, t, reduction=red)
+        torch.cuda.synchronize()
+        if red == "mean":
+            assert math.isnan(float(res["loss"]))
+        elif red == "sum":
+            assert float(res["loss"]) == 0.0
+        else:
+            assert res["loss"].numel() == 0
+
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_bad_targets_flagged(mode):
+    wl = _small("tiny", 12, 257, ignore_frac=0.0)
+    tgt = W.targets(wl)
+    tgt[3] = 257
+    tgt[7] = -5
+    out, xh, _, w = run(wl, mode, "none", 1.0, tgt=tgt)
+    assert out["status"]["status"] & 1
+    assert math.isnan(out["row_loss"][3]) and math.isnan(out["row_loss"][7])
+    assert np.all(out["grad"][[3, 7]] == 0.0)
+    good = [i for i in range(12) if i not in (3, 7)]
+    ref = reference(wl, xh, tgt, w, "none", 1.0)
+    assert_loss_close(out["row_loss"][good], ref["row_loss"][good])
+
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_ignore_index_inside_vocab(mode):
+    dev = _dev()
+    wl = _small("tiny", 10, 64)
+    tgt = W.targets(wl)
+    tgt[::3] = 5
+    xh = W.logits(wl, tgt)
+    x = xh.to(dev)
+    t = torch.from_numpy(tgt).to(dev)
+    if mode == "fused":
+        res = vf.forward_fused_inplace(x, t, ignore_index=5, reduction="none", row_loss=True)
+        g = x
+    else:
+        res = vf.forward_stats(x, t, ignore_index=5, reduction="none", row_loss=True)
+        g = vf.backward_from_stats(x, t, res["stats"], torch.ones(10, device=dev),
+                                   res["workspace"], ignore_index=5, reduction="none")
+    torch.cuda.synchronize()
+    r = oracle.cross_entropy(W.as_f64(xh), tgt, None, 5, 0.0, "none")
+    assert_loss_close(res["loss"].cpu().numpy(), r.loss)
+    assert torch.all(g[::3] == 0)
+
+
+def test_nan_logit_propagates():
+    dev = _dev()
+    wl = _small("tiny", 4, 100)
+    tgt = W.targets(wl)
+    xh = W.logits(wl, tgt)
+    xh[2, 17] = float("nan")
+    for mode in ("fused", "split"):
+        x = xh.to(dev)
+        t = torch.from_numpy(tgt).to(dev)
+        if mode == "fused":
+            res = vf.forward_fused_inplace(x, t, reduction="none")
+            g = x
+        else:
+            res = vf.forward_stats(x, t, reduction="none")
+            g = vf.backward_from_stats(x, t, res["stats"], torch.ones(4, device=dev),
+                                       res["workspace"], reduction="none")
+        torch.cuda.synchronize()
+        loss = res["loss"].cpu()
+        assert math.isnan(loss[2]) and torch.isfinite(loss[[0, 1, 3]]).all()
+        assert torch.isnan(g[2]).all() and torch.isfinite(g[[0, 1, 3]]).all()
+
+
+def test_grad_output_one_skips_and_next_below_scales():
+    dev = _dev()
+    wl = _small("llm_head", 8, 4096)
+    tgt = W.targets(wl)
+    xh = W.logits(wl, tgt)
+    x = xh.to(dev)
+    t = torch.from_numpy(tgt).to(dev)
+    vf.forward_fused_inplace(x, t)
+    g0 = x.clone()
+    vf.scale_grad(x, torch.tensor(1.0, device=dev))
+    torch.cuda.synchronize()
+    assert torch.equal(x, g0)
+    below = float(np.nextafter(np.float32(1.0), np.float32(0.0)))
+    vf.scale_grad(x, torch.tensor(below, device=dev))
+    expect = (g0.float() * below).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(x, expect)
+
+
+def test_deterministic_repeat():
+    dev = _dev()
+    wl = W.with_rows(W.WORKLOADS["llm_head"], 64)
+    tgt = W.targets(wl)
+    xh = W.logits(wl, tgt)
+    outs = []
+    for _ in range(2):
+        x = xh.to(dev)
+        res = vf.forward_fused_inplace(x, torch.from_numpy(tgt).to(dev), label_smoothing=0.1)
+        torch.cuda.synchronize()
+        outs.append((x.cpu(), res["loss"].cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+# ---------------------------------------------------------------- autograd and host syncs
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+@pytest.mark.parametrize("reduction,go", [("mean", 1.0), ("sum", 0.37), ("none", 0.37)])
+@pytest.mark.parametrize("variant", ["plain", "smoothing", "weights"])
+def test_no_host_sync(mode, reduction, go, variant):
+    """Forward and backward under torch's sync debug mode "error" (the
+    pages' no-host-sync test, here for mean too)."""
+    dev = _dev()
+    wl = _small("llm_head", 64, 8000, weighted=(variant == "weights"),
+                label_smoothing=0.1 if variant != "plain" else 0.0)
+    tgt = W.targets(wl)
+    xh = W.logits(wl, tgt)
+    w = W.class_weights(wl)
+    x = xh.to(dev).requires_grad_(True)
+    t = torch.from_numpy(tgt).to(dev)
+    wt = None if w is None else torch.from_numpy(w).to(dev)
+    gout = _go_tensor(go, reduction, wl.BT, dev)
+    torch.cuda.synchronize()
+    torch.cuda.set_sync_debug_mode("error")
+    try:
+        from vocab_softmax_cross_amd import cross_entropy
+        loss = cross_entropy(x, t, wt, -100, wl.label_smoothing, reduction, mode=mode)
+        loss.backward(gout)
+    finally:
+        torch.cuda.set_sync_debug_mode("default")
+    torch.cuda.synchronize()
+    ref = oracle.cross_entropy(W.as_f64(xh), tgt, w, -100, wl.label_smoothing, reduction,
+                               go if reduction != "none" else np.full(wl.BT, go), wl.dtype)
+    assert_loss_close(loss.detach().cpu().numpy(), ref.loss)
+    rep = grad_report(x.grad.float().cpu().numpy(), ref.grad, wl.dtype, W.as_f64(xh), tgt,
+                      ref.stats, ref.cls, ref.scale, wl.label_smoothing, w, ref.norm.sum_w)
+    assert rep.floor_fail == 0, rep
+
+
+def test_fused_second_backward_raises():
+    dev = _dev()
+    x = torch.randn(4, 64, device=dev, dtype=torch.bfloat16, requires_grad=True)
+    t = torch.randint(0, 64, (4,), device=dev)
+    from vocab_softmax_cross_amd import cross_entropy
+    loss = cross_entropy(x, t)
+    loss.backward(retain_graph=True)
+    with pytest.raises(RuntimeError):
+        loss.backward()
+
+
+def test_fused_peak_memory_is_one_logits_tensor():
+    """Forward + backward allocate O(rows) beyond the logits (linkedin#1290:
+    peak memory equals one logits tensor)."""
+    dev = _dev()
+    wl = W.with_rows(W.WORKLOADS["llm_head"], 1024)
+    tgt = W.targets(wl)
+    x = W.logits(wl, tgt).to(dev).requires_grad_(True)
+    t = torch.from_numpy(tgt).to(dev)
+    from vocab_softmax_cross_amd import cross_entropy
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    loss = cross_entropy(x, t, label_smoothing=0.1)
+    loss.backward()
+    torch.cuda.synchronize()
+    extra = torch.cuda.max_memory_allocated() - base
+    assert extra <= 64 * wl.BT + (1 << 20), extra
+
+
+def test_graph_capture_replays_match_eager():
+    """The fused step captured in a HIP graph: every replay (with eager work
+    and synchronizations in between) equals the eager result."""
+    dev = _dev()
+    wl = W.with_rows(W.WORKLOADS["llm_head"], 128)
+    tgt = W.targets(wl)
+    xh = W.logits(wl, tgt)
+    t = torch.from_numpy(tgt).to(dev)
+    pristine = xh.to(dev)
+    x = pristine.clone()
+    eager = vf.forward_fused_inplace(x, t, label_smoothing=0.1)
+    torch.cuda.synchronize()
+    eager_g, eager_l = x.clone(), eager["loss"].clone()
+
+    static_x = pristine.clone()
+    ws = vf.workspace_for(wl.BT, dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        vf.forward_fused_inplace(static_x, t, label_smoothing=0.1, workspace=ws)  # warm-up
+    torch.cuda.current_stream().wait_stream(s)
+    static_x.copy_(pristine)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        res = vf.forward_fused_inplace(static_x, t, label_smoothing=0.1, workspace=ws)
+    for _ in range(3):
+        static_x.copy_(pristine)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(static_x, eager_g)
+        assert torch.equal(res["loss"], eager_l)
+        _ = (pristine.float() * 2).sum()  # unrelated eager work between replays

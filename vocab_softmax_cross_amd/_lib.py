@@ -1,0 +1,140 @@
+"""ctypes binding of libvsce.so: the C ABI of include/vsce.h under the same names.
+
+Argument marshalling only: every function here forwards plain device pointers,
+sizes and a HIP stream handle to the library and raises if the library
+returns an error code.  There is no fallback: without the built library (on
+the host or the GPU) importing the functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_float, c_int32, c_int64, c_size_t, c_void_p
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libvsce.so")
+
+# vsce_dtype, vsce_reduction and return codes (include/vsce.h)
+F32, BF16, F16 = 0, 1, 2
+REDUCTION_NONE, REDUCTION_MEAN, REDUCTION_SUM = 0, 1, 2
+REDUCTIONS = {"none": REDUCTION_NONE, "mean": REDUCTION_MEAN, "sum": REDUCTION_SUM}
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_LAUNCH = 0, -1, -2, -3
+STATUS_BAD_TARGET = 1
+STATS_STRIDE = 4
+WS_W, WS_SUM_W, WS_N_VALID, WS_N_INVALID, WS_STATUS, WS_HEADER_BYTES = 0, 8, 16, 24, 32, 256
+
+EXPORTS = ("vsce_workspace_bytes", "ce_forward_fused_inplace", "ce_forward_stats",
+           "ce_backward_from_stats", "ce_scale_grad", "vsce_strerror", "vsce_version")
+
+
+class Problem(ctypes.Structure):
+    """struct vsce_problem."""
+    _fields_ = [
+        ("rows", c_int64),
+        ("vocab", c_int64),
+        ("row_stride", c_int64),
+        ("dtype", c_int32),
+        ("reduction", c_int32),
+        ("target", c_void_p),
+        ("class_weight", c_void_p),
+        ("ignore_index", c_int64),
+        ("label_smoothing", c_float),
+        ("reserved", c_int32),
+    ]
+
+
+class Outputs(ctypes.Structure):
+    """struct vsce_outputs."""
+    _fields_ = [
+        ("loss", c_void_p),
+        ("row_loss", c_void_p),
+        ("token_acc", c_void_p),
+        ("acc_mean", c_void_p),
+    ]
+
+
+class VsceError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} ({code})")
+        self.code = code
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libvsce.so from the package directory (build it with
+    ``python -m vocab_softmax_cross_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m vocab_softmax_cross_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    lib.vsce_workspace_bytes.argtypes = [c_int64]
+    lib.vsce_workspace_bytes.restype = c_size_t
+    lib.ce_forward_fused_inplace.argtypes = [P(Problem), c_void_p, P(Outputs), c_void_p, c_void_p]
+    lib.ce_forward_fused_inplace.restype = ctypes.c_int
+    lib.ce_forward_stats.argtypes = [P(Problem), c_void_p, c_void_p, P(Outputs), c_void_p, c_void_p]
+    lib.ce_forward_stats.restype = ctypes.c_int
+    lib.ce_backward_from_stats.argtypes = [P(Problem), c_void_p, c_void_p, c_void_p, c_void_p,
+                                           c_int64, c_void_p, c_void_p]
+    lib.ce_backward_from_stats.restype = ctypes.c_int
+    lib.ce_scale_grad.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_int32, c_void_p, c_int64,
+                                  c_int32, c_void_p]
+    lib.ce_scale_grad.restype = ctypes.c_int
+    lib.vsce_strerror.argtypes = [ctypes.c_int]
+    lib.vsce_strerror.restype = ctypes.c_char_p
+    lib.vsce_version.argtypes = []
+    lib.vsce_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, code: int) -> int:
+    if code != OK:
+        raise VsceError(fn, code, load().vsce_strerror(code).decode())
+    return code
+
+
+def vsce_workspace_bytes(rows: int) -> int:
+    return int(load().vsce_workspace_bytes(rows))
+
+
+def vsce_version() -> int:
+    return int(load().vsce_version())
+
+
+def ce_forward_fused_inplace(problem: Problem, logits_inout: int, outputs: Outputs,
+                             workspace: int, stream: int) -> int:
+    return _check("ce_forward_fused_inplace", load().ce_forward_fused_inplace(
+        ctypes.byref(problem), logits_inout, ctypes.byref(outputs), workspace, stream))
+
+
+def ce_forward_stats(problem: Problem, logits: int, stats: int, outputs: Outputs,
+                     workspace: int, stream: int) -> int:
+    return _check("ce_forward_stats", load().ce_forward_stats(
+        ctypes.byref(problem), logits, stats, ctypes.byref(outputs), workspace, stream))
+
+
+def ce_backward_from_stats(problem: Problem, logits: int, grad: int, stats: int,
+                           grad_output: int, grad_output_stride: int, workspace: int,
+                           stream: int) -> int:
+    return _check("ce_backward_from_stats", load().ce_backward_from_stats(
+        ctypes.byref(problem), logits, grad, stats, grad_output, grad_output_stride, workspace,
+        stream))
+
+
+def ce_scale_grad(grad: int, rows: int, vocab: int, row_stride: int, dtype: int,
+                  grad_output: int, grad_output_stride: int, skip_if_one: int,
+                  stream: int) -> int:
+    return _check("ce_scale_grad", load().ce_scale_grad(
+        grad, rows, vocab, row_stride, dtype, grad_output, grad_output_stride, skip_if_one,
+        stream))
+
+
+def raw_call(name: str, *args) -> int:
+    """Call an entry point and return its code without raising (tests of the
+    argument checks)."""
+    return int(getattr(load(), name)(*args))

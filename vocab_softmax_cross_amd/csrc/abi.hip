@@ -1,0 +1,266 @@
+// The C ABI of libvsce.so (declared in include/vsce.h): argument checks,
+// workspace layout and the launch sequence of each entry point.
+//
+// Every check happens before the first HIP call, so a rejected call enqueues
+// nothing; the entry points never allocate, synchronize or read device data.
+#include <math.h>
+#include <stdint.h>
+
+#include "common.h"
+#include "launch.h"
+#include "vsce.h"
+
+namespace vsce {
+namespace {
+
+constexpr int64_t kAlign = 256;
+
+int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(int dt) {
+  switch (dt) {
+    case VSCE_F32: return 4;
+    case VSCE_BF16:
+    case VSCE_F16: return 2;
+    default: return 0;
+  }
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checks a problem descriptor and fills the derived fields.
+int check_problem(const vsce_problem* pb, const void* logits, Prob& p) {
+  if (!pb) return VSCE_ERR_INVALID;
+  const int eb = elem_bytes(pb->dtype);
+  if (eb == 0) return VSCE_ERR_INVALID;
+  if (pb->rows < 0 || pb->vocab < 1 || pb->row_stride < pb->vocab) return VSCE_ERR_INVALID;
+  if (pb->reduction < VSCE_REDUCTION_NONE || pb->reduction > VSCE_REDUCTION_SUM)
+    return VSCE_ERR_INVALID;
+  if (pb->reserved != 0) return VSCE_ERR_INVALID;
+  const float eps = pb->label_smoothing;
+  if (!(eps >= 0.0f && eps <= 1.0f)) return VSCE_ERR_INVALID;  // also rejects NaN
+  if (pb->rows > 0 && (!pb->target || !logits)) return VSCE_ERR_INVALID;
+  if (logits && !aligned(logits, static_cast<uintptr_t>(eb))) return VSCE_ERR_INVALID;
+  if (pb->class_weight && !aligned(pb->class_weight, 4)) return VSCE_ERR_INVALID;
+  // Row byte offsets are 32-bit in the kernels; grids are 31-bit.
+  if (pb->vocab * eb >= (int64_t(1) << 31)) return VSCE_ERR_UNSUPPORTED;
+  if (pb->rows > 0x7fffffffLL) return VSCE_ERR_UNSUPPORTED;
+
+  p.rows = pb->rows;
+  p.V = pb->vocab;
+  p.stride = pb->row_stride;
+  p.dt = pb->dtype;
+  p.red = pb->reduction;
+  p.target = pb->target;
+  p.weight = pb->class_weight;
+  p.ignore_index = pb->ignore_index;
+  p.eps = eps;
+  p.eta = eps / static_cast<float>(pb->vocab);
+  p.elem_bytes = eb;
+  const int vec = 16 / eb;
+  p.vec_ok = aligned(logits, 16) && (pb->row_stride * eb) % 16 == 0 && pb->vocab % vec == 0 &&
+             (!pb->class_weight || aligned(pb->class_weight, 16));
+  return VSCE_OK;
+}
+
+int check_workspace(const void* ws) {
+  if (!ws || !aligned(ws, kAlign)) return VSCE_ERR_INVALID;
+  return VSCE_OK;
+}
+
+int check_outputs(const vsce_outputs* out) {
+  if (!out || !out->loss) return VSCE_ERR_INVALID;
+  return VSCE_OK;
+}
+
+// Per-row destinations of the forward kernels.
+RowArgs row_args(const Prob& p, void* x, const vsce_outputs* out, void* workspace) {
+  RowArgs a = {};
+  char* ws = static_cast<char*>(workspace);
+  float* loss_scratch = reinterpret_cast<float*>(ws + VSCE_WS_HEADER_BYTES);
+  float* acc_scratch =
+      reinterpret_cast<float*>(ws + VSCE_WS_HEADER_BYTES + align_up(4 * p.rows));
+  a.x = x;
+  a.g = x;
+  a.stride = p.stride;
+  a.V = p.V;
+  a.target = p.target;
+  a.weight = p.weight;
+  a.ignore_index = p.ignore_index;
+  a.eps = p.eps;
+  a.eta = p.eta;
+  a.mean = (p.red == VSCE_REDUCTION_MEAN);
+  if (p.red == VSCE_REDUCTION_NONE) {
+    a.loss_rows = out->loss;
+    a.loss_rows2 = out->row_loss;
+  } else {
+    a.loss_rows = out->row_loss ? out->row_loss : loss_scratch;
+  }
+  a.acc_rows = out->token_acc ? out->token_acc : (out->acc_mean ? acc_scratch : nullptr);
+  a.rows = p.rows;
+  a.ws = reinterpret_cast<const WsHeader*>(ws);
+  return a;
+}
+
+int forward_common(const Prob& p, RowArgs a, const vsce_outputs* out, void* workspace,
+                   bool fused, hipStream_t stream) {
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(workspace);
+  int rc = launch_prologue(p, hdr, stream);
+  if (rc != VSCE_OK) return rc;
+  if (p.rows > 0) {
+    if (fused) {
+      rc = launch_fused_resident(p, a, stream);
+      if (rc == VSCE_ERR_UNSUPPORTED) rc = launch_fused_stream(p, a, stream);
+    } else {
+      rc = launch_stats(p, a, stream);
+    }
+    if (rc != VSCE_OK) return rc;
+  }
+  return launch_finalize(p, a.loss_rows, a.acc_rows, out->loss, out->acc_mean, hdr, stream);
+}
+
+}  // namespace
+
+int launch_fused_resident(const Prob& p, RowArgs a, hipStream_t s) {
+  if (!p.vec_ok) return VSCE_ERR_UNSUPPORTED;
+  a.nvec = p.V / (16 / p.elem_bytes);
+  switch (p.dt) {
+    case VSCE_F32: return fused_resident_dt<VSCE_F32>(p, a, s);
+    case VSCE_BF16: return fused_resident_dt<VSCE_BF16>(p, a, s);
+    case VSCE_F16: return fused_resident_dt<VSCE_F16>(p, a, s);
+    default: return VSCE_ERR_INVALID;
+  }
+}
+
+namespace {
+int stream_any(int which, const Prob& p, const RowArgs& a, hipStream_t s) {
+  switch (p.dt) {
+    case VSCE_F32: return stream_dt<VSCE_F32>(which, p, a, s);
+    case VSCE_BF16: return stream_dt<VSCE_BF16>(which, p, a, s);
+    case VSCE_F16: return stream_dt<VSCE_F16>(which, p, a, s);
+    default: return VSCE_ERR_INVALID;
+  }
+}
+}  // namespace
+
+int launch_stats(const Prob& p, RowArgs a, hipStream_t s) {
+  return stream_any(kStreamStats, p, a, s);
+}
+int launch_fused_stream(const Prob& p, RowArgs a, hipStream_t s) {
+  return stream_any(kStreamFused, p, a, s);
+}
+int launch_backward(const Prob& p, RowArgs a, hipStream_t s) {
+  return stream_any(kStreamBackward, p, a, s);
+}
+int launch_scale(const Prob& p, RowArgs a, hipStream_t s) {
+  return stream_any(kStreamScale, p, a, s);
+}
+
+}  // namespace vsce
+
+using namespace vsce;
+
+extern "C" {
+
+size_t vsce_workspace_bytes(int64_t rows) {
+  if (rows < 0) return 0;
+  return static_cast<size_t>(VSCE_WS_HEADER_BYTES + 2 * align_up(4 * rows));
+}
+
+int ce_forward_fused_inplace(const vsce_problem* problem, void* logits_inout,
+                             const vsce_outputs* out, void* workspace, hipStream_t stream) {
+  Prob p;
+  int rc = check_problem(problem, logits_inout, p);
+  if (rc == VSCE_OK) rc = check_outputs(out);
+  if (rc == VSCE_OK) rc = check_workspace(workspace);
+  if (rc != VSCE_OK) return rc;
+  return forward_common(p, row_args(p, logits_inout, out, workspace), out, workspace, true,
+                        stream);
+}
+
+int ce_forward_stats(const vsce_problem* problem, const void* logits, float* stats,
+                     const vsce_outputs* out, void* workspace, hipStream_t stream) {
+  Prob p;
+  int rc = check_problem(problem, logits, p);
+  if (rc == VSCE_OK) rc = check_outputs(out);
+  if (rc == VSCE_OK) rc = check_workspace(workspace);
+  if (rc == VSCE_OK && p.rows > 0 && (!stats || !aligned(stats, 16))) rc = VSCE_ERR_INVALID;
+  if (rc != VSCE_OK) return rc;
+  RowArgs a = row_args(p, const_cast<void*>(logits), out, workspace);
+  a.stats = stats;
+  return forward_common(p, a, out, workspace, false, stream);
+}
+
+int ce_backward_from_stats(const vsce_problem* problem, const void* logits, void* grad,
+                           const float* stats, const float* grad_output,
+                           int64_t grad_output_stride, const void* workspace,
+                           hipStream_t stream) {
+  Prob p;
+  int rc = check_problem(problem, logits, p);
+  if (rc == VSCE_OK) rc = check_workspace(workspace);
+  if (rc != VSCE_OK) return rc;
+  if (p.rows == 0) return VSCE_OK;
+  if (!grad || !aligned(grad, static_cast<uintptr_t>(p.elem_bytes))) return VSCE_ERR_INVALID;
+  if (!stats || !aligned(stats, 16) || !grad_output) return VSCE_ERR_INVALID;
+  if (grad_output_stride != 0 && grad_output_stride != 1) return VSCE_ERR_INVALID;
+  // The vector path needs the output aligned like the input.
+  if (p.vec_ok && !aligned(grad, 16)) p.vec_ok = false;
+  RowArgs a = {};
+  a.x = const_cast<void*>(logits);
+  a.g = grad;
+  a.stride = p.stride;
+  a.V = p.V;
+  a.target = p.target;
+  a.weight = p.weight;
+  a.ignore_index = p.ignore_index;
+  a.eps = p.eps;
+  a.eta = p.eta;
+  a.mean = (p.red == VSCE_REDUCTION_MEAN);
+  a.stats = const_cast<float*>(stats);
+  a.go = grad_output;
+  a.go_stride = grad_output_stride;
+  a.rows = p.rows;
+  a.ws = static_cast<const WsHeader*>(workspace);
+  return launch_backward(p, a, stream);
+}
+
+int ce_scale_grad(void* grad, int64_t rows, int64_t vocab, int64_t row_stride, int32_t dtype,
+                  const float* grad_output, int64_t grad_output_stride, int32_t skip_if_one,
+                  hipStream_t stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0 || rows < 0 || vocab < 1 || row_stride < vocab) return VSCE_ERR_INVALID;
+  if (grad_output_stride != 0 && grad_output_stride != 1) return VSCE_ERR_INVALID;
+  if (rows == 0) return VSCE_OK;
+  if (!grad || !grad_output || !aligned(grad, static_cast<uintptr_t>(eb))) return VSCE_ERR_INVALID;
+  if (vocab * eb >= (int64_t(1) << 31) || rows > 0x7fffffffLL) return VSCE_ERR_UNSUPPORTED;
+  Prob p = {};
+  p.rows = rows;
+  p.V = vocab;
+  p.stride = row_stride;
+  p.dt = dtype;
+  p.elem_bytes = eb;
+  p.vec_ok = aligned(grad, 16) && (row_stride * eb) % 16 == 0 && vocab % (16 / eb) == 0;
+  RowArgs a = {};
+  a.g = grad;
+  a.stride = row_stride;
+  a.V = vocab;
+  a.go = grad_output;
+  a.go_stride = grad_output_stride;
+  a.skip_if_one = skip_if_one != 0;
+  a.rows = rows;
+  return launch_scale(p, a, stream);
+}
+
+const char* vsce_strerror(int code) {
+  switch (code) {
+    case VSCE_OK: return "ok";
+    case VSCE_ERR_INVALID: return "invalid argument";
+    case VSCE_ERR_UNSUPPORTED: return "unsupported combination";
+    case VSCE_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown error";
+  }
+}
+
+int vsce_version(void) { return 100; }
+
+}  // extern "C"

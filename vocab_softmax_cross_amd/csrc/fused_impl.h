@@ -1,0 +1,236 @@
+// Fused forward + in-place gradient with the whole row held on chip.
+// (Template definitions; fused_<dtype>.hip instantiate one element type each.)
+//
+// One workgroup per row.  The row is read from HBM once, with 16-byte
+// vector loads: thread t holds vectors t, t + NT, t + 2 NT, ... of the row,
+// the first NREG of them in registers and the next NLDS in LDS (loaded
+// straight into LDS with global_load_lds_dwordx4).  Three passes then run
+// over the on-chip copy:
+//   1. the row maximum M (workgroup max, one barrier);
+//   2. the sum of exp(x - M) with every element equal to M left out, the
+//      number of such elements and the first index of M (only the wavefronts
+//      holding M take this careful path; the others just add), plus the
+//      (weighted) logit sum for label smoothing (workgroup sum, one barrier);
+//   3. the gradient, written over the logits with one store per vector; the
+//      lane that owns the target column substitutes the fp32 true-class value
+//      before its store.
+// The design follows the fused kernel of Liger-Kernel PR #1268 ("pass 1"
+// online statistics, "pass 2" in-place gradient, one O(1) true-class
+// correction, fp32 per the linkedin#1329 commit message), with the second
+// read of the logits served from registers and LDS instead of memory.
+#pragma once
+
+#include <tuple>
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+#include "rowmath.h"
+
+namespace vsce {
+namespace {
+
+template <int DT, bool WEIGHTED>
+__device__ inline void load_weights(const float* w, int64_t j, float (&wv)[Dt<DT>::VEC]) {
+  constexpr int VEC = Dt<DT>::VEC;
+  if constexpr (WEIGHTED) {
+    const float4* p = reinterpret_cast<const float4*>(w + j * VEC);
+#pragma unroll
+    for (int q = 0; q < VEC / 4; ++q) {
+      const float4 t = p[q];
+      wv[4 * q + 0] = t.x;
+      wv[4 * q + 1] = t.y;
+      wv[4 * q + 2] = t.z;
+      wv[4 * q + 3] = t.w;
+    }
+  }
+}
+
+template <int DT, int NT, int NREG, int NLDS, bool WEIGHTED, int WPE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
+void fused_resident_kernel(const RowArgs a) {
+  using D = Dt<DT>;
+  constexpr int VEC = D::VEC;
+  constexpr int NW = NT / kWave;
+  constexpr uint32_t SLOT_BYTES = NT * 16u;  // bytes between a thread's vectors
+  __shared__ uint4 xl[NLDS > 0 ? NLDS * NT : 1];
+  __shared__ float red_max[NW];
+  __shared__ float4 red_sum[NW];
+
+  const int tid = threadIdx.x;
+  const int64_t n = blockIdx.x;
+  const int nvec = static_cast<int>(a.nvec);
+  char* rowb = static_cast<char*>(a.x) + n * a.stride * D::BYTES;
+  const auto rsrc = make_rsrc(rowb, static_cast<uint32_t>(a.V * D::BYTES));
+  const uint32_t voff = static_cast<uint32_t>(tid) * 16u;
+  auto in_row = [&](int k) { return k * NT + tid < nvec; };
+  // Lanes past the end of the row get a per-lane offset beyond num_records,
+  // so the buffer range check drops them whether or not it counts soffset.
+  auto lane_off = [&](int k) { return in_row(k) ? voff : kOutOfRange; };
+  const int64_t y = a.target[n];
+  const int cls = row_class(y, a.V, a.ignore_index);
+
+  if (cls != kValid) {  // uniform over the workgroup: zero gradient, no read
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    static_for<NREG + NLDS>([&](auto k) { buf_store16(rsrc, lane_off(k), k * SLOT_BYTES, z); });
+    if (tid == 0) store_row(a, n, (cls == kIgnored) ? 0.0f : __builtin_nanf(""), 0.0f);
+    return;
+  }
+
+  const float xy = D::load1(rowb, y);
+
+  // ---- one read of the row: registers, then LDS (lanes past the row read 0
+  //      and are masked out of every pass below)
+  uint4 r[NREG];
+  static_for<NREG>([&](auto k) { r[k] = buf_load16(rsrc, lane_off(k), k * SLOT_BYTES); });
+  if constexpr (NLDS > 0) {
+    const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~(kWave - 1));
+    static_for<NLDS>([&](auto k) {
+      buf_load16_lds(rsrc, xl + k * NT + wave_base, lane_off(NREG + k), (NREG + k) * SLOT_BYTES);
+    });
+  }
+
+  // ---- pass 1: row maximum
+  float mx = -__builtin_inff();
+  auto max_vec = [&](const uint4 v) {
+    float f[VEC];
+    D::unpack(v, f);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) mx = fmaxf(mx, f[i]);
+  };
+  static_for<NREG>([&](auto k) {
+    if (in_row(k)) max_vec(r[k]);
+  });
+  if constexpr (NLDS > 0) {
+    // Each lane reads back only the LDS slots its own wavefront loaded.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    static_for<NLDS>([&](auto k) {
+      if (in_row(NREG + k)) max_vec(xl[k * NT + tid]);
+    });
+  }
+  const float M = block_max<NT>(mx, red_max);
+  const float ML = M * kLog2e;
+  static_for<NREG>([&](auto k) { opaque(r[k]); });
+
+  // ---- pass 2: sums below the maximum, ties, first index, logit sum
+  RowSums rs = {0.0f, 0.0f, 0, 0x7fffffff};
+  auto accumulate = [&](auto careful, const uint4 v, int64_t j) {
+    float f[VEC], wv[VEC];
+    D::unpack(v, f);
+    load_weights<DT, WEIGHTED>(a.weight, j, wv);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const float e = exp_shifted(f[i], ML);
+      if constexpr (decltype(careful)::value) {
+        const bool eq = (f[i] == M);
+        rs.s += eq ? 0.0f : e;
+        rs.cnt += eq ? 1 : 0;
+        if (eq) rs.first = min(rs.first, static_cast<int>(j * VEC + i));
+      } else {
+        rs.s += e;
+      }
+      if constexpr (WEIGHTED) rs.S = __builtin_fmaf(wv[i], f[i], rs.S);
+      else rs.S += f[i];
+    }
+  };
+  auto sum_pass = [&](auto careful) {
+    static_for<NREG>([&](auto k) {
+      if (in_row(k)) accumulate(careful, r[k], k * NT + tid);
+    });
+    static_for<NLDS>([&](auto k) {
+      if (in_row(NREG + k)) accumulate(careful, xl[k * NT + tid], (NREG + k) * NT + tid);
+    });
+  };
+  // Wavefront-uniform choice: only wavefronts that hold the maximum need the
+  // compare per element.
+  if (__ballot(mx == M) != 0ull) sum_pass(std::true_type{});
+  else sum_pass(std::false_type{});
+  rs = block_sums<NT>(rs, red_sum);
+  static_for<NREG>([&](auto k) { opaque(r[k]); });
+
+  const float dp = rs.s + static_cast<float>(rs.cnt - 1);  // d' = d - 1
+  const float sum_w = static_cast<float>(a.ws->sum_w);
+  const float wy = WEIGHTED ? a.weight[y] : 1.0f;
+  if (tid == 0)
+    store_row(a, n, row_loss(M, dp, xy, rs.S, wy, sum_w, a.eps, a.eta),
+              (static_cast<int64_t>(rs.first) == y) ? 1.0f : 0.0f);
+
+  // ---- pass 3: gradient over the on-chip row, one store per vector
+  const float sigma = a.mean ? static_cast<float>(1.0 / a.ws->W) : 1.0f;
+  const RowTerms t = row_terms(M, dp, xy, wy, sum_w, a.eps, a.eta, sigma);
+  const int64_t jy = y / VEC;
+  const int ky = static_cast<int>(jy / NT);  // slot and lane owning the target
+  const int ty = static_cast<int>(jy % NT);
+  const int iy = static_cast<int>(y % VEC);
+  auto grad_vec = [&](const uint4 v, int k) {
+    float f[VEC], wv[VEC];
+    D::unpack(v, f);
+    load_weights<DT, WEIGHTED>(a.weight, static_cast<int64_t>(k) * NT + tid, wv);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const float b = WEIGHTED ? t.B * wv[i] : t.B;
+      f[i] = __builtin_fmaf(exp_shifted(f[i], t.ML), t.K, -b);
+    }
+    if (k == ky && tid == ty) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i)
+        if (i == iy) f[i] = t.dxy;
+    }
+    buf_store16(rsrc, voff, static_cast<uint32_t>(k) * SLOT_BYTES, D::pack(f));
+  };
+  static_for<NREG>([&](auto k) {
+    if (in_row(k)) grad_vec(r[k], k);
+  });
+  static_for<NLDS>([&](auto k) {
+    if (in_row(NREG + k)) grad_vec(xl[k * NT + tid], NREG + k);
+  });
+}
+
+// Shapes of the resident kernel: threads per workgroup, vectors per thread in
+// registers and in LDS, and the minimum wavefronts per SIMD to compile for
+// (which caps the registers per wavefront at 512 / WPE).
+template <int NT_, int NREG_, int NLDS_, int WPE_>
+struct Shape {
+  static constexpr int NT = NT_, NREG = NREG_, NLDS = NLDS_, WPE = WPE_;
+};
+
+using Shapes = std::tuple<Shape<64, 4, 0, 4>,       // rows up to 256 vectors
+                          Shape<256, 8, 0, 4>,      // 2048 vectors
+                          Shape<256, 16, 0, 4>,     // 4096 vectors
+                          Shape<512, 16, 0, 4>,     // 8192 vectors
+                          Shape<512, 23, 9, 4>,     // 16384 vectors: 2 workgroups per CU
+                          Shape<1024, 16, 4, 4>,    // 20480 vectors
+                          Shape<1024, 24, 8, 4>>;   // 32768 vectors
+
+template <int DT, bool W, class SH>
+int launch_shape(const Prob& p, const RowArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((fused_resident_kernel<DT, SH::NT, SH::NREG, SH::NLDS, W, SH::WPE>),
+                     dim3(static_cast<unsigned>(p.rows)), dim3(SH::NT), 0, s, a);
+  return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
+}
+
+template <int DT, bool W, size_t I = 0>
+int pick_shape(const Prob& p, const RowArgs& a, hipStream_t s) {
+  if constexpr (I == std::tuple_size<Shapes>::value) {
+    return VSCE_ERR_UNSUPPORTED;
+  } else {
+    using SH = std::tuple_element_t<I, Shapes>;
+    if (a.nvec <= static_cast<int64_t>(SH::NT) * (SH::NREG + SH::NLDS))
+      return launch_shape<DT, W, SH>(p, a, s);
+    return pick_shape<DT, W, I + 1>(p, a, s);
+  }
+}
+
+template <int DT>
+int dispatch_weighted(const Prob& p, const RowArgs& a, hipStream_t s) {
+  return p.weight ? pick_shape<DT, true>(p, a, s) : pick_shape<DT, false>(p, a, s);
+}
+
+}  // namespace
+
+template <int DT>
+int fused_resident_dt(const Prob& p, const RowArgs& a, hipStream_t s) {
+  return dispatch_weighted<DT>(p, a, s);
+}
+
+}  // namespace vsce

@@ -1,0 +1,78 @@
+// Internal interface between the C-ABI layer (abi.cpp) and the kernel
+// translation units.  Host code only; every function enqueues work on the
+// given stream and returns a VSCE_* code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vsce.h"
+
+namespace vsce {
+
+struct WsHeader;
+
+// A validated problem with the derived quantities the launchers need.
+struct Prob {
+  int64_t rows;
+  int64_t V;
+  int64_t stride;  // elements
+  int dt;          // vsce_dtype
+  int red;         // vsce_reduction
+  const int64_t* target;
+  const float* weight;
+  int64_t ignore_index;
+  float eps;
+  float eta;       // eps / V
+  int elem_bytes;
+  bool vec_ok;     // rows start 16-byte aligned and V fills whole 16-byte vectors
+};
+
+// Arguments of every per-row kernel (passed by value).
+struct RowArgs {
+  void* x;              // logits (the gradient is written here by the fused kernels)
+  void* g;              // gradient output of the split backward (may equal x)
+  int64_t stride;       // elements between rows
+  int64_t V;
+  int64_t nvec;         // 16-byte vectors per row (vector path) or V (scalar path)
+  const int64_t* target;
+  const float* weight;  // [V] or null
+  int64_t ignore_index;
+  float eps;
+  float eta;
+  int mean;             // sigma = 1 / W (mean) else 1
+  float* loss_rows;     // [rows] per-row loss (never null)
+  float* loss_rows2;    // [rows] second copy of the per-row loss, or null
+  float* acc_rows;      // [rows] or null
+  float* stats;         // [rows][4] or null
+  const float* go;      // grad_output (backward / scale)
+  int64_t go_stride;    // 0 (scalar) or 1 (per row)
+  int skip_if_one;
+  int64_t rows;
+  int64_t chunks;       // column chunks per row (chunked kernels)
+  const WsHeader* ws;
+};
+
+int launch_prologue(const Prob& p, WsHeader* ws, hipStream_t s);
+int launch_finalize(const Prob& p, const float* loss_rows, const float* acc_rows, float* loss_out,
+                    float* acc_mean_out, const WsHeader* ws, hipStream_t s);
+
+// Row held on chip (registers + LDS) between its passes: one logits read and
+// one gradient write.  VSCE_ERR_UNSUPPORTED when the row does not fit.
+int launch_fused_resident(const Prob& p, RowArgs a, hipStream_t s);
+template <int DT>
+int fused_resident_dt(const Prob& p, const RowArgs& a, hipStream_t s);
+// Streaming kernels by element type; `which` is kStreamStats .. kStreamScale.
+enum { kStreamStats = 0, kStreamFused = 1, kStreamBackward = 2, kStreamScale = 3 };
+template <int DT>
+int stream_dt(int which, const Prob& p, const RowArgs& a, hipStream_t s);
+// Any row length: the row is streamed twice (statistics, then gradient).
+int launch_fused_stream(const Prob& p, RowArgs a, hipStream_t s);
+// Split forward: one logits read, statistics + loss.
+int launch_stats(const Prob& p, RowArgs a, hipStream_t s);
+// Split backward: logits read + gradient write from the saved statistics.
+int launch_backward(const Prob& p, RowArgs a, hipStream_t s);
+// In-place grad_output scale.
+int launch_scale(const Prob& p, RowArgs a, hipStream_t s);
+
+}  // namespace vsce

@@ -1,0 +1,116 @@
+// The two single-workgroup kernels around each forward:
+//
+//  prologue_kernel  the batch normalizers on the device (Liger-Kernel PR
+//                   #1622, Summary: the non-ignored count and target-weight
+//                   sum that "mean" divides by, the class-weight sum that eps
+//                   multiplies; its Details note that avoiding the host sync
+//                   needs the count passed to the kernel as a device pointer,
+//                   which is what this header in the workspace is), plus the
+//                   bad-target status bit.
+//  finalize_kernel  the none / sum / mean reduction of the per-row losses and
+//                   the accuracy mean (accuracy divided by the count on the
+//                   device, same Summary).
+//
+// Both sum in fp64 in a fixed order (per-thread strided partial sums, then a
+// fixed tree), so results do not depend on scheduling and need no atomics.
+#include "common.h"
+#include "launch.h"
+#include "rowmath.h"
+
+namespace vsce {
+namespace {
+
+constexpr int kSmallNT = 1024;
+
+// Fixed-order workgroup sum of doubles; every thread gets the result.
+__device__ inline double block_sum_d(double v, double* sh) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  __syncthreads();  // `sh` may still be read by a previous call
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  double r = 0.0;
+#pragma unroll
+  for (int w = 0; w < kSmallNT / kWave; ++w) r += sh[w];
+  return r;
+}
+
+__global__ __launch_bounds__(kSmallNT) void prologue_kernel(const int64_t* target, int64_t rows,
+                                                           int64_t V, const float* weight,
+                                                           int64_t ignore_index, WsHeader* ws) {
+  __shared__ double sh[kSmallNT / kWave];
+  double W = 0.0, nv = 0.0, ni = 0.0, sw = 0.0;
+  for (int64_t n = threadIdx.x; n < rows; n += kSmallNT) {
+    const int64_t y = target[n];
+    const int cls = row_class(y, V, ignore_index);
+    if (cls == kValid) {
+      nv += 1.0;
+      W += weight ? static_cast<double>(weight[y]) : 1.0;
+    } else if (cls == kInvalid) {
+      ni += 1.0;
+    }
+  }
+  if (weight) {
+    for (int64_t c = threadIdx.x; c < V; c += kSmallNT) sw += static_cast<double>(weight[c]);
+  }
+  W = block_sum_d(W, sh);
+  nv = block_sum_d(nv, sh);
+  ni = block_sum_d(ni, sh);
+  sw = weight ? block_sum_d(sw, sh) : static_cast<double>(V);
+  if (threadIdx.x == 0) {
+    ws->W = W;
+    ws->sum_w = sw;
+    ws->n_valid = static_cast<int64_t>(nv);
+    ws->n_invalid = static_cast<int64_t>(ni);
+    ws->status = (ni > 0.0) ? VSCE_STATUS_BAD_TARGET : 0u;
+    ws->pad0 = 0u;
+  }
+}
+
+__global__ __launch_bounds__(kSmallNT) void finalize_kernel(const float* loss_rows,
+                                                           const float* acc_rows, int64_t rows,
+                                                           int red, float* loss_out,
+                                                           float* acc_mean_out,
+                                                           const WsHeader* ws) {
+  __shared__ double sh[kSmallNT / kWave];
+  if (red != VSCE_REDUCTION_NONE) {
+    double t = 0.0;
+    for (int64_t n = threadIdx.x; n < rows; n += kSmallNT) t += static_cast<double>(loss_rows[n]);
+    t = block_sum_d(t, sh);
+    if (threadIdx.x == 0) {
+      if (red == VSCE_REDUCTION_MEAN) {
+        const double W = ws->W;
+        loss_out[0] = static_cast<float>(W != 0.0 ? t / W : __builtin_nan(""));
+      } else {
+        loss_out[0] = static_cast<float>(t);
+      }
+    }
+  }
+  if (acc_mean_out) {
+    double h = 0.0;
+    for (int64_t n = threadIdx.x; n < rows; n += kSmallNT) h += static_cast<double>(acc_rows[n]);
+    h = block_sum_d(h, sh);
+    if (threadIdx.x == 0) {
+      const double nv = static_cast<double>(ws->n_valid);
+      acc_mean_out[0] = static_cast<float>(nv != 0.0 ? h / nv : __builtin_nan(""));
+    }
+  }
+}
+
+}  // namespace
+
+int launch_prologue(const Prob& p, WsHeader* ws, hipStream_t s) {
+  hipLaunchKernelGGL(prologue_kernel, dim3(1), dim3(kSmallNT), 0, s, p.target, p.rows, p.V,
+                     p.weight, p.ignore_index, ws);
+  return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
+}
+
+int launch_finalize(const Prob& p, const float* loss_rows, const float* acc_rows, float* loss_out,
+                    float* acc_mean_out, const WsHeader* ws, hipStream_t s) {
+  if (p.red == VSCE_REDUCTION_NONE && acc_mean_out == nullptr) return VSCE_OK;
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kSmallNT), 0, s, loss_rows, acc_rows, p.rows,
+                     p.red, loss_out, acc_mean_out, ws);
+  return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
+}
+
+}  // namespace vsce

@@ -1,0 +1,366 @@
+// Streaming kernels: rows are read from memory as they are consumed.
+// (Template definitions; stream_<dtype>.hip instantiate one element type each.)
+//
+//  stats_kernel      split forward (TransformerEngine PR #2325: the forward
+//                    saves the per-row max, sum, target logit and
+//                    scaled_x_sum and computes the loss): one read per row.
+//  backward_kernel   split backward (same PR: fp32 gradient from the saved
+//                    statistics, grad_output applied, target handled once,
+//                    written in the input type): one read + one write.
+//  scale_kernel      in-place grad_output scale of a saved gradient
+//                    (linkedin#1290 commit message; SKIP_IF_ONE of Liger-Kernel
+//                    PR #1622): returns at once where grad_output == 1.0.
+//  fused_stream_kernel  fused forward + gradient for rows too long to keep on
+//                    chip: the statistics pass, then the gradient pass reading
+//                    the row a second time.
+//
+// Each thread keeps an online (max, sum) pair per lane: a batch of U vectors
+// raises the lane max once and rescales the sum once.  After the workgroup
+// max M is known, the lanes whose own max equals M recompute their sum with
+// the elements equal to M left out (re-reading their share of the row), so
+// d' = d - 1 never loses the small terms to the leading 1.
+#pragma once
+
+#include <tuple>
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+#include "rowmath.h"
+
+namespace vsce {
+namespace {
+
+// Elements of one "group": a 16-byte vector on the vector path, one element
+// on the scalar path (rows that are not 16-byte aligned).
+template <int DT, bool VECP>
+struct Grp {
+  using D = Dt<DT>;
+  static constexpr int E = VECP ? D::VEC : 1;
+  __device__ static inline void load(const char* row, int64_t g, float (&f)[E]) {
+    if constexpr (VECP) {
+      D::unpack(reinterpret_cast<const uint4*>(row)[g], f);
+    } else {
+      f[0] = D::load1(row, g);
+    }
+  }
+  __device__ static inline void store(char* row, int64_t g, const float (&f)[E]) {
+    if constexpr (VECP) {
+      reinterpret_cast<uint4*>(row)[g] = D::pack(f);
+    } else {
+      D::store1(row, g, f[0]);
+    }
+  }
+  __device__ static inline void weights(const float* w, int64_t g, float (&wv)[E]) {
+    if constexpr (VECP) {
+      const float4* p = reinterpret_cast<const float4*>(w + g * E);
+#pragma unroll
+      for (int q = 0; q < E / 4; ++q) {
+        const float4 t = p[q];
+        wv[4 * q] = t.x;
+        wv[4 * q + 1] = t.y;
+        wv[4 * q + 2] = t.z;
+        wv[4 * q + 3] = t.w;
+      }
+    } else {
+      wv[0] = w[g];
+    }
+  }
+};
+
+// Per-row statistics by streaming: returns (M, d', S, first) on every thread.
+// Must be called by the whole workgroup (it contains barriers).
+template <int DT, int NT, int U, bool WEIGHTED, bool VECP>
+__device__ inline void stream_stats(const RowArgs& a, const char* row, float& M_out,
+                                    float& dp_out, float& S_out, int& first_out, float* red_max,
+                                    float4* red_sum) {
+  using G = Grp<DT, VECP>;
+  constexpr int E = G::E;
+  const int tid = threadIdx.x;
+  const int64_t ng = a.nvec;
+  float m = -__builtin_inff(), s = 0.0f, S = 0.0f;
+
+  for (int64_t g0 = 0; g0 < ng; g0 += static_cast<int64_t>(NT) * U) {
+    float f[U][E];
+    bool ok[U];
+    static_for<U>([&](auto u) {
+      const int64_t g = g0 + u * NT + tid;
+      ok[u] = g < ng;
+      if (ok[u]) G::load(row, g, f[u]);
+    });
+    float bm = -__builtin_inff();
+    static_for<U>([&](auto u) {
+      if (ok[u]) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) bm = fmaxf(bm, f[u][i]);
+      }
+    });
+    if (bm > m) {
+      s *= __builtin_amdgcn_exp2f((m - bm) * kLog2e);
+      m = bm;
+    }
+    const float ML = (m == -__builtin_inff()) ? 0.0f : m * kLog2e;
+    static_for<U>([&](auto u) {
+      if (ok[u]) {
+        float wv[E];
+        if constexpr (WEIGHTED) G::weights(a.weight, g0 + u * NT + tid, wv);
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          s += exp_shifted(f[u][i], ML);
+          if constexpr (WEIGHTED) S = __builtin_fmaf(wv[i], f[u][i], S);
+          else S += f[u][i];
+        }
+      }
+    });
+  }
+
+  const float M = block_max<NT>(m, red_max);
+  const float ML = (M == -__builtin_inff()) ? 0.0f : M * kLog2e;
+  RowSums rs = {0.0f, S, 0, 0x7fffffff};
+  if (m == M) {
+    // This lane holds the row maximum: recompute its share exactly.
+    for (int64_t g0 = 0; g0 < ng; g0 += static_cast<int64_t>(NT) * U) {
+      static_for<U>([&](auto u) {
+        const int64_t g = g0 + u * NT + tid;
+        if (g < ng) {
+          float f[E];
+          G::load(row, g, f);
+#pragma unroll
+          for (int i = 0; i < E; ++i) {
+            const bool eq = (f[i] == M);
+            rs.s += eq ? 0.0f : exp_shifted(f[i], ML);
+            rs.cnt += eq ? 1 : 0;
+            if (eq) rs.first = min(rs.first, static_cast<int>(g * E + i));
+          }
+        }
+      });
+    }
+  } else {
+    rs.s = (m == -__builtin_inff()) ? 0.0f : s * __builtin_amdgcn_exp2f((m - M) * kLog2e);
+  }
+  rs = block_sums<NT>(rs, red_sum);
+  M_out = M;
+  dp_out = rs.s + static_cast<float>(rs.cnt - 1);
+  S_out = rs.S;
+  first_out = rs.first;
+}
+
+// Writes the gradient of one row segment [g_begin, g_end) of groups, with
+// the true-class element substituted by its owner.
+template <int DT, int NT, int U, bool WEIGHTED, bool VECP>
+__device__ inline void stream_grad(const RowArgs& a, const char* src, char* dst, int64_t g_begin,
+                                   int64_t g_end, const RowTerms& t, int64_t y) {
+  using G = Grp<DT, VECP>;
+  constexpr int E = G::E;
+  const int tid = threadIdx.x;
+  const int64_t gy = y / E;
+  const int iy = static_cast<int>(y % E);
+  for (int64_t g0 = g_begin; g0 < g_end; g0 += static_cast<int64_t>(NT) * U) {
+    float f[U][E];
+    static_for<U>([&](auto u) {
+      const int64_t g = g0 + u * NT + tid;
+      if (g < g_end) G::load(src, g, f[u]);
+    });
+    static_for<U>([&](auto u) {
+      const int64_t g = g0 + u * NT + tid;
+      if (g < g_end) {
+        float wv[E];
+        if constexpr (WEIGHTED) G::weights(a.weight, g, wv);
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const float b = WEIGHTED ? t.B * wv[i] : t.B;
+          f[u][i] = __builtin_fmaf(exp_shifted(f[u][i], t.ML), t.K, -b);
+        }
+        if (g == gy) {
+#pragma unroll
+          for (int i = 0; i < E; ++i)
+            if (i == iy) f[u][i] = t.dxy;
+        }
+        G::store(dst, g, f[u]);
+      }
+    });
+  }
+}
+
+template <int DT, bool VECP>
+__device__ inline void stream_zero(char* dst, int64_t g_begin, int64_t g_end, int nt, int u_) {
+  using G = Grp<DT, VECP>;
+  float z[G::E];
+#pragma unroll
+  for (int i = 0; i < G::E; ++i) z[i] = 0.0f;
+  for (int64_t g = g_begin + threadIdx.x; g < g_end; g += nt) G::store(dst, g, z);
+}
+
+__device__ inline float row_weight(const RowArgs& a, int64_t y, bool weighted) {
+  return weighted ? a.weight[y] : 1.0f;
+}
+
+template <int DT, int NT, int U, bool WEIGHTED, bool VECP>
+__global__ __launch_bounds__(NT) void stats_kernel(const RowArgs a) {
+  using D = Dt<DT>;
+  __shared__ float red_max[NT / kWave];
+  __shared__ float4 red_sum[NT / kWave];
+  const int64_t n = blockIdx.x;
+  const char* row = static_cast<const char*>(a.x) + n * a.stride * D::BYTES;
+  const int64_t y = a.target[n];
+  const int cls = row_class(y, a.V, a.ignore_index);
+  if (cls != kValid) {
+    if (threadIdx.x == 0) {
+      store_row(a, n, (cls == kIgnored) ? 0.0f : __builtin_nanf(""), 0.0f);
+      if (a.stats) reinterpret_cast<float4*>(a.stats)[n] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
+  float M, dp, S;
+  int first;
+  stream_stats<DT, NT, U, WEIGHTED, VECP>(a, row, M, dp, S, first, red_max, red_sum);
+  if (threadIdx.x == 0) {
+    const float xy = D::load1(row, y);
+    const float sum_w = static_cast<float>(a.ws->sum_w);
+    store_row(a, n, row_loss(M, dp, xy, S, row_weight(a, y, WEIGHTED), sum_w, a.eps, a.eta),
+              (static_cast<int64_t>(first) == y) ? 1.0f : 0.0f);
+    if (a.stats)
+      reinterpret_cast<float4*>(a.stats)[n] = make_float4(M, dp, xy, a.eps > 0.0f ? S : 0.0f);
+  }
+}
+
+template <int DT, int NT, int U, bool WEIGHTED, bool VECP>
+__global__ __launch_bounds__(NT) void fused_stream_kernel(const RowArgs a) {
+  using D = Dt<DT>;
+  __shared__ float red_max[NT / kWave];
+  __shared__ float4 red_sum[NT / kWave];
+  const int64_t n = blockIdx.x;
+  char* row = static_cast<char*>(a.x) + n * a.stride * D::BYTES;
+  const int64_t y = a.target[n];
+  const int cls = row_class(y, a.V, a.ignore_index);
+  if (cls != kValid) {
+    stream_zero<DT, VECP>(row, 0, a.nvec, NT, U);
+    if (threadIdx.x == 0) store_row(a, n, (cls == kIgnored) ? 0.0f : __builtin_nanf(""), 0.0f);
+    return;
+  }
+  float M, dp, S;
+  int first;
+  stream_stats<DT, NT, U, WEIGHTED, VECP>(a, row, M, dp, S, first, red_max, red_sum);
+  const float xy = D::load1(row, y);
+  const float sum_w = static_cast<float>(a.ws->sum_w);
+  const float wy = row_weight(a, y, WEIGHTED);
+  if (threadIdx.x == 0)
+    store_row(a, n, row_loss(M, dp, xy, S, wy, sum_w, a.eps, a.eta),
+              (static_cast<int64_t>(first) == y) ? 1.0f : 0.0f);
+  // Every thread has read x[y] before any thread overwrites it: the block
+  // reduction inside stream_stats ended with a barrier, and x[y] is re-read
+  // here, so order the read before the first store of the gradient pass.
+  __syncthreads();
+  const float sigma = a.mean ? static_cast<float>(1.0 / a.ws->W) : 1.0f;
+  const RowTerms t = row_terms(M, dp, xy, wy, sum_w, a.eps, a.eta, sigma);
+  stream_grad<DT, NT, U, WEIGHTED, VECP>(a, row, row, 0, a.nvec, t, y);
+}
+
+// Split backward over (row, column chunk) workgroups.
+template <int DT, int NT, int U, bool WEIGHTED, bool VECP>
+__global__ __launch_bounds__(NT) void backward_kernel(const RowArgs a) {
+  using D = Dt<DT>;
+  const int64_t b = blockIdx.x;
+  const int64_t n = b / a.chunks;
+  const int64_t c = b - n * a.chunks;
+  const int64_t per = static_cast<int64_t>(NT) * U;
+  const int64_t g_begin = c * per;
+  const int64_t g_end = min(a.nvec, g_begin + per);
+  const char* src = static_cast<const char*>(a.x) + n * a.stride * D::BYTES;
+  char* dst = static_cast<char*>(a.g) + n * a.stride * D::BYTES;
+  const int64_t y = a.target[n];
+  const int cls = row_class(y, a.V, a.ignore_index);
+  if (cls != kValid) {
+    stream_zero<DT, VECP>(dst, g_begin, g_end, NT, U);
+    return;
+  }
+  const float4 st = reinterpret_cast<const float4*>(a.stats)[n];
+  const float go = a.go[n * a.go_stride];
+  const float sigma = (a.mean ? static_cast<float>(1.0 / a.ws->W) : 1.0f) * go;
+  const float sum_w = static_cast<float>(a.ws->sum_w);
+  const RowTerms t =
+      row_terms(st.x, st.y, st.z, row_weight(a, y, WEIGHTED), sum_w, a.eps, a.eta, sigma);
+  stream_grad<DT, NT, U, WEIGHTED, VECP>(a, src, dst, g_begin, g_end, t, y);
+}
+
+template <int DT, int NT, int U, bool VECP>
+__global__ __launch_bounds__(NT) void scale_kernel(const RowArgs a) {
+  using D = Dt<DT>;
+  using G = Grp<DT, VECP>;
+  const int64_t b = blockIdx.x;
+  const int64_t n = b / a.chunks;
+  const int64_t c = b - n * a.chunks;
+  const float go = a.go[n * a.go_stride];
+  if (a.skip_if_one && go == 1.0f) return;
+  const int64_t per = static_cast<int64_t>(NT) * U;
+  const int64_t g_begin = c * per;
+  const int64_t g_end = min(a.nvec, g_begin + per);
+  char* row = static_cast<char*>(a.g) + n * a.stride * D::BYTES;
+  float f[U][G::E];
+  static_for<U>([&](auto u) {
+    const int64_t g = g_begin + u * NT + threadIdx.x;
+    if (g < g_end) G::load(row, g, f[u]);
+  });
+  static_for<U>([&](auto u) {
+    const int64_t g = g_begin + u * NT + threadIdx.x;
+    if (g < g_end) {
+#pragma unroll
+      for (int i = 0; i < G::E; ++i) f[u][i] *= go;
+      G::store(row, g, f[u]);
+    }
+  });
+}
+
+constexpr int kStreamNT = 256;
+constexpr int kStreamU = 4;
+
+template <int DT>
+int64_t groups(const Prob& p) {
+  return p.vec_ok ? p.V / Dt<DT>::VEC : p.V;
+}
+
+template <class K>
+int launch(K kernel, int64_t grid, int nt, const RowArgs& a, hipStream_t s) {
+  if (grid <= 0) return VSCE_OK;
+  if (grid > 0x7fffffffLL) return VSCE_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(nt), 0, s, a);
+  return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
+}
+
+enum Which { kStats, kFusedStream, kBackward, kScale };
+
+template <int DT, bool W, bool VECP>
+int launch_which(Which which, const Prob& p, RowArgs a, hipStream_t s) {
+  constexpr int NT = kStreamNT, U = kStreamU;
+  a.nvec = groups<DT>(p);
+  const int64_t per = static_cast<int64_t>(NT) * U;
+  a.chunks = (a.nvec + per - 1) / per;
+  switch (which) {
+    case kStats: return launch(stats_kernel<DT, NT, U, W, VECP>, p.rows, NT, a, s);
+    case kFusedStream: return launch(fused_stream_kernel<DT, NT, U, W, VECP>, p.rows, NT, a, s);
+    case kBackward:
+      return launch(backward_kernel<DT, NT, U, W, VECP>, p.rows * a.chunks, NT, a, s);
+    case kScale: return launch(scale_kernel<DT, NT, U, VECP>, p.rows * a.chunks, NT, a, s);
+  }
+  return VSCE_ERR_INVALID;
+}
+
+template <int DT>
+int dispatch(Which which, const Prob& p, const RowArgs& a, hipStream_t s) {
+  const bool w = p.weight != nullptr && which != kScale;
+  if (p.vec_ok) {
+    return w ? launch_which<DT, true, true>(which, p, a, s)
+             : launch_which<DT, false, true>(which, p, a, s);
+  }
+  return w ? launch_which<DT, true, false>(which, p, a, s)
+           : launch_which<DT, false, false>(which, p, a, s);
+}
+
+}  // namespace
+
+template <int DT>
+int stream_dt(int which, const Prob& p, const RowArgs& a, hipStream_t s) {
+  return dispatch<DT>(static_cast<Which>(which), p, a, s);
+}
+
+}  // namespace vsce

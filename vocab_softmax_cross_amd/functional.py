@@ -1,0 +1,255 @@
+"""PyTorch entry points over the C ABI: device memory and streams come from
+torch, every step of the computation runs in libvsce.so's HIP kernels.
+
+Two modes (the pages' two designs):
+
+* ``fused``: Liger-Kernel PR #1268's fused kernel.  The forward writes the
+  gradient over the logits buffer (so peak memory stays at one logits tensor,
+  per the linkedin#1290 commit message); the backward scales it in place by
+  grad_output through the raw kernel (no autograd version bump), returning at
+  once when grad_output == 1.0 (Liger-Kernel PR #1622, SKIP_IF_ONE).  After the
+  call the logits tensor holds the gradient.
+* ``split``: TransformerEngine PR #2325's split.  The forward saves per-row
+  statistics (m, d', x_y, S) and leaves the logits intact; the backward
+  recomputes the gradient in fp32 from them and writes it in the input type.
+
+Nothing here synchronizes with the host: the normalizers and the loss
+reduction stay on the device.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+_DTYPES = {torch.float32: L.F32, torch.bfloat16: L.BF16, torch.float16: L.F16}
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _rows_view(logits: torch.Tensor) -> torch.Tensor:
+    """[..., V] -> a [rows, V] view with unit class stride (no copy)."""
+    if logits.dim() < 2:
+        raise ValueError("logits must have shape [..., V]")
+    if logits.stride(-1) != 1:
+        raise ValueError("logits must be contiguous along the class dimension")
+    if logits.dim() == 2:
+        return logits
+    return logits.view(-1, logits.shape[-1])
+
+
+def make_problem(x2d: torch.Tensor, target: torch.Tensor, weight: Optional[torch.Tensor],
+                 ignore_index: int, label_smoothing: float, reduction: str) -> L.Problem:
+    if x2d.dtype not in _DTYPES:
+        raise TypeError(f"unsupported logits dtype {x2d.dtype}")
+    if target.dtype != torch.int64 or target.device != x2d.device:
+        raise TypeError("target must be an int64 tensor on the logits' device")
+    if not target.is_contiguous() or target.numel() != x2d.shape[0]:
+        raise ValueError("target must be contiguous with one entry per row")
+    if weight is not None:
+        if weight.dtype != torch.float32 or not weight.is_contiguous() or weight.numel() != x2d.shape[1]:
+            raise ValueError("class weights must be a contiguous float32 [V] tensor")
+    p = L.Problem()
+    p.rows = x2d.shape[0]
+    p.vocab = x2d.shape[1]
+    p.row_stride = x2d.stride(0) if x2d.shape[0] > 1 else x2d.shape[1]
+    p.dtype = _DTYPES[x2d.dtype]
+    p.reduction = L.REDUCTIONS[reduction]
+    p.target = target.data_ptr() or None
+    p.class_weight = None if weight is None else weight.data_ptr()
+    p.ignore_index = int(ignore_index)
+    p.label_smoothing = float(label_smoothing)
+    p.reserved = 0
+    return p
+
+
+def workspace_for(rows: int, device) -> torch.Tensor:
+    return torch.empty(L.vsce_workspace_bytes(rows), dtype=torch.uint8, device=device)
+
+
+def _outputs(rows: int, reduction: str, device, row_loss: bool, accuracy: bool):
+    f32 = dict(dtype=torch.float32, device=device)
+    loss = torch.empty(max(rows, 1) if reduction == "none" else 1, **f32)
+    rl = torch.empty(max(rows, 1), **f32) if row_loss else None
+    acc = torch.empty(max(rows, 1), **f32) if accuracy else None
+    accm = torch.empty(1, **f32) if accuracy else None
+    o = L.Outputs()
+    o.loss = loss.data_ptr()
+    o.row_loss = None if rl is None else rl.data_ptr()
+    o.token_acc = None if acc is None else acc.data_ptr()
+    o.acc_mean = None if accm is None else accm.data_ptr()
+    res = {
+        "loss": loss[:rows] if reduction == "none" else loss[0],
+        "row_loss": None if rl is None else rl[:rows],
+        "token_acc": None if acc is None else acc[:rows],
+        "acc_mean": None if accm is None else accm[0],
+    }
+    return o, res
+
+
+def forward_fused_inplace(logits: torch.Tensor, target: torch.Tensor,
+                          weight: Optional[torch.Tensor] = None, ignore_index: int = -100,
+                          label_smoothing: float = 0.0, reduction: str = "mean",
+                          row_loss: bool = False, accuracy: bool = False,
+                          workspace: Optional[torch.Tensor] = None) -> dict:
+    """ce_forward_fused_inplace: loss outputs; the logits buffer now holds the
+    gradient of the reduced loss for grad_output = 1."""
+    x = _rows_view(logits)
+    p = make_problem(x, target.reshape(-1), weight, ignore_index, label_smoothing, reduction)
+    ws = workspace if workspace is not None else workspace_for(p.rows, x.device)
+    o, res = _outputs(p.rows, reduction, x.device, row_loss, accuracy)
+    L.ce_forward_fused_inplace(p, x.data_ptr(), o, ws.data_ptr(), _stream(x))
+    res["workspace"] = ws
+    return res
+
+
+def forward_stats(logits: torch.Tensor, target: torch.Tensor,
+                  weight: Optional[torch.Tensor] = None, ignore_index: int = -100,
+                  label_smoothing: float = 0.0, reduction: str = "mean",
+                  row_loss: bool = False, accuracy: bool = False,
+                  workspace: Optional[torch.Tensor] = None) -> dict:
+    """ce_forward_stats: loss outputs plus the [rows, 4] statistics."""
+    x = _rows_view(logits)
+    p = make_problem(x, target.reshape(-1), weight, ignore_index, label_smoothing, reduction)
+    ws = workspace if workspace is not None else workspace_for(p.rows, x.device)
+    stats = torch.empty((max(p.rows, 1), L.STATS_STRIDE), dtype=torch.float32, device=x.device)
+    o, res = _outputs(p.rows, reduction, x.device, row_loss, accuracy)
+    L.ce_forward_stats(p, x.data_ptr(), stats.data_ptr(), o, ws.data_ptr(), _stream(x))
+    res["stats"] = stats[:p.rows]
+    res["workspace"] = ws
+    return res
+
+
+def _grad_output(go: torch.Tensor, rows: int, reduction: str, device):
+    go = go.detach()
+    if go.device != device:
+        raise ValueError("grad_output must live on the logits' device")
+    go = go.to(torch.float32).reshape(-1).contiguous()
+    if go.numel() == 1:
+        return go, 0
+    if reduction == "none" and go.numel() == rows:
+        return go, 1
+    raise ValueError("grad_output must be a scalar or hold one value per row")
+
+
+def backward_from_stats(logits: torch.Tensor, target: torch.Tensor, stats: torch.Tensor,
+                        grad_output: torch.Tensor, workspace: torch.Tensor,
+                        weight: Optional[torch.Tensor] = None, ignore_index: int = -100,
+                        label_smoothing: float = 0.0, reduction: str = "mean",
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ce_backward_from_stats: the gradient in the logits' type (``out`` may be
+    the logits themselves for an in-place backward)."""
+    x = _rows_view(logits)
+    p = make_problem(x, target.reshape(-1), weight, ignore_index, label_smoothing, reduction)
+    g = (torch.empty_strided(x.size(), x.stride(), dtype=x.dtype, device=x.device)
+         if out is None else _rows_view(out))
+    if g.shape != x.shape or g.dtype != x.dtype or g.stride() != x.stride():
+        raise ValueError("out must match the logits' shape, dtype and strides")
+    go, stride = _grad_output(grad_output, p.rows, reduction, x.device)
+    L.ce_backward_from_stats(p, x.data_ptr(), g.data_ptr(), stats.data_ptr(), go.data_ptr(),
+                             stride, workspace.data_ptr(), _stream(x))
+    return g.view(logits.shape) if out is None else out
+
+
+def scale_grad(grad: torch.Tensor, grad_output: torch.Tensor, reduction: str = "mean",
+               skip_if_one: bool = True) -> torch.Tensor:
+    """ce_scale_grad: grad <- grad * grad_output in place (skipped where it is 1.0)."""
+    g = _rows_view(grad)
+    rows, V = g.shape
+    go, stride = _grad_output(grad_output, rows, reduction, g.device)
+    L.ce_scale_grad(g.data_ptr(), rows, V, g.stride(0) if rows > 1 else V, _DTYPES[g.dtype],
+                    go.data_ptr(), stride, 1 if skip_if_one else 0, _stream(g))
+    return grad
+
+
+class FusedCrossEntropy(torch.autograd.Function):
+    """Fused mode: gradient computed in the forward, over the logits buffer."""
+
+    @staticmethod
+    def forward(ctx, logits, target, weight, ignore_index, label_smoothing, reduction, accuracy):
+        res = forward_fused_inplace(logits, target, weight, ignore_index, label_smoothing,
+                                    reduction, accuracy=accuracy)
+        # The buffer now holds the gradient; it is written through raw pointers,
+        # so autograd's version counter is untouched.
+        ctx.save_for_backward(logits.detach())
+        ctx.reduction = reduction
+        ctx.grad_scaled_in_place = False
+        ctx.workspace = res["workspace"]
+        if accuracy:
+            ctx.mark_non_differentiable(res["token_acc"], res["acc_mean"])
+            return res["loss"], res["token_acc"], res["acc_mean"]
+        return res["loss"]
+
+    @staticmethod
+    def backward(ctx, grad_loss, *unused):
+        if ctx.grad_scaled_in_place:
+            raise RuntimeError("the fused cross-entropy gradient was already scaled in place; "
+                               "a second backward (retain_graph=True) is not supported")
+        ctx.grad_scaled_in_place = True
+        (grad,) = ctx.saved_tensors
+        scale_grad(grad, grad_loss, ctx.reduction, skip_if_one=True)
+        return grad, None, None, None, None, None, None
+
+
+class SplitCrossEntropy(torch.autograd.Function):
+    """Split mode: statistics in the forward, fp32 gradient in the backward."""
+
+    @staticmethod
+    def forward(ctx, logits, target, weight, ignore_index, label_smoothing, reduction, accuracy,
+                inplace_backward):
+        res = forward_stats(logits, target, weight, ignore_index, label_smoothing, reduction,
+                            accuracy=accuracy)
+        ctx.save_for_backward(logits, target, res["stats"], res["workspace"],
+                              *([] if weight is None else [weight]))
+        ctx.args = (ignore_index, label_smoothing, reduction, weight is not None, inplace_backward)
+        if accuracy:
+            ctx.mark_non_differentiable(res["token_acc"], res["acc_mean"])
+            return res["loss"], res["token_acc"], res["acc_mean"]
+        return res["loss"]
+
+    @staticmethod
+    def backward(ctx, grad_loss, *unused):
+        logits, target, stats, ws, *w = ctx.saved_tensors
+        ignore_index, ls, reduction, weighted, inplace = ctx.args
+        g = backward_from_stats(logits, target, stats, grad_loss, ws, w[0] if weighted else None,
+                                ignore_index, ls, reduction,
+                                out=logits.detach() if inplace else None)
+        return g, None, None, None, None, None, None, None
+
+
+def cross_entropy(logits: torch.Tensor, target: torch.Tensor, weight: Optional[torch.Tensor] = None,
+                  ignore_index: int = -100, label_smoothing: float = 0.0,
+                  reduction: str = "mean", *, mode: str = "fused", return_accuracy: bool = False,
+                  inplace_backward: bool = False):
+    """Softmax cross-entropy over the last dimension of ``logits``.
+
+    ``mode="fused"`` overwrites ``logits`` with the gradient during the
+    forward; ``mode="split"`` keeps them (and with ``inplace_backward`` writes
+    the gradient over them in the backward).  With ``return_accuracy`` also
+    returns the per-token accuracy and its mean over non-ignored rows.
+    """
+    if reduction not in L.REDUCTIONS:
+        raise ValueError(f"reduction must be one of {tuple(L.REDUCTIONS)}")
+    if mode == "fused":
+        return FusedCrossEntropy.apply(logits, target, weight, ignore_index, label_smoothing,
+                                       reduction, return_accuracy)
+    if mode == "split":
+        return SplitCrossEntropy.apply(logits, target, weight, ignore_index, label_smoothing,
+                                       reduction, return_accuracy, inplace_backward)
+    raise ValueError("mode must be 'fused' or 'split'")
+
+
+def status(workspace: torch.Tensor) -> dict:
+    """Reads the workspace header (a device-to-host copy: synchronizes)."""
+    h = workspace[:L.WS_HEADER_BYTES].cpu()
+    return {
+        "W": float(h[L.WS_W:L.WS_W + 8].view(torch.float64)[0]),
+        "sum_w": float(h[L.WS_SUM_W:L.WS_SUM_W + 8].view(torch.float64)[0]),
+        "n_valid": int(h[L.WS_N_VALID:L.WS_N_VALID + 8].view(torch.int64)[0]),
+        "n_invalid": int(h[L.WS_N_INVALID:L.WS_N_INVALID + 8].view(torch.int64)[0]),
+        "status": int(h[L.WS_STATUS:L.WS_STATUS + 4].view(torch.int32)[0]),
+    }
