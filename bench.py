@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Throughput of the fused softmax cross-entropy hot path on one MI355X.
+
+One step = one forward + backward of the whole path over one batch through
+the C ABI: the device-side normalizers, the fused row kernel (loss, accuracy
+and the gradient written over the logits), the loss reduction, and the
+grad_output scale (a no-op launch at grad_output = 1.0).  The default workload
+is the LLM head: BT = 8192 rows of V = 128256 bf16 logits ~ N(0, 2), 5% of
+rows ignored, label smoothing 0.1, mean reduction.
+
+Each step gets its own freshly written copy of the logits (a ring of
+pre-filled buffers in HBM), because the fused forward overwrites its input
+with the gradient.  The run prints one JSON line:
+  value      rows per second of whole fwd+bwd steps (wall clock over K steps)
+  roofline   the row kernel alone: algorithmic bytes per launch / its mean
+             launch time from HIP events recorded around that launch
+  cpu_baseline  the fp64 oracle on a bounded sample of the same rows
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+RING_CAP_BYTES = 120 << 30  # HBM for pre-filled logits copies
+PROFILE = os.path.join(ROOT, "profiles", "traffic_fused_resident_llm_head.md")
+KERNEL_SOURCES = ["common.h", "rowmath.h", "fused_impl.h", "fused_bf16.hip"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llm_head")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-modes", action="store_true",
+                    help="skip the split-mode and grad_output != 1 context timings")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle time budget for the cpu_baseline sample")
+    return ap.parse_args()
+
+
+class Hip:
+    """The few HIP runtime calls the bench needs (events), via ctypes."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, e: int) -> None:
+        self.lib.hipEventDestroy(e)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "vocab_softmax_cross_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch of the row kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel sources."""
+    if not os.path.exists(PROFILE):
+        return None
+    vals = {}
+    with open(PROFILE) as fh:
+        for line in fh:
+            if line.startswith("traffic:"):
+                for kv in line[len("traffic:"):].split():
+                    k, _, v = kv.partition("=")
+                    vals[k] = v
+    if vals.get("workload") != workload or vals.get("kernel_sources") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, tgt, budget_s: float):
+    """The oracle (fp64 forward + gradient + rounding) on consecutive row
+    chunks until about `budget_s` of oracle time; rows per second."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    chunk = 512
+    done, spent = 0, 0.0
+    while done < wl.BT and spent < budget_s:
+        r1 = min(wl.BT, done + chunk)
+        x = W.as_f64(W.logits_rows(wl, done, r1, tgt))
+        t0 = time.perf_counter()
+        oracle.normalizer(tgt, wl.V, None)
+        r = oracle.rows(x, tgt[done:r1], None, -100, wl.label_smoothing, want_grad=True)
+        g = r.grad * (1.0 / max(1, int(np.sum(tgt != -100))))
+        oracle.round_to(g, wl.dtype)
+        spent += time.perf_counter() - t0
+        done = r1
+        del x, r, g
+    return {"value": done / spent, "unit": "rows/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"first {done} of {wl.BT} rows ({done * wl.V:.3g} elements), fp64 "
+                      f"forward + gradient + rounding to {wl.dtype}, {spent:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(rows shard across GPUs with no exchange; see DESIGN.md). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import vocab_softmax_cross_amd._lib as L
+    import workloads as W
+
+    L.load()
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS[args.workload]
+    K, Wu = args.steps, args.warmup
+    tgt = W.targets(wl)
+    n_valid = int(np.sum((tgt >= 0) & (tgt < wl.V)))
+    row_bytes = wl.V * wl.elem_bytes
+
+    t0 = time.perf_counter()
+    host = W.logits(wl, tgt)
+    gen_s = time.perf_counter() - t0
+    pristine = host.to(dev)
+    del host
+    ring_n = max(1, min(K + Wu, RING_CAP_BYTES // max(1, wl.BT * row_bytes)))
+    ring = [torch.empty_like(pristine) for _ in range(ring_n)]
+
+    def refill():
+        for b in ring:
+            b.copy_(pristine)
+        torch.cuda.synchronize()
+
+    t = torch.from_numpy(tgt).to(dev)
+    w = W.class_weights(wl)
+    wt = None if w is None else torch.from_numpy(w).to(dev)
+    red = wl.reductions[0]
+    ws = torch.empty(L.vsce_workspace_bytes(wl.BT), dtype=torch.uint8, device=dev)
+    loss = torch.empty(wl.BT if red == "none" else 1, dtype=torch.float32, device=dev)
+    stats = torch.empty((wl.BT, L.STATS_STRIDE), dtype=torch.float32, device=dev)
+    go_one = torch.ones(1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    dt = {"f32": L.F32, "bf16": L.BF16, "f16": L.F16}[wl.dtype]
+
+    def problem(buf):
+        p = L.Problem()
+        p.rows, p.vocab, p.row_stride = wl.BT, wl.V, wl.V
+        p.dtype, p.reduction = dt, L.REDUCTIONS[red]
+        p.target = t.data_ptr()
+        p.class_weight = None if wt is None else wt.data_ptr()
+        p.ignore_index, p.label_smoothing, p.reserved = -100, wl.label_smoothing, 0
+        return p
+
+    problems = [problem(b) for b in ring]
+    outs = L.Outputs()
+    outs.loss = loss.data_ptr()
+    hip = Hip()
+    ev = [(hip.event(), hip.event()) for _ in range(K)]
+
+    def fused_step(i, go, timed_events=None):
+        b = ring[i % ring_n]
+        if timed_events is None:
+            L.ce_forward_fused_inplace(problems[i % ring_n], b.data_ptr(), outs, ws.data_ptr(),
+                                       stream)
+        else:
+            L.ce_forward_fused_inplace_timed(problems[i % ring_n], b.data_ptr(), outs,
+                                             ws.data_ptr(), stream, *timed_events)
+        L.ce_scale_grad(b.data_ptr(), wl.BT, wl.V, wl.V, dt, go.data_ptr(),
+                        1 if go.numel() > 1 else 0, 1, stream)
+
+    def split_step(i, go):
+        b = ring[i % ring_n]
+        L.ce_forward_stats(problems[i % ring_n], b.data_ptr(), stats.data_ptr(), outs,
+                           ws.data_ptr(), stream)
+        L.ce_backward_from_stats(problems[i % ring_n], b.data_ptr(), b.data_ptr(),
+                                 stats.data_ptr(), go.data_ptr(), 1 if go.numel() > 1 else 0,
+                                 ws.data_ptr(), stream)
+
+    def timed(step_fn, go, events=False):
+        refill()
+        for i in range(Wu):
+            step_fn(i, go)
+        torch.cuda.synchronize()
+        t_begin = time.perf_counter()
+        for i in range(K):
+            if events:
+                step_fn(Wu + i, go, ev[i])
+            else:
+                step_fn(Wu + i, go)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t_begin
+
+    wall = timed(fused_step, go_one, events=True)
+    kernel_ms = [hip.elapsed_ms(a, b) for a, b in ev]
+    mean_kernel_s = float(np.mean(kernel_ms)) / 1e3
+
+    # algorithmic bytes: valid rows read + write, ignored rows write only,
+    # plus the int64 target and fp32 loss of every row
+    kernel_bytes = (2 * n_valid + (wl.BT - n_valid)) * row_bytes + 12 * wl.BT
+    step_bytes = kernel_bytes + 8 * wl.BT + 4 * wl.BT  # normalizer + reduction reads
+    ms_per_step = wall / K * 1e3
+    value = wl.BT * K / wall
+    achieved = kernel_bytes / mean_kernel_s / 1e9
+
+    extra = {}
+    if not args.no_extra_modes:
+        go37 = torch.full((1,), 0.37, dtype=torch.float32, device=dev)
+        w37 = timed(fused_step, go37)
+        wsp = timed(split_step, go_one)
+        # the scale pass reads and writes every row
+        extra["fused_go0.37"] = {"ms_per_step": round(w37 / K * 1e3, 4),
+                                 "rows_per_s": round(wl.BT * K / w37, 1),
+                                 "alg_GBps": round((kernel_bytes + 2 * wl.BT * row_bytes) * K
+                                                   / w37 / 1e9, 1)}
+        extra["split_go1"] = {"ms_per_step": round(wsp / K * 1e3, 4),
+                              "rows_per_s": round(wl.BT * K / wsp, 1),
+                              "alg_GBps": round((3 * n_valid * row_bytes
+                                                 + (wl.BT - n_valid) * row_bytes) * K
+                                                / wsp / 1e9, 1)}
+
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, tgt, args.cpu_seconds)
+
+    line = {
+        "metric": "fwd+bwd rows/s and HBM GB/s (% of peak) at BT=8192, V=128256 bf16",
+        "value": round(value, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wu,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",  # arithmetic type; the logits buffer type is in config
+        "data": "synthetic",
+        "config": {"workload": wl.name, "BT": wl.BT, "V": wl.V, "logits": wl.dtype,
+                   "label_smoothing": wl.label_smoothing, "ignored_rows": wl.BT - n_valid,
+                   "reduction": red, "grad_output": 1.0, "mode": "fused in-place"},
+        "step_GBps": round(step_bytes * K / wall / 1e9, 1),
+        "step_pct_of_hbm_peak": round(100 * step_bytes * K / wall / 1e9 / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": stored_traffic(wl.name),
+                     "kernel": "fused_resident_kernel", "bytes_per_launch": kernel_bytes,
+                     "mean_launch_ms": round(mean_kernel_s * 1e3, 4)},
+        "modes": extra,
+        "cpu_baseline": cpu,
+        "input_gen_s": round(gen_s, 1),
+        "ring_buffers": ring_n,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

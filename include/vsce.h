@@ -162,6 +162,18 @@ int ce_forward_fused_inplace(const vsce_problem *problem, void *logits_inout,
                              hipStream_t stream);
 
 /*
+ * Measurement variant of ce_forward_fused_inplace: identical work, plus
+ * hipEventRecord(begin) and hipEventRecord(end) on `stream` immediately
+ * before and after the launch of the row kernel (not the normalizer and
+ * reduction launches around it), so that the caller can time that kernel
+ * alone with hipEventElapsedTime.  The events are created and owned by the
+ * caller; either may be NULL.  Returns VSCE_ERR_LAUNCH if recording fails.
+ */
+int ce_forward_fused_inplace_timed(const vsce_problem *problem, void *logits_inout,
+                                   const vsce_outputs *out, void *workspace,
+                                   hipStream_t stream, hipEvent_t begin, hipEvent_t end);
+
+/*
  * Split forward (TransformerEngine PR #2325 online_softmax_kernel +
  * cross_entropy_forward_kernel): reads the logits once and writes the loss
  * outputs and `stats` ([rows][VSCE_STATS_STRIDE] fp32: m, d', x[y], S; rows

@@ -23,7 +23,8 @@ STATUS_BAD_TARGET = 1
 STATS_STRIDE = 4
 WS_W, WS_SUM_W, WS_N_VALID, WS_N_INVALID, WS_STATUS, WS_HEADER_BYTES = 0, 8, 16, 24, 32, 256
 
-EXPORTS = ("vsce_workspace_bytes", "ce_forward_fused_inplace", "ce_forward_stats",
+EXPORTS = ("vsce_workspace_bytes", "ce_forward_fused_inplace", "ce_forward_fused_inplace_timed",
+           "ce_forward_stats",
            "ce_backward_from_stats", "ce_scale_grad", "vsce_strerror", "vsce_version")
 
 
@@ -76,6 +77,9 @@ def load() -> ctypes.CDLL:
     lib.vsce_workspace_bytes.restype = c_size_t
     lib.ce_forward_fused_inplace.argtypes = [P(Problem), c_void_p, P(Outputs), c_void_p, c_void_p]
     lib.ce_forward_fused_inplace.restype = ctypes.c_int
+    lib.ce_forward_fused_inplace_timed.argtypes = [P(Problem), c_void_p, P(Outputs), c_void_p,
+                                                   c_void_p, c_void_p, c_void_p]
+    lib.ce_forward_fused_inplace_timed.restype = ctypes.c_int
     lib.ce_forward_stats.argtypes = [P(Problem), c_void_p, c_void_p, P(Outputs), c_void_p, c_void_p]
     lib.ce_forward_stats.restype = ctypes.c_int
     lib.ce_backward_from_stats.argtypes = [P(Problem), c_void_p, c_void_p, c_void_p, c_void_p,
@@ -110,6 +114,12 @@ def ce_forward_fused_inplace(problem: Problem, logits_inout: int, outputs: Outpu
                              workspace: int, stream: int) -> int:
     return _check("ce_forward_fused_inplace", load().ce_forward_fused_inplace(
         ctypes.byref(problem), logits_inout, ctypes.byref(outputs), workspace, stream))
+
+
+def ce_forward_fused_inplace_timed(problem: Problem, logits_inout: int, outputs: Outputs,
+                                   workspace: int, stream: int, begin: int, end: int) -> int:
+    return _check("ce_forward_fused_inplace_timed", load().ce_forward_fused_inplace_timed(
+        ctypes.byref(problem), logits_inout, ctypes.byref(outputs), workspace, stream, begin, end))
 
 
 def ce_forward_stats(problem: Problem, logits: int, stats: int, outputs: Outputs,

@@ -103,10 +103,12 @@ RowArgs row_args(const Prob& p, void* x, const vsce_outputs* out, void* workspac
 }
 
 int forward_common(const Prob& p, RowArgs a, const vsce_outputs* out, void* workspace,
-                   bool fused, hipStream_t stream) {
+                   bool fused, hipStream_t stream, hipEvent_t ev_begin = nullptr,
+                   hipEvent_t ev_end = nullptr) {
   WsHeader* hdr = reinterpret_cast<WsHeader*>(workspace);
   int rc = launch_prologue(p, hdr, stream);
   if (rc != VSCE_OK) return rc;
+  if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return VSCE_ERR_LAUNCH;
   if (p.rows > 0) {
     if (fused) {
       rc = launch_fused_resident(p, a, stream);
@@ -116,6 +118,7 @@ int forward_common(const Prob& p, RowArgs a, const vsce_outputs* out, void* work
     }
     if (rc != VSCE_OK) return rc;
   }
+  if (ev_end && hipEventRecord(ev_end, stream) != hipSuccess) return VSCE_ERR_LAUNCH;
   return launch_finalize(p, a.loss_rows, a.acc_rows, out->loss, out->acc_mean, hdr, stream);
 }
 
@@ -176,6 +179,18 @@ int ce_forward_fused_inplace(const vsce_problem* problem, void* logits_inout,
   if (rc != VSCE_OK) return rc;
   return forward_common(p, row_args(p, logits_inout, out, workspace), out, workspace, true,
                         stream);
+}
+
+int ce_forward_fused_inplace_timed(const vsce_problem* problem, void* logits_inout,
+                                   const vsce_outputs* out, void* workspace, hipStream_t stream,
+                                   hipEvent_t begin, hipEvent_t end) {
+  Prob p;
+  int rc = check_problem(problem, logits_inout, p);
+  if (rc == VSCE_OK) rc = check_outputs(out);
+  if (rc == VSCE_OK) rc = check_workspace(workspace);
+  if (rc != VSCE_OK) return rc;
+  return forward_common(p, row_args(p, logits_inout, out, workspace), out, workspace, true,
+                        stream, begin, end);
 }
 
 int ce_forward_stats(const vsce_problem* problem, const void* logits, float* stats,

@@ -31,6 +31,8 @@ pages use random logits only, so no dataset is stood in for.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Optional, Tuple
 
@@ -39,6 +41,7 @@ import torch
 
 BLOCK = 256
 IGNORE_INDEX = -100
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
@@ -161,13 +164,21 @@ def logits_rows(wl: Workload, r0: int, r1: int, tgt: Optional[np.ndarray] = None
     out = torch.empty((max(0, r1 - r0), wl.V), dtype=wl.torch_dtype)
     if r1 <= r0:
         return out
-    for b in range(r0 // BLOCK, (r1 - 1) // BLOCK + 1):
+
+    def fill(b):
         blk = _raw_block(wl, b)
         s0 = b * BLOCK
         if not np.all(np.isnan(prob[s0:s0 + blk.shape[0]])):
             _place_targets(wl, blk, s0, tgt, prob)
         lo, hi = max(r0, s0), min(r1, s0 + blk.shape[0])
         out[lo - r0:hi - r0] = blk[lo - s0:hi - s0]
+
+    blocks = range(r0 // BLOCK, (r1 - 1) // BLOCK + 1)
+    if len(blocks) == 1:
+        fill(blocks[0])
+    else:  # blocks are independent streams: draw them on several threads
+        with ThreadPoolExecutor(min(len(blocks), _THREADS)) as ex:
+            list(ex.map(fill, blocks))
     return out
 
 
