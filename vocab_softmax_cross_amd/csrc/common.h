@@ -150,21 +150,36 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
 }
+// Cache policy of the logits and gradient streams: non-temporal (the "nt"
+// bit), since every byte is touched once per pass and the tensors are far
+// larger than the caches.
+constexpr int kNT = 2;
+
 __device__ inline uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNT);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                    const uint4 v) {
   const u32x4_t w = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, kNT);
 }
 // 16 bytes per lane straight into LDS; lane i of the wavefront lands at
 // lds_wave + 16 i, so `lds_wave` must be the same for the whole wavefront.
 __device__ inline void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_wave, uint32_t voff,
                                       uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave,
-                                           16, voff, soff, 0, 0);
+                                           16, voff, soff, 0, kNT);
+}
+
+// Plain-pointer 16-byte loads and stores with the same non-temporal policy.
+__device__ inline uint4 nt_load16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline void nt_store16(void* p, const uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, static_cast<u32x4_t*>(p));
 }
 
 // Hides a register-held vector from the optimizer so that a pass over the

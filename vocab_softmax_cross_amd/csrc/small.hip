@@ -40,6 +40,8 @@ __global__ __launch_bounds__(kSmallNT) void prologue_kernel(const int64_t* targe
                                                            int64_t ignore_index, WsHeader* ws) {
   __shared__ double sh[kSmallNT / kWave];
   double W = 0.0, nv = 0.0, ni = 0.0, sw = 0.0;
+  // Unrolled so that several independent target loads are in flight.
+#pragma unroll 8
   for (int64_t n = threadIdx.x; n < rows; n += kSmallNT) {
     const int64_t y = target[n];
     const int cls = row_class(y, V, ignore_index);
@@ -51,6 +53,7 @@ __global__ __launch_bounds__(kSmallNT) void prologue_kernel(const int64_t* targe
     }
   }
   if (weight) {
+#pragma unroll 8
     for (int64_t c = threadIdx.x; c < V; c += kSmallNT) sw += static_cast<double>(weight[c]);
   }
   W = block_sum_d(W, sh);
@@ -75,6 +78,7 @@ __global__ __launch_bounds__(kSmallNT) void finalize_kernel(const float* loss_ro
   __shared__ double sh[kSmallNT / kWave];
   if (red != VSCE_REDUCTION_NONE) {
     double t = 0.0;
+#pragma unroll 8
     for (int64_t n = threadIdx.x; n < rows; n += kSmallNT) t += static_cast<double>(loss_rows[n]);
     t = block_sum_d(t, sh);
     if (threadIdx.x == 0) {
@@ -88,6 +92,7 @@ __global__ __launch_bounds__(kSmallNT) void finalize_kernel(const float* loss_ro
   }
   if (acc_mean_out) {
     double h = 0.0;
+#pragma unroll 8
     for (int64_t n = threadIdx.x; n < rows; n += kSmallNT) h += static_cast<double>(acc_rows[n]);
     h = block_sum_d(h, sh);
     if (threadIdx.x == 0) {

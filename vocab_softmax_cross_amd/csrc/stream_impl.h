@@ -39,14 +39,14 @@ struct Grp {
   static constexpr int E = VECP ? D::VEC : 1;
   __device__ static inline void load(const char* row, int64_t g, float (&f)[E]) {
     if constexpr (VECP) {
-      D::unpack(reinterpret_cast<const uint4*>(row)[g], f);
+      D::unpack(nt_load16(row + g * 16), f);
     } else {
       f[0] = D::load1(row, g);
     }
   }
   __device__ static inline void store(char* row, int64_t g, const float (&f)[E]) {
     if constexpr (VECP) {
-      reinterpret_cast<uint4*>(row)[g] = D::pack(f);
+      nt_store16(row + g * 16, D::pack(f));
     } else {
       D::store1(row, g, f[0]);
     }
@@ -283,36 +283,43 @@ __global__ __launch_bounds__(NT) void backward_kernel(const RowArgs a) {
   stream_grad<DT, NT, U, WEIGHTED, VECP>(a, src, dst, g_begin, g_end, t, y);
 }
 
+// Grid-stride over (row, column chunk) work items, so that a grad_output of
+// 1.0 costs one small launch: every workgroup reads the scalar once and
+// returns.
 template <int DT, int NT, int U, bool VECP>
 __global__ __launch_bounds__(NT) void scale_kernel(const RowArgs a) {
   using D = Dt<DT>;
   using G = Grp<DT, VECP>;
-  const int64_t b = blockIdx.x;
-  const int64_t n = b / a.chunks;
-  const int64_t c = b - n * a.chunks;
-  const float go = a.go[n * a.go_stride];
-  if (a.skip_if_one && go == 1.0f) return;
+  if (a.skip_if_one && a.go_stride == 0 && a.go[0] == 1.0f) return;
   const int64_t per = static_cast<int64_t>(NT) * U;
-  const int64_t g_begin = c * per;
-  const int64_t g_end = min(a.nvec, g_begin + per);
-  char* row = static_cast<char*>(a.g) + n * a.stride * D::BYTES;
-  float f[U][G::E];
-  static_for<U>([&](auto u) {
-    const int64_t g = g_begin + u * NT + threadIdx.x;
-    if (g < g_end) G::load(row, g, f[u]);
-  });
-  static_for<U>([&](auto u) {
-    const int64_t g = g_begin + u * NT + threadIdx.x;
-    if (g < g_end) {
+  const int64_t items = a.rows * a.chunks;
+  for (int64_t b = blockIdx.x; b < items; b += gridDim.x) {
+    const int64_t n = b / a.chunks;
+    const int64_t c = b - n * a.chunks;
+    const float go = a.go[n * a.go_stride];
+    if (a.skip_if_one && go == 1.0f) continue;
+    const int64_t g_begin = c * per;
+    const int64_t g_end = min(a.nvec, g_begin + per);
+    char* row = static_cast<char*>(a.g) + n * a.stride * D::BYTES;
+    float f[U][G::E];
+    static_for<U>([&](auto u) {
+      const int64_t g = g_begin + u * NT + threadIdx.x;
+      if (g < g_end) G::load(row, g, f[u]);
+    });
+    static_for<U>([&](auto u) {
+      const int64_t g = g_begin + u * NT + threadIdx.x;
+      if (g < g_end) {
 #pragma unroll
-      for (int i = 0; i < G::E; ++i) f[u][i] *= go;
-      G::store(row, g, f[u]);
-    }
-  });
+        for (int i = 0; i < G::E; ++i) f[u][i] *= go;
+        G::store(row, g, f[u]);
+      }
+    });
+  }
 }
 
 constexpr int kStreamNT = 256;
 constexpr int kStreamU = 4;
+constexpr int64_t kScaleGrid = 2048;  // 8 workgroups per CU
 
 template <int DT>
 int64_t groups(const Prob& p) {
@@ -340,7 +347,8 @@ int launch_which(Which which, const Prob& p, RowArgs a, hipStream_t s) {
     case kFusedStream: return launch(fused_stream_kernel<DT, NT, U, W, VECP>, p.rows, NT, a, s);
     case kBackward:
       return launch(backward_kernel<DT, NT, U, W, VECP>, p.rows * a.chunks, NT, a, s);
-    case kScale: return launch(scale_kernel<DT, NT, U, VECP>, p.rows * a.chunks, NT, a, s);
+    case kScale:
+      return launch(scale_kernel<DT, NT, U, VECP>, min(p.rows * a.chunks, kScaleGrid), NT, a, s);
   }
   return VSCE_ERR_INVALID;
 }
