@@ -279,7 +279,7 @@ def main():
         "step_pct_of_hbm_peak": round(100 * step_bytes * K / wall / 1e9 / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": stored_traffic(wl.name),
+                     "traffic": stored_traffic(wl.name), "traffic_unit": "bytes/launch",
                      "kernel": "fused_resident_kernel", "bytes_per_launch": kernel_bytes,
                      "mean_launch_ms": round(mean_kernel_s * 1e3, 4)},
         "modes": extra,
