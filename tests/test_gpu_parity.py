@@ -261,9 +261,12 @@ def test_ragged_vocab_bf16(V, mode):
     check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0), xh, tgt, w)
 
 
-@pytest.mark.parametrize("V", [8, 64, 2048, 16384, 32768, 65536, 131072, 163840, 262144])
+@pytest.mark.parametrize("V", [8, 64, 2048, 16384, 32768, 65536, 128264, 130568, 131072, 163840,
+                               262144])
 def test_every_resident_shape(V):
-    """One row length per on-chip shape boundary, with a ragged last slot."""
+    """One row length per on-chip shape boundary (V - 8: a ragged last
+    slot), including the exact capacity of the shape with a partial LDS slot
+    (130560) and the headline row length (128256)."""
     wl = _small("llm_head", 9, V - 8 if V > 8 else V)
     out, xh, tgt, w = run(wl, "fused", "mean", 1.0, accuracy=True)
     check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0), xh, tgt, w)

@@ -51,6 +51,10 @@ struct Dt<VSCE_F32> {
     f[2] = __uint_as_float(v.z);
     f[3] = __uint_as_float(v.w);
   }
+  // one 32-bit word = EPW elements
+  static constexpr int EPW = 1;
+  __device__ static inline void word_fresh(uint32_t w, float (&f)[1]) { f[0] = __uint_as_float(w); }
+  __device__ static inline uint32_t pack_word(const float (&f)[1]) { return __float_as_uint(f[0]); }
   __device__ static inline uint4 pack(const float (&f)[4]) {
     return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
                       __float_as_uint(f[3]));
@@ -81,6 +85,22 @@ struct Dt<VSCE_BF16> {
       f[2 * i] = __uint_as_float(w[i] << 16);
       f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
+  }
+  // The same conversion of one 32-bit word as volatile asm: each pass over a
+  // register-held row unpacks again instead of the compiler keeping the fp32
+  // copies of an earlier pass alive, which would double the registers the
+  // row needs.
+  static constexpr int EPW = 2;
+  __device__ static inline void word_fresh(uint32_t w, float (&f)[2]) {
+    uint32_t lo, hi;
+    asm volatile("v_lshlrev_b32 %0, 16, %2\n\tv_and_b32 %1, 0xffff0000, %2"
+                 : "=&v"(lo), "=v"(hi)
+                 : "v"(w));
+    f[0] = __uint_as_float(lo);
+    f[1] = __uint_as_float(hi);
+  }
+  __device__ static inline uint32_t pack_word(const float (&f)[2]) {
+    return pack_bf16x2(f[0], f[1]);
   }
   __device__ static inline uint4 pack(const float (&f)[8]) {
     return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
@@ -113,6 +133,21 @@ struct Dt<VSCE_F16> {
       f[2 * i] = static_cast<float>(h[0]);
       f[2 * i + 1] = static_cast<float>(h[1]);
     }
+  }
+  // Volatile-asm conversion of one word (see Dt<VSCE_BF16>::word_fresh).
+  static constexpr int EPW = 2;
+  __device__ static inline void word_fresh(uint32_t w, float (&f)[2]) {
+    float lo, hi;
+    asm volatile(
+        "v_cvt_f32_f16 %0, %2\n\t"
+        "v_cvt_f32_f16_sdwa %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1"
+        : "=&v"(lo), "=v"(hi)
+        : "v"(w));
+    f[0] = lo;
+    f[1] = hi;
+  }
+  __device__ static inline uint32_t pack_word(const float (&f)[2]) {
+    return pack_f16x2(f[0], f[1]);
   }
   __device__ static inline uint4 pack(const float (&f)[8]) {
     return make_uint4(pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3]), pack_f16x2(f[4], f[5]),
@@ -182,49 +217,82 @@ __device__ inline void nt_store16(void* p, const uint4 v) {
   __builtin_nontemporal_store(w, static_cast<u32x4_t*>(p));
 }
 
-// Hides a register-held vector from the optimizer so that a pass over the
-// row unpacks it again instead of keeping the previous pass's fp32 copies
-// alive (which would double the registers a resident row needs).
-__device__ inline void opaque(uint4& v) {
-  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
-}
-
 // exp(x - m) as 2^(x*log2e - m*log2e) on the hardware base-2 exponential.
 __device__ inline float exp_shifted(float x, float m_log2e) {
   return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -m_log2e));
 }
 
 // ---------------------------------------------------------------- reductions
+// Wavefront all-reduce on the DPP crossbar: within each row of 16 lanes in
+// four steps (swap neighbours, swap pairs, mirror halves, mirror the row),
+// then the four row results are read into scalar registers and combined.
+// Fixed order, so the result does not depend on scheduling.
+
+template <int CTRL>
+__device__ inline int dpp_mov(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppSwap1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppSwap2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+
+template <class Op>
+__device__ inline float wave_reduce(float v, Op op) {
+  v = op(v, __int_as_float(dpp_mov<kDppSwap1>(__float_as_int(v))));
+  v = op(v, __int_as_float(dpp_mov<kDppSwap2>(__float_as_int(v))));
+  v = op(v, __int_as_float(dpp_mov<kDppHalfMirror>(__float_as_int(v))));
+  v = op(v, __int_as_float(dpp_mov<kDppMirror>(__float_as_int(v))));
+  const int b = __float_as_int(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+
+template <class Op>
+__device__ inline int wave_reduce(int v, Op op) {
+  v = op(v, dpp_mov<kDppSwap1>(v));
+  v = op(v, dpp_mov<kDppSwap2>(v));
+  v = op(v, dpp_mov<kDppHalfMirror>(v));
+  v = op(v, dpp_mov<kDppMirror>(v));
+  const int r0 = __builtin_amdgcn_readlane(v, 0);
+  const int r1 = __builtin_amdgcn_readlane(v, 16);
+  const int r2 = __builtin_amdgcn_readlane(v, 32);
+  const int r3 = __builtin_amdgcn_readlane(v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
 
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 
+__device__ inline int wave_sum(int v) {
+  return wave_reduce(v, [](int a, int b) { return a + b; });
+}
+
+__device__ inline int wave_min(int v) {
+  return wave_reduce(v, [](int a, int b) { return min(a, b); });
+}
+
+// fp64 sums (the single-workgroup normalizer and reduction kernels only).
 __device__ inline double wave_sum(double v) {
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
 
-__device__ inline int wave_sum(int v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// A value every lane of the wavefront holds, moved to a scalar register (it
+// frees a vector register for the resident row).
+__device__ inline float uniform(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
-
-__device__ inline int wave_min(int v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
-}
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Workgroup max over NT threads; every thread gets the result.  `sh` holds
 // NT/64 floats and is not reused until the next barrier.
@@ -239,7 +307,7 @@ __device__ inline float block_max(float v, float* sh) {
   float r = sh[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) r = fmaxf(r, sh[w]);
-  return r;
+  return uniform(r);
 }
 
 // The per-row sums merged once the row maximum is known: the sum of the
@@ -274,6 +342,10 @@ __device__ inline RowSums block_sums(RowSums v, float4* sh) {
     r.cnt += __float_as_int(q.z);
     r.first = min(r.first, __float_as_int(q.w));
   }
+  r.s = uniform(r.s);
+  r.S = uniform(r.S);
+  r.cnt = uniform(r.cnt);
+  r.first = uniform(r.first);
   return r;
 }
 

@@ -30,30 +30,19 @@
 namespace vsce {
 namespace {
 
-template <int DT, bool WEIGHTED>
-__device__ inline void load_weights(const float* w, int64_t j, float (&wv)[Dt<DT>::VEC]) {
-  constexpr int VEC = Dt<DT>::VEC;
-  if constexpr (WEIGHTED) {
-    const float4* p = reinterpret_cast<const float4*>(w + j * VEC);
-#pragma unroll
-    for (int q = 0; q < VEC / 4; ++q) {
-      const float4 t = p[q];
-      wv[4 * q + 0] = t.x;
-      wv[4 * q + 1] = t.y;
-      wv[4 * q + 2] = t.z;
-      wv[4 * q + 3] = t.w;
-    }
-  }
-}
-
-template <int DT, int NT, int NREG, int NLDS, bool WEIGHTED, int WPE>
+// LDS_CAP: vectors of LDS actually allocated (<= NLDS * NT).  The last LDS
+// slot may be partial: the shape then serves rows of at most NT * NREG +
+// LDS_CAP vectors, and no lane past that ever touches LDS.
+template <int DT, int NT, int NREG, int NLDS, int LDS_CAP, bool WEIGHTED, int WPE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
 void fused_resident_kernel(const RowArgs a) {
   using D = Dt<DT>;
   constexpr int VEC = D::VEC;
   constexpr int NW = NT / kWave;
   constexpr uint32_t SLOT_BYTES = NT * 16u;  // bytes between a thread's vectors
-  __shared__ uint4 xl[NLDS > 0 ? NLDS * NT : 1];
+  static_assert(LDS_CAP <= NLDS * NT && LDS_CAP > (NLDS - 1) * NT - (NLDS == 0 ? 1 : 0),
+                "the capped LDS must still reach into the last LDS slot");
+  __shared__ uint4 xl[NLDS > 0 ? LDS_CAP : 1];
   __shared__ float red_max[NW];
   __shared__ float4 red_sum[NW];
 
@@ -77,7 +66,7 @@ void fused_resident_kernel(const RowArgs a) {
     return;
   }
 
-  const float xy = D::load1(rowb, y);
+  const float xy = uniform(D::load1(rowb, y));
 
   // ---- one read of the row: registers, then LDS (lanes past the row read 0
   //      and are masked out of every pass below)
@@ -85,18 +74,32 @@ void fused_resident_kernel(const RowArgs a) {
   static_for<NREG>([&](auto k) { r[k] = buf_load16(rsrc, lane_off(k), k * SLOT_BYTES); });
   if constexpr (NLDS > 0) {
     const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~(kWave - 1));
+    // Exec-masked rather than range-checked: lanes past the row write nothing
+    // to LDS (the last slot's allocation may end before them).
     static_for<NLDS>([&](auto k) {
-      buf_load16_lds(rsrc, xl + k * NT + wave_base, lane_off(NREG + k), (NREG + k) * SLOT_BYTES);
+      if (in_row(NREG + k))
+        buf_load16_lds(rsrc, xl + k * NT + wave_base, voff, (NREG + k) * SLOT_BYTES);
     });
   }
 
   // ---- pass 1: row maximum
   float mx = -__builtin_inff();
+  // Every pass works on one 32-bit word (EPW elements) at a time, so only a
+  // few fp32 temporaries are live next to the resident row.
+  constexpr int EPW = D::EPW;
+  auto words = [](const uint4 v) {
+    struct W4 { uint32_t w[4]; };
+    return W4{{v.x, v.y, v.z, v.w}};
+  };
   auto max_vec = [&](const uint4 v) {
-    float f[VEC];
-    D::unpack(v, f);
+    const auto w = words(v);
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) mx = fmaxf(mx, f[i]);
+    for (int q = 0; q < 4; ++q) {
+      float f[EPW];
+      D::word_fresh(w.w[q], f);
+#pragma unroll
+      for (int e = 0; e < EPW; ++e) mx = fmaxf(mx, f[e]);
+    }
   };
   static_for<NREG>([&](auto k) {
     if (in_row(k)) max_vec(r[k]);
@@ -110,27 +113,30 @@ void fused_resident_kernel(const RowArgs a) {
   }
   const float M = block_max<NT>(mx, red_max);
   const float ML = M * kLog2e;
-  static_for<NREG>([&](auto k) { opaque(r[k]); });
 
   // ---- pass 2: sums below the maximum, ties, first index, logit sum
   RowSums rs = {0.0f, 0.0f, 0, 0x7fffffff};
-  auto accumulate = [&](auto careful, const uint4 v, int64_t j) {
-    float f[VEC], wv[VEC];
-    D::unpack(v, f);
-    load_weights<DT, WEIGHTED>(a.weight, j, wv);
+  auto accumulate = [&](auto careful, const uint4 v, int j) {
+    const auto w = words(v);
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      const float e = exp_shifted(f[i], ML);
-      if constexpr (decltype(careful)::value) {
-        const bool eq = (f[i] == M);
-        rs.s += eq ? 0.0f : e;
-        rs.cnt += eq ? 1 : 0;
-        if (eq) rs.first = min(rs.first, static_cast<int>(j * VEC + i));
-      } else {
-        rs.s += e;
+    for (int q = 0; q < 4; ++q) {
+      float f[EPW];
+      D::word_fresh(w.w[q], f);
+#pragma unroll
+      for (int e = 0; e < EPW; ++e) {
+        const int i = q * EPW + e;  // element within the vector
+        const float ex = exp_shifted(f[e], ML);
+        if constexpr (decltype(careful)::value) {
+          const bool eq = (f[e] == M);
+          rs.s += eq ? 0.0f : ex;
+          rs.cnt += eq ? 1 : 0;
+          if (eq) rs.first = min(rs.first, j * VEC + i);
+        } else {
+          rs.s += ex;
+        }
+        if constexpr (WEIGHTED) rs.S = __builtin_fmaf(a.weight[j * VEC + i], f[e], rs.S);
+        else rs.S += f[e];
       }
-      if constexpr (WEIGHTED) rs.S = __builtin_fmaf(wv[i], f[i], rs.S);
-      else rs.S += f[i];
     }
   };
   auto sum_pass = [&](auto careful) {
@@ -146,37 +152,57 @@ void fused_resident_kernel(const RowArgs a) {
   if (__ballot(mx == M) != 0ull) sum_pass(std::true_type{});
   else sum_pass(std::false_type{});
   rs = block_sums<NT>(rs, red_sum);
-  static_for<NREG>([&](auto k) { opaque(r[k]); });
 
   const float dp = rs.s + static_cast<float>(rs.cnt - 1);  // d' = d - 1
-  const float sum_w = static_cast<float>(a.ws->sum_w);
-  const float wy = WEIGHTED ? a.weight[y] : 1.0f;
+  const float sum_w = uniform(static_cast<float>(a.ws->sum_w));
+  const float wy = uniform(WEIGHTED ? a.weight[y] : 1.0f);
   if (tid == 0)
     store_row(a, n, row_loss(M, dp, xy, rs.S, wy, sum_w, a.eps, a.eta),
               (static_cast<int64_t>(rs.first) == y) ? 1.0f : 0.0f);
 
   // ---- pass 3: gradient over the on-chip row, one store per vector
-  const float sigma = a.mean ? static_cast<float>(1.0 / a.ws->W) : 1.0f;
-  const RowTerms t = row_terms(M, dp, xy, wy, sum_w, a.eps, a.eta, sigma);
+  const float sigma = uniform(a.mean ? static_cast<float>(1.0 / a.ws->W) : 1.0f);
+  RowTerms t = row_terms(M, dp, xy, wy, sum_w, a.eps, a.eta, sigma);
+  t.ML = uniform(t.ML);
+  t.K = uniform(t.K);
+  t.B = uniform(t.B);
+  t.dxy = uniform(t.dxy);
   const int64_t jy = y / VEC;
   const int ky = static_cast<int>(jy / NT);  // slot and lane owning the target
   const int ty = static_cast<int>(jy % NT);
   const int iy = static_cast<int>(y % VEC);
   auto grad_vec = [&](const uint4 v, int k) {
-    float f[VEC], wv[VEC];
-    D::unpack(v, f);
-    load_weights<DT, WEIGHTED>(a.weight, static_cast<int64_t>(k) * NT + tid, wv);
+    const int j = k * NT + tid;
+    auto w = words(v);
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      const float b = WEIGHTED ? t.B * wv[i] : t.B;
-      f[i] = __builtin_fmaf(exp_shifted(f[i], t.ML), t.K, -b);
+    for (int q = 0; q < 4; ++q) {
+      float f[EPW];
+      D::word_fresh(w.w[q], f);
+#pragma unroll
+      for (int e = 0; e < EPW; ++e) {
+        const float b = WEIGHTED ? t.B * a.weight[j * VEC + q * EPW + e] : t.B;
+        f[e] = __builtin_fmaf(exp_shifted(f[e], t.ML), t.K, -b);
+      }
+      w.w[q] = D::pack_word(f);  // the result word replaces the input word
     }
     if (k == ky && tid == ty) {
+      // The owner of the target column writes the fp32 true-class value,
+      // rounded once, in place of its softmax term.
+      float f[EPW];
+      const int q = iy / EPW;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i)
-        if (i == iy) f[i] = t.dxy;
+      for (int qq = 0; qq < 4; ++qq) {
+        if (qq == q) {
+          D::word_fresh(w.w[qq], f);
+#pragma unroll
+          for (int e = 0; e < EPW; ++e)
+            if (qq * EPW + e == iy) f[e] = t.dxy;
+          w.w[qq] = D::pack_word(f);
+        }
+      }
     }
-    buf_store16(rsrc, voff, static_cast<uint32_t>(k) * SLOT_BYTES, D::pack(f));
+    buf_store16(rsrc, voff, static_cast<uint32_t>(k) * SLOT_BYTES,
+                make_uint4(w.w[0], w.w[1], w.w[2], w.w[3]));
   };
   static_for<NREG>([&](auto k) {
     if (in_row(k)) grad_vec(r[k], k);
@@ -189,22 +215,26 @@ void fused_resident_kernel(const RowArgs a) {
 // Shapes of the resident kernel: threads per workgroup, vectors per thread in
 // registers and in LDS, and the minimum wavefronts per SIMD to compile for
 // (which caps the registers per wavefront at 512 / WPE).
-template <int NT_, int NREG_, int NLDS_, int WPE_>
+template <int NT_, int NREG_, int NLDS_, int WPE_, int LDS_CAP_ = NT_ * NLDS_>
 struct Shape {
-  static constexpr int NT = NT_, NREG = NREG_, NLDS = NLDS_, WPE = WPE_;
+  static constexpr int NT = NT_, NREG = NREG_, NLDS = NLDS_, WPE = WPE_, LDS_CAP = LDS_CAP_;
+  static constexpr int64_t CAPACITY = static_cast<int64_t>(NT_) * NREG_ + LDS_CAP_;
 };
 
 using Shapes = std::tuple<Shape<64, 4, 0, 4>,       // rows up to 256 vectors
                           Shape<256, 8, 0, 4>,      // 2048 vectors
                           Shape<256, 16, 0, 4>,     // 4096 vectors
                           Shape<512, 16, 0, 4>,     // 8192 vectors
-                          Shape<512, 23, 9, 4>,     // 16384 vectors: 2 workgroups per CU
+                          // 16320 vectors (bf16 V <= 130560): 2 workgroups per CU,
+                          // 64 VGPRs and 79 KB of LDS each
+                          Shape<1024, 11, 5, 8, 5056>,
                           Shape<1024, 16, 4, 4>,    // 20480 vectors
                           Shape<1024, 24, 8, 4>>;   // 32768 vectors
 
 template <int DT, bool W, class SH>
 int launch_shape(const Prob& p, const RowArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((fused_resident_kernel<DT, SH::NT, SH::NREG, SH::NLDS, W, SH::WPE>),
+  hipLaunchKernelGGL(
+      (fused_resident_kernel<DT, SH::NT, SH::NREG, SH::NLDS, SH::LDS_CAP, W, SH::WPE>),
                      dim3(static_cast<unsigned>(p.rows)), dim3(SH::NT), 0, s, a);
   return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
 }
@@ -215,7 +245,7 @@ int pick_shape(const Prob& p, const RowArgs& a, hipStream_t s) {
     return VSCE_ERR_UNSUPPORTED;
   } else {
     using SH = std::tuple_element_t<I, Shapes>;
-    if (a.nvec <= static_cast<int64_t>(SH::NT) * (SH::NREG + SH::NLDS))
+    if (a.nvec <= SH::CAPACITY)
       return launch_shape<DT, W, SH>(p, a, s);
     return pick_shape<DT, W, I + 1>(p, a, s);
   }
