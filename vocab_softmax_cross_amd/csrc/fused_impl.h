@@ -66,7 +66,6 @@ void fused_resident_kernel(const RowArgs a) {
     return;
   }
 
-  const float xy = uniform(D::load1(rowb, y));
 
   // ---- one read of the row: registers, then LDS (lanes past the row read 0
   //      and are masked out of every pass below)
@@ -81,6 +80,10 @@ void fused_resident_kernel(const RowArgs a) {
         buf_load16_lds(rsrc, xl + k * NT + wave_base, voff, (NREG + k) * SLOT_BYTES);
     });
   }
+
+  // The target logit: issued after the row's loads and consumed after pass 2,
+  // so its latency never holds up the row stream.
+  const float xy_lane = D::load1(rowb, y);
 
   // ---- pass 1: row maximum
   float mx = -__builtin_inff();
@@ -154,6 +157,7 @@ void fused_resident_kernel(const RowArgs a) {
   rs = block_sums<NT>(rs, red_sum);
 
   const float dp = rs.s + static_cast<float>(rs.cnt - 1);  // d' = d - 1
+  const float xy = uniform(xy_lane);
   const float sum_w = uniform(static_cast<float>(a.ws->sum_w));
   const float wy = uniform(WEIGHTED ? a.weight[y] : 1.0f);
   if (tid == 0)
