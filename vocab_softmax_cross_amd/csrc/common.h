@@ -172,6 +172,24 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// ---------------------------------------------------------------- XCD-aware order
+// The chip hands consecutive workgroups of a launch to its 8 XCDs in turn
+// (workgroup b runs on XCD b mod 8), and each XCD has its own L2 and its own
+// address-translation caches.  xcd_contiguous() renumbers a one-item-per-
+// workgroup grid so that the workgroups one XCD runs take one contiguous range
+// of items: the rows an XCD has in flight then lie side by side in memory
+// instead of every 8th row of a window 8 times wider.  It is a bijection on
+// [0, items) for every items (XCD x takes items/8 items, one more if x is
+// below items mod 8), so results never depend on the dispatch order; only the
+// speed does.
+constexpr int64_t kXcds = 8;
+
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t b, int64_t items) {
+  const int64_t q = items / kXcds, r = items % kXcds;
+  const int64_t x = b % kXcds;
+  return x * q + (x < r ? x : r) + b / kXcds;
+}
+
 // ---------------------------------------------------------------- buffer access
 // A buffer resource covers one row: a 32-bit byte offset per lane (VGPR) plus
 // a per-instruction constant (SGPR), and lanes past num_records read zeros and

@@ -47,7 +47,7 @@ void fused_resident_kernel(const RowArgs a) {
   __shared__ float4 red_sum[NW];
 
   const int tid = threadIdx.x;
-  const int64_t n = blockIdx.x;
+  const int64_t n = xcd_contiguous(blockIdx.x, a.rows);
   const int nvec = static_cast<int>(a.nvec);
   char* rowb = static_cast<char*>(a.x) + n * a.stride * D::BYTES;
   const auto rsrc = make_rsrc(rowb, static_cast<uint32_t>(a.V * D::BYTES));

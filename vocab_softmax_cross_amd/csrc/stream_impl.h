@@ -200,7 +200,7 @@ __global__ __launch_bounds__(NT) void stats_kernel(const RowArgs a) {
   using D = Dt<DT>;
   __shared__ float red_max[NT / kWave];
   __shared__ float4 red_sum[NT / kWave];
-  const int64_t n = blockIdx.x;
+  const int64_t n = xcd_contiguous(blockIdx.x, a.rows);
   const char* row = static_cast<const char*>(a.x) + n * a.stride * D::BYTES;
   const int64_t y = a.target[n];
   const int cls = row_class(y, a.V, a.ignore_index);
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(NT) void fused_stream_kernel(const RowArgs a) {
   using D = Dt<DT>;
   __shared__ float red_max[NT / kWave];
   __shared__ float4 red_sum[NT / kWave];
-  const int64_t n = blockIdx.x;
+  const int64_t n = xcd_contiguous(blockIdx.x, a.rows);
   char* row = static_cast<char*>(a.x) + n * a.stride * D::BYTES;
   const int64_t y = a.target[n];
   const int cls = row_class(y, a.V, a.ignore_index);
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(NT) void fused_stream_kernel(const RowArgs a) {
 template <int DT, int NT, int U, bool WEIGHTED, bool VECP>
 __global__ __launch_bounds__(NT) void backward_kernel(const RowArgs a) {
   using D = Dt<DT>;
-  const int64_t b = blockIdx.x;
+  const int64_t b = xcd_contiguous(blockIdx.x, a.rows * a.chunks);
   const int64_t n = b / a.chunks;
   const int64_t c = b - n * a.chunks;
   const int64_t per = static_cast<int64_t>(NT) * U;
