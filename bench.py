@@ -103,13 +103,16 @@ def stored_traffic(workload: str):
         return None
 
 
-def cpu_baseline(wl, tgt, budget_s: float):
+def cpu_baseline(wl, tgt, budget_s: float, threads: int = 0):
     """The oracle (fp64 forward + gradient + rounding) on consecutive row
-    chunks until about `budget_s` of oracle time; rows per second."""
+    chunks until about `budget_s` of oracle time; rows per second.  `threads`
+    = 0 uses every host core the OpenMP runtime sees."""
     import numpy as np
     import oracle
     import workloads as W
-    chunk = 512
+    default_threads = oracle.max_threads()
+    oracle.set_threads(threads if threads > 0 else default_threads)
+    chunk = 512 if threads != 1 else 64
     done, spent = 0, 0.0
     while done < wl.BT and spent < budget_s:
         r1 = min(wl.BT, done + chunk)
@@ -122,7 +125,9 @@ def cpu_baseline(wl, tgt, budget_s: float):
         spent += time.perf_counter() - t0
         done = r1
         del x, r, g
-    return {"value": done / spent, "unit": "rows/s", "cores": oracle.max_threads(),
+    cores = oracle.max_threads()
+    oracle.set_threads(default_threads)
+    return {"value": done / spent, "unit": "rows/s", "cores": cores,
             "kind": "oracle",
             "sample": f"first {done} of {wl.BT} rows ({done * wl.V:.3g} elements), fp64 "
                       f"forward + gradient + rounding to {wl.dtype}, {spent:.1f} s"}
@@ -251,13 +256,28 @@ def main():
                                                  + (wl.BT - n_valid) * row_bytes) * K
                                                 / wsp / 1e9, 1)}
 
+    # Practical ceiling: the runtime's own device-to-device copy of one
+    # logits buffer (reads and writes the same bytes as the row kernel's
+    # valid rows), timed over K copies.
+    copy_src, copy_dst = pristine, ring[0]
+    torch.cuda.synchronize()
+    t_copy = time.perf_counter()
+    for _ in range(K):
+        copy_dst.copy_(copy_src)
+    torch.cuda.synchronize()
+    copy_s = (time.perf_counter() - t_copy) / K
+    copy_ceiling = {"kind": "torch copy_ (device to device)", "bytes": 2 * wl.BT * row_bytes,
+                    "ms": round(copy_s * 1e3, 4),
+                    "GBps": round(2 * wl.BT * row_bytes / copy_s / 1e9, 1)}
+
     for a, b in ev:
         hip.destroy(a)
         hip.destroy(b)
 
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, tgt, args.cpu_seconds)
+        cpu1 = cpu_baseline(wl, tgt, args.cpu_seconds / 3, threads=1)
 
     line = {
         "metric": "fwd+bwd rows/s and HBM GB/s (% of peak) at BT=8192, V=128256 bf16",
@@ -283,7 +303,9 @@ def main():
                      "kernel": "fused_resident_kernel", "bytes_per_launch": kernel_bytes,
                      "mean_launch_ms": round(mean_kernel_s * 1e3, 4)},
         "modes": extra,
+        "copy_ceiling": copy_ceiling,
         "cpu_baseline": cpu,
+        "cpu_baseline_1thread": cpu1,
         "input_gen_s": round(gen_s, 1),
         "ring_buffers": ring_n,
     }

@@ -74,6 +74,8 @@ def _load():
         lib.oracle_rows.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -85,6 +87,11 @@ def _ptr(a: Optional[np.ndarray]):
 def max_threads() -> int:
     """Threads the oracle's OpenMP loops use (OMP_NUM_THREADS or all cores)."""
     return int(_load().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Use `n` threads in the oracle's parallel loops from now on."""
+    _load().oracle_set_threads(int(n))
 
 
 def round_to(values: np.ndarray, dtype: str) -> np.ndarray:

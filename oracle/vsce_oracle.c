@@ -61,6 +61,16 @@ int oracle_max_threads(void) {
 #endif
 }
 
+/* Thread count of the later parallel loops (rows are independent, so the
+ * results do not depend on it). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /*
  * Round-to-nearest, ties-to-even, of an fp64 value to a binary format with
  * `p` significand bits (hidden bit included), minimum normal exponent `emin`

@@ -44,6 +44,16 @@ def test_version_and_workspace_size():
     assert L.vsce_workspace_bytes(8192) == L.WS_HEADER_BYTES + 2 * 8192 * 4
 
 
+def test_header_constants_match_the_binding():
+    text = open(HEADER).read()
+    defines = {m.group(1): int(m.group(2), 0)
+               for m in re.finditer(r"^#define\s+VSCE_(\w+)\s+(\w+)", text, flags=re.M)
+               if re.fullmatch(r"0x[0-9a-fA-F]+|\d+", m.group(2))}
+    for name in ("WS_W", "WS_SUM_W", "WS_N_VALID", "WS_N_INVALID", "WS_STATUS",
+                 "WS_HEADER_BYTES", "STATS_STRIDE"):
+        assert defines[name] == getattr(L, name), name
+
+
 def test_struct_layout_matches_the_header():
     assert ctypes.sizeof(L.Problem) == 64
     assert L.Problem.label_smoothing.offset == 56

@@ -32,6 +32,7 @@ static_assert(offsetof(WsHeader, sum_w) == VSCE_WS_SUM_W, "header layout");
 static_assert(offsetof(WsHeader, n_valid) == VSCE_WS_N_VALID, "header layout");
 static_assert(offsetof(WsHeader, n_invalid) == VSCE_WS_N_INVALID, "header layout");
 static_assert(offsetof(WsHeader, status) == VSCE_WS_STATUS, "header layout");
+static_assert(sizeof(WsHeader) <= VSCE_WS_HEADER_BYTES, "header layout");
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -170,6 +171,25 @@ __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int
 template <int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// A workgroup barrier that orders LDS only: each wavefront waits for its own
+// LDS operations, not for its global stores to complete (which a full
+// __syncthreads() would, and which a kernel that streams its output need
+// never wait for).  For exchanges through LDS alone.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// threadIdx.x passed through an empty asm: in a loop, what is derived from
+// it per lane (masks, LDS addresses) is then rebuilt where it is used instead
+// of being held in registers across the whole loop.
+__device__ __forceinline__ int fresh_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
 }
 
 // ---------------------------------------------------------------- XCD-aware order
@@ -315,13 +335,13 @@ __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v);
 // Workgroup max over NT threads; every thread gets the result.  `sh` holds
 // NT/64 floats and is not reused until the next barrier.
 template <int NT>
-__device__ inline float block_max(float v, float* sh) {
+__device__ inline float block_max(float v, float* sh, int t = fresh_tid()) {
   constexpr int NW = NT / kWave;
   v = wave_max(v);
   if (NW == 1) return v;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lane = t & (kWave - 1), wave = uniform(t / kWave);
   if (lane == 0) sh[wave] = v;
-  __syncthreads();
+  lds_barrier();
   float r = sh[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) r = fmaxf(r, sh[w]);
@@ -340,17 +360,17 @@ struct RowSums {
 };
 
 template <int NT>
-__device__ inline RowSums block_sums(RowSums v, float4* sh) {
+__device__ inline RowSums block_sums(RowSums v, float4* sh, int t = fresh_tid()) {
   constexpr int NW = NT / kWave;
   v.s = wave_sum(v.s);
   v.S = wave_sum(v.S);
   v.cnt = wave_sum(v.cnt);
   v.first = wave_min(v.first);
   if (NW == 1) return v;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lane = t & (kWave - 1), wave = uniform(t / kWave);
   if (lane == 0)
     sh[wave] = make_float4(v.s, v.S, __int_as_float(v.cnt), __int_as_float(v.first));
-  __syncthreads();
+  lds_barrier();
   RowSums r = {0.f, 0.f, 0, 0x7fffffff};
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
