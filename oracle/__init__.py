@@ -70,7 +70,8 @@ def _load():
         lib.oracle_round_one.restype = ctypes.c_double
         lib.oracle_normalizer.argtypes = [i64, p, i64, p, i64, p, p, p, p]
         lib.oracle_normalizer.restype = None
-        lib.oracle_rows.argtypes = [i64, i64, p, p, p, i64, ctypes.c_double, p, p, p, p, p]
+        d = ctypes.c_double
+        lib.oracle_rows.argtypes = [i64, i64, p, p, p, i64, d, d, d, p, p, p, p, p, p, p, p]
         lib.oracle_rows.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -126,46 +127,66 @@ def normalizer(target: np.ndarray, V: int, weight: Optional[np.ndarray] = None,
 
 @dataclass
 class Rows:
-    loss: np.ndarray       # [n] unreduced, unscaled per-row loss
-    stats: np.ndarray      # [n, 4] (m, d', x_y, S)
-    argmax: np.ndarray     # [n] first index of the max
+    loss: np.ndarray       # [n] unreduced per-row loss (cross-entropy + z-loss)
+    z: np.ndarray          # [n] the z-loss part alone
+    stats: np.ndarray      # [n, 4] (m, d', x_y, S) of the (capped) logits
+    argmax: np.ndarray     # [n] first index of the max of the stored logits
     cls: np.ndarray        # [n] 0 valid, 1 ignored, 2 invalid
-    grad: Optional[np.ndarray]  # [n, V] unscaled dloss_n/dx, or None
+    grad: Optional[np.ndarray]  # [n, V] dloss_n/dx with the per-row scales, or None
 
 
 def rows(x: np.ndarray, target: np.ndarray, weight: Optional[np.ndarray] = None,
          ignore_index: int = -100, label_smoothing: float = 0.0,
-         want_grad: bool = True) -> Rows:
-    """Per-row loss, statistics, argmax and unscaled gradient (see vsce_oracle.c)."""
+         want_grad: bool = True, softcap: float = 0.0, z_loss: float = 0.0,
+         scale: Optional[np.ndarray] = None, scale_z: Optional[np.ndarray] = None) -> Rows:
+    """Per-row loss, statistics, argmax and gradient (see vsce_oracle.c).
+
+    The gradient's cross-entropy part is multiplied by ``scale`` and its
+    z-loss part by ``scale_z`` (per row; None: 1), before the softcap factor.
+    """
     x = np.ascontiguousarray(x, dtype=np.float64)
     if x.ndim != 2:
         raise ValueError("x must be [rows, V]")
     n, V = x.shape
     t = np.ascontiguousarray(target, dtype=np.int64).reshape(n)
     w = None if weight is None else np.ascontiguousarray(weight, dtype=np.float64).reshape(V)
+    sc = None if scale is None else np.ascontiguousarray(scale, dtype=np.float64).reshape(n)
+    sz = None if scale_z is None else np.ascontiguousarray(scale_z, dtype=np.float64).reshape(n)
     loss = np.empty(n, np.float64)
+    z = np.empty(n, np.float64)
     stats = np.empty((n, 4), np.float64)
     am = np.empty(n, np.int64)
     cls = np.empty(n, np.int32)
     grad = np.empty((n, V), np.float64) if want_grad else None
     _load().oracle_rows(n, V, _ptr(x), _ptr(t), _ptr(w), ignore_index,
-                        float(label_smoothing), _ptr(loss), _ptr(stats), _ptr(am),
-                        _ptr(cls), _ptr(grad))
-    return Rows(loss, stats, am, cls, grad)
+                        float(label_smoothing), float(softcap), float(z_loss), _ptr(sc), _ptr(sz),
+                        _ptr(loss), _ptr(z), _ptr(stats), _ptr(am), _ptr(cls), _ptr(grad))
+    return Rows(loss, z, stats, am, cls, grad)
 
 
-def reduce_loss(row_loss: np.ndarray, cls: np.ndarray, W: float, reduction: str):
+def reduce_loss(row_loss: np.ndarray, cls: np.ndarray, W: float, reduction: str,
+                row_z: Optional[np.ndarray] = None, n_valid: Optional[int] = None):
     """none -> the per-row vector; sum -> sum over rows; mean -> sum / W.
 
-    Ignored rows hold 0 and invalid rows NaN, so both enter the sum as they are.
+    With ``row_z`` (the z-loss part of each row loss), "mean" divides the
+    cross-entropy part by W and the z-loss part by ``n_valid``: class weights
+    weigh the cross-entropy only.  Ignored rows hold 0 and invalid rows NaN,
+    so both enter the sums as they are.
     """
     if reduction == "none":
         return np.asarray(row_loss, dtype=np.float64).copy()
-    total = math.fsum(float(v) for v in row_loss) if not np.isnan(row_loss).any() else math.nan
+
+    def fsum(v):
+        return math.fsum(float(e) for e in v) if not np.isnan(v).any() else math.nan
+
     if reduction == "sum":
-        return total
+        return fsum(row_loss)
     if reduction == "mean":
-        return total / W if W != 0 else math.nan
+        if row_z is None:
+            return fsum(row_loss) / W if W != 0 else math.nan
+        ce = fsum(np.asarray(row_loss) - np.asarray(row_z))
+        zs = fsum(row_z)
+        return (ce / W if W != 0 else math.nan) + (zs / n_valid if n_valid else math.nan)
     raise ValueError(reduction)
 
 
@@ -190,6 +211,7 @@ def token_accuracy(argmax: np.ndarray, target: np.ndarray, cls: np.ndarray):
 @dataclass
 class Result:
     loss: object                 # float (mean/sum) or [BT] array (none)
+    z_loss: object               # the z-loss part, reduced like the loss
     row_loss: np.ndarray
     stats: np.ndarray
     argmax: np.ndarray
@@ -197,7 +219,8 @@ class Result:
     acc: np.ndarray
     acc_mean: float
     norm: Normalizer
-    scale: np.ndarray            # [BT] per-row gradient factor
+    scale: np.ndarray            # [BT] per-row factor of the cross-entropy gradient
+    scale_z: np.ndarray          # [BT] per-row factor of the z-loss gradient
     grad: Optional[np.ndarray] = None      # [BT, V] exact scaled gradient (fp64)
     grad_rn: Optional[np.ndarray] = None   # the same, rounded once to the buffer type
     extra: dict = field(default_factory=dict)
@@ -206,7 +229,7 @@ class Result:
 def cross_entropy(x: np.ndarray, target: np.ndarray, weight: Optional[np.ndarray] = None,
                   ignore_index: int = -100, label_smoothing: float = 0.0,
                   reduction: str = "mean", grad_output=1.0, dtype: Optional[str] = None,
-                  want_grad: bool = True) -> Result:
+                  want_grad: bool = True, softcap: float = 0.0, z_loss: float = 0.0) -> Result:
     """Whole-batch oracle for small inputs: everything the hot path computes.
 
     ``x`` holds the stored logits upcast exactly to fp64 ([BT, V]).  ``dtype``
@@ -215,13 +238,16 @@ def cross_entropy(x: np.ndarray, target: np.ndarray, weight: Optional[np.ndarray
     x = np.ascontiguousarray(x, dtype=np.float64)
     BT, V = x.shape
     nz = normalizer(target, V, weight, ignore_index)
-    r = rows(x, target, weight, ignore_index, label_smoothing, want_grad)
-    loss = reduce_loss(r.loss, r.cls, nz.W, reduction)
-    acc, acc_mean = token_accuracy(r.argmax, target, r.cls)
     scale = grad_scale(reduction, nz.W, grad_output, BT)
-    res = Result(loss, r.loss, r.stats, r.argmax, r.cls, acc, acc_mean, nz, scale)
+    scale_z = grad_scale(reduction, float(nz.n_valid), grad_output, BT)
+    r = rows(x, target, weight, ignore_index, label_smoothing, want_grad, softcap, z_loss,
+             scale, scale_z)
+    loss = reduce_loss(r.loss, r.cls, nz.W, reduction, r.z, nz.n_valid)
+    zl = reduce_loss(r.z, r.cls, float(nz.n_valid), reduction)
+    acc, acc_mean = token_accuracy(r.argmax, target, r.cls)
+    res = Result(loss, zl, r.loss, r.stats, r.argmax, r.cls, acc, acc_mean, nz, scale, scale_z)
     if want_grad:
-        res.grad = r.grad * scale[:, None]
+        res.grad = r.grad
         res.grad[r.cls != VALID] = 0.0
         if dtype is not None:
             res.grad_rn = round_to(res.grad, dtype)

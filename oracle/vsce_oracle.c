@@ -33,12 +33,20 @@
  * cross_entropy (the pages validate loss, gradients and accuracy against
  * PyTorch: [L1622] Testing Done).
  *
+ * Logit soft-capping and the z-loss are named by [L1268] (What changed: the
+ * target correction keeps the softcap factor; Correctness: the CE suite
+ * covers softcap and z-loss) with no formula, so both take their plain
+ * definitions: capped logits s * tanh(x / s) replace the logits everywhere
+ * (s = 0: off), and a valid row adds lambda * lse^2 with lse taken over the
+ * capped logits (lambda = 0: off).
+ *
  * Build: gcc -O2 -fopenmp -shared -fPIC vsce_oracle.c -o liboracle.so -lm
  * (no -ffast-math: the arithmetic must be IEEE fp64 as written).
  */
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -151,39 +159,55 @@ void oracle_normalizer(int64_t BT, const int64_t *target, int64_t V,
 }
 
 /*
- * Per-row forward and (unscaled) gradient, for `nrows` rows of `V` logits
- * (x is row-major with row stride V, the stored values upcast exactly).
+ * Per-row forward and gradient, for `nrows` rows of `V` logits (x is
+ * row-major with row stride V, the stored values upcast exactly).
+ *
+ * Soft-capping first: with softcap s > 0 every logit is replaced by
+ *   xt[c] = s tanh(x[c] / s),   dxt[c]/dx[c] = 1 / cosh^2(x[c] / s)
+ * (s = 0: xt = x, factor 1).  Everything below reads xt.
  *
  * For a valid row with target y, weights w (all ones when weight == NULL),
  * eps = label_smoothing and eta = eps / V:
- *   m    = max_c x[c]; cstar = the first index attaining it
- *   d'   = sum over c != cstar of exp(x[c] - m)          (d = 1 + d')
+ *   m    = max_c xt[c]; cstar = the first index attaining it
+ *   d'   = sum over c != cstar of exp(xt[c] - m)          (d = 1 + d')
  *   lse  = m + log1p(d')
- *   loss = (1 - eps) w[y] (lse - x[y]) + eta * sum_c w[c] (lse - x[c])
- *   p[c] = exp(x[c] - lse)
- * Every lse - x[c] is evaluated as (m - x[c]) + log1p(d'), the same quantity
- * without the cancellation of lse against x[c] when the loss is small.
- *   dloss/dx[c] = p[c] ((1 - eps) w[y] + eta sum_k w[k]) - eta w[c]
- *                 - (1 - eps) w[y] [c == y]
- * The loss is PyTorch's smoothed, weighted cross-entropy for one row; the
- * gradient has the structure of [L1268]'s pass 2 (softmax, X_block += -eps,
- * then -(1 - label_smoothing) at the target) with the class weights of
- * [L1622].
+ *   ce   = (1 - eps) w[y] (lse - xt[y]) + eta * sum_c w[c] (lse - xt[c])
+ *   z    = z_loss * lse^2
+ *   loss = ce + z
+ *   p[c] = exp(xt[c] - lse)
+ * Every lse - xt[c] is evaluated as (m - xt[c]) + log1p(d'), the same
+ * quantity without the cancellation of lse against xt[c] when the loss is
+ * small.
+ *   dce/dxt[c] = p[c] ((1 - eps) w[y] + eta sum_k w[k]) - eta w[c]
+ *                - (1 - eps) w[y] [c == y]
+ *   dz/dxt[c]  = 2 z_loss lse p[c]
+ * The cross-entropy part is PyTorch's smoothed, weighted cross-entropy for
+ * one row; its gradient has the structure of [L1268]'s pass 2 (softmax,
+ * X_block += -eps, then -(1 - label_smoothing) at the target) with the class
+ * weights of [L1622].
+ *
+ * The gradient written is, per row n,
+ *   grad[c] = (scale_ce[n] dce/dxt[c] + scale_z[n] dz/dxt[c]) dxt[c]/dx[c]
+ * (scale_ce / scale_z NULL: 1), so that a reduction may normalise the two
+ * parts differently.
  *
  * Per-row statistics, as saved by the split forward ([TE2325] m_d_X_y):
- *   stats = (m, d', x[y], S) with S = sum_c w[c] x[c] when eps > 0, else 0.
+ *   stats = (m, d', xt[y], S) with S = sum_c w[c] xt[c] when eps > 0, else 0.
  * The second slot holds d' = d - 1 rather than d (same information; d' keeps
  * its relative precision when one class dominates).
  *
  * Ignored rows: loss 0, gradient 0, stats 0.  Invalid rows: loss NaN,
- * gradient 0, stats 0.  argmax is computed for every row (first index).
+ * gradient 0, stats 0.  argmax is the first index of the maximum of the
+ * stored logits x (soft-capping is increasing, so it names the same class),
+ * for every row.  row_z (may be NULL) receives z alone.
  *
  * `grad` may be NULL (no gradient wanted).
  */
 void oracle_rows(int64_t nrows, int64_t V, const double *x,
                  const int64_t *target, const double *weight,
-                 int64_t ignore_index, double label_smoothing,
-                 double *row_loss, double *stats, int64_t *argmax,
+                 int64_t ignore_index, double label_smoothing, double softcap,
+                 double z_loss, const double *scale_ce, const double *scale_z,
+                 double *row_loss, double *row_z, double *stats, int64_t *argmax,
                  int32_t *cls_out, double *grad) {
   const double eps = label_smoothing;
   const double eta = eps / (double)V;
@@ -191,65 +215,94 @@ void oracle_rows(int64_t nrows, int64_t V, const double *x,
   for (int64_t c = 0; c < V; ++c) sum_w += weight ? weight[c] : 1.0;
 
   int64_t n;
-#pragma omp parallel for schedule(dynamic, 1)
-  for (n = 0; n < nrows; ++n) {
-    const double *xr = x + n * V;
-    double *gr = grad ? grad + n * V : NULL;
-    const int64_t y = target[n];
-    const int cls = row_class(y, V, ignore_index);
-    cls_out[n] = cls;
+#pragma omp parallel
+  {
+    double *xt = (double *)malloc((size_t)V * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+    for (n = 0; n < nrows; ++n) {
+      const double *xr = x + n * V;
+      double *gr = grad ? grad + n * V : NULL;
+      const int64_t y = target[n];
+      const int cls = row_class(y, V, ignore_index);
+      cls_out[n] = cls;
 
-    /* max and its first index (NaN never compares greater) */
-    double m = -INFINITY;
-    int64_t cstar = 0;
-    for (int64_t c = 0; c < V; ++c) {
-      if (xr[c] > m) {
-        m = xr[c];
-        cstar = c;
+      /* argmax of the stored logits, first index (NaN never compares greater) */
+      double mx = -INFINITY;
+      int64_t am = 0;
+      for (int64_t c = 0; c < V; ++c) {
+        if (xr[c] > mx) {
+          mx = xr[c];
+          am = c;
+        }
       }
-    }
-    argmax[n] = cstar;
+      argmax[n] = am;
 
-    if (cls != ORACLE_VALID) {
-      row_loss[n] = (cls == ORACLE_IGNORED) ? 0.0 : NAN;
-      for (int k = 0; k < 4; ++k) stats[4 * n + k] = 0.0;
-      if (gr)
-        for (int64_t c = 0; c < V; ++c) gr[c] = 0.0;
-      continue;
-    }
+      if (cls != ORACLE_VALID) {
+        row_loss[n] = (cls == ORACLE_IGNORED) ? 0.0 : NAN;
+        if (row_z) row_z[n] = (cls == ORACLE_IGNORED) ? 0.0 : NAN;
+        for (int k = 0; k < 4; ++k) stats[4 * n + k] = 0.0;
+        if (gr)
+          for (int64_t c = 0; c < V; ++c) gr[c] = 0.0;
+        continue;
+      }
 
-    double dprime = 0.0;
-    for (int64_t c = 0; c < V; ++c)
-      if (c != cstar) dprime += exp(xr[c] - m);
-    /* a NaN anywhere in the row must reach the loss and the gradient (the
-       max scan above never selects a NaN) */
-    for (int64_t c = 0; c < V; ++c)
-      if (isnan(xr[c])) dprime = NAN;
-    const double lg = log1p(dprime); /* lse - m */
+      for (int64_t c = 0; c < V; ++c)
+        xt[c] = (softcap > 0.0) ? softcap * tanh(xr[c] / softcap) : xr[c];
 
-    const double wy = weight ? weight[y] : 1.0;
-    double smooth = 0.0, S = 0.0;
-    for (int64_t c = 0; c < V; ++c) {
-      const double wc = weight ? weight[c] : 1.0;
-      smooth += wc * ((m - xr[c]) + lg);
-      S += wc * xr[c];
-    }
-    row_loss[n] = (1.0 - eps) * wy * ((m - xr[y]) + lg) + eta * smooth;
+      /* max of the (capped) logits and its first index */
+      double m = -INFINITY;
+      int64_t cstar = 0;
+      for (int64_t c = 0; c < V; ++c) {
+        if (xt[c] > m) {
+          m = xt[c];
+          cstar = c;
+        }
+      }
 
-    stats[4 * n + 0] = m;
-    stats[4 * n + 1] = dprime;
-    stats[4 * n + 2] = xr[y];
-    stats[4 * n + 3] = (eps > 0.0) ? S : 0.0;
+      double dprime = 0.0;
+      for (int64_t c = 0; c < V; ++c)
+        if (c != cstar) dprime += exp(xt[c] - m);
+      /* a NaN anywhere in the row must reach the loss and the gradient (the
+         max scan above never selects a NaN) */
+      for (int64_t c = 0; c < V; ++c)
+        if (isnan(xt[c])) dprime = NAN;
+      const double lg = log1p(dprime); /* lse - m */
+      const double lse = m + lg;
 
-    if (gr) {
-      const double A = (1.0 - eps) * wy + eta * sum_w;
+      const double wy = weight ? weight[y] : 1.0;
+      double smooth = 0.0, S = 0.0;
       for (int64_t c = 0; c < V; ++c) {
         const double wc = weight ? weight[c] : 1.0;
-        const double p = exp((xr[c] - m) - lg);
-        double g = p * A - eta * wc;
-        if (c == y) g -= (1.0 - eps) * wy;
-        gr[c] = g;
+        smooth += wc * ((m - xt[c]) + lg);
+        S += wc * xt[c];
+      }
+      const double z = z_loss * lse * lse;
+      row_loss[n] = (1.0 - eps) * wy * ((m - xt[y]) + lg) + eta * smooth + z;
+      if (row_z) row_z[n] = z;
+
+      stats[4 * n + 0] = m;
+      stats[4 * n + 1] = dprime;
+      stats[4 * n + 2] = xt[y];
+      stats[4 * n + 3] = (eps > 0.0) ? S : 0.0;
+
+      if (gr) {
+        const double sc = scale_ce ? scale_ce[n] : 1.0;
+        const double sz = scale_z ? scale_z[n] : 1.0;
+        const double A = (1.0 - eps) * wy + eta * sum_w;
+        for (int64_t c = 0; c < V; ++c) {
+          const double wc = weight ? weight[c] : 1.0;
+          const double p = exp((xt[c] - m) - lg);
+          double g = p * A - eta * wc;
+          if (c == y) g -= (1.0 - eps) * wy;
+          g = sc * g + sz * (2.0 * z_loss * lse * p);
+          if (softcap > 0.0) {
+            const double ch = cosh(xr[c] / softcap);
+            g /= ch * ch;
+          }
+          gr[c] = g;
+        }
       }
     }
+    free(xt);
   }
 }

@@ -367,3 +367,133 @@ def test_reproduces_the_dxy_accuracy_table():
         assert e_fold <= 0.5, (p, e_fold)
         assert e_fold == pytest.approx(before, abs=0.15), (p, e_fold, before)
         assert e_rmw == pytest.approx(at, rel=0.15), (p, e_rmw, at)
+
+
+# ---------------------------------------------------------------- soft-capping and z-loss
+# The pages name both features without a formula (Liger-Kernel PR #1268,
+# What changed and Correctness); the oracle takes their plain definitions:
+# capped logits s*tanh(x/s), and lambda * lse^2 per valid row.
+
+def _torch_capped_ce(x, t, w, eps, reduction, softcap, z_loss, go=1.0):
+    """Loss and input gradient through torch's own cross_entropy, tanh and
+    autograd (fp64), with the z-loss mean taken over the valid rows."""
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    capped = softcap * torch.tanh(xt / softcap) if softcap > 0 else xt
+    tt = torch.tensor(t)
+    wt = None if w is None else torch.tensor(w, dtype=torch.float64)
+    valid = tt != -100
+    ce = F.cross_entropy(capped, tt, weight=wt, ignore_index=-100, label_smoothing=eps,
+                         reduction=reduction)
+    z_rows = z_loss * torch.logsumexp(capped, dim=1) ** 2 * valid
+    if reduction == "none":
+        loss = ce + z_rows
+        loss.backward(torch.as_tensor(go, dtype=torch.float64).expand_as(loss))
+        return loss.detach().numpy(), xt.grad.numpy()
+    z = z_rows.sum() / valid.sum() if reduction == "mean" else z_rows.sum()
+    loss = ce + z
+    (loss * go).backward()
+    return float(loss.detach()), xt.grad.numpy()
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+@pytest.mark.parametrize("weighted,eps", [(False, 0.0), (True, 0.1)])
+@pytest.mark.parametrize("softcap,z_loss", [(30.0, 0.0), (0.0, 1e-3), (5.0, 0.2)])
+def test_softcap_and_z_loss_match_torch_autograd(reduction, weighted, eps, softcap, z_loss):
+    x, t, w = _problem(21, 24, 300, weighted=weighted, ignore_frac=0.2, sigma=6.0)
+    go = np.linspace(0.5, 1.5, 24) if reduction == "none" else 0.7
+    r = oracle.cross_entropy(x, t, w, label_smoothing=eps, reduction=reduction,
+                             grad_output=go, softcap=softcap, z_loss=z_loss)
+    ref_loss, ref_grad = _torch_capped_ce(x, t, w, eps, reduction, softcap, z_loss, go)
+    np.testing.assert_allclose(r.loss, ref_loss, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(r.grad, ref_grad, rtol=1e-10, atol=1e-15)
+
+
+def test_very_large_cap_is_plain_cross_entropy():
+    x, t, w = _problem(22, 16, 200, weighted=True, sigma=2.0)
+    a = oracle.cross_entropy(x, t, w, label_smoothing=0.1)
+    b = oracle.cross_entropy(x, t, w, label_smoothing=0.1, softcap=1e7)
+    assert b.loss == pytest.approx(a.loss, rel=1e-12)
+    np.testing.assert_allclose(b.grad, a.grad, rtol=1e-9, atol=1e-16)
+
+
+@pytest.mark.parametrize("z_loss", [0.0, 1e-4, 0.5])
+def test_z_loss_uniform_logits_closed_form(z_loss):
+    """Equal logits a: lse = a + log V, p = 1/V, loss = log V + lambda lse^2,
+    dloss/dx_c = (1 + 2 lambda lse) / V - [c == y]."""
+    V, a, y = 1000, 3.25, 17
+    x = np.full((1, V), a)
+    r = oracle.cross_entropy(x, np.array([y]), z_loss=z_loss, reduction="sum")
+    lse = a + math.log(V)
+    assert r.loss == pytest.approx(math.log(V) + z_loss * lse * lse, rel=1e-13)
+    assert r.z_loss == pytest.approx(z_loss * lse * lse, rel=1e-13, abs=0)
+    g = np.full(V, (1 + 2 * z_loss * lse) / V)
+    g[y] -= 1.0
+    np.testing.assert_allclose(r.grad[0], g, rtol=1e-12, atol=1e-16)
+    assert r.stats[0, 0] == a and r.stats[0, 2] == a
+
+
+def test_softcap_uniform_logits_closed_form():
+    """Equal logits a capped at s: every capped logit is s tanh(a/s), so the
+    loss is log V, and dloss/dx_c = (1/V - [c == y]) / cosh^2(a/s)."""
+    V, a, y, s = 64, 7.0, 3, 5.0
+    x = np.full((1, V), a)
+    r = oracle.cross_entropy(x, np.array([y]), softcap=s, reduction="sum")
+    assert r.loss == pytest.approx(math.log(V), rel=1e-13)
+    g = np.full(V, 1.0 / V)
+    g[y] -= 1.0
+    np.testing.assert_allclose(r.grad[0], g / math.cosh(a / s) ** 2, rtol=1e-12)
+    assert r.stats[0, 0] == pytest.approx(s * math.tanh(a / s), rel=1e-15)
+
+
+def test_softcap_z_loss_gradient_is_finite_difference_of_loss():
+    x, t, w = _problem(23, 3, 40, weighted=True, sigma=8.0)
+    kw = dict(weight=w, label_smoothing=0.05, reduction="sum", softcap=6.0, z_loss=0.03)
+    r = oracle.cross_entropy(x, t, **kw)
+    h = 1e-4  # the loss is O(50): a smaller step drowns in fp64 roundoff
+    for n in range(3):
+        for c in (0, int(t[n]), 17, 39):
+            xp, xm = x.copy(), x.copy()
+            xp[n, c] += h
+            xm[n, c] -= h
+            fd = (oracle.cross_entropy(xp, t, **kw).loss
+                  - oracle.cross_entropy(xm, t, **kw).loss) / (2 * h)
+            assert r.grad[n, c] == pytest.approx(fd, rel=1e-6, abs=1e-9)
+
+
+def test_softcap_z_loss_brute_force_50_digits():
+    mpmath.mp.dps = 50
+    x, t, w = _problem(24, 2, 12, weighted=True, sigma=9.0)
+    s, lam, eps = 4.0, 0.07, 0.1
+    r = oracle.rows(x, t, w, label_smoothing=eps, softcap=s, z_loss=lam)
+    V = x.shape[1]
+    wm = [mpmath.mpf(float(v)) for v in w]
+
+    def loss_of(xs, y):
+        xt = [mpmath.mpf(s) * mpmath.tanh(v / mpmath.mpf(s)) for v in xs]
+        lse = mpmath.log(mpmath.fsum(mpmath.exp(v) for v in xt))
+        sm = mpmath.fsum(wm[c] * (lse - xt[c]) for c in range(V))
+        return ((1 - mpmath.mpf(eps)) * wm[y] * (lse - xt[y]) + mpmath.mpf(eps) / V * sm
+                + mpmath.mpf(lam) * lse ** 2)
+
+    for n in range(2):
+        pt = [mpmath.mpf(float(v)) for v in x[n]]
+        y = int(t[n])
+        assert r.loss[n] == pytest.approx(float(loss_of(pt, y)), rel=1e-13)
+        for c in (0, y, V - 1):
+            d = [0] * V
+            d[c] = 1
+            g = mpmath.diff(lambda *v: loss_of(list(v), y), pt, tuple(d))
+            assert r.grad[n, c] == pytest.approx(float(g), rel=1e-11, abs=1e-15)
+
+
+def test_accuracy_uses_the_stored_logits_when_the_cap_saturates():
+    """tanh(50) and tanh(60) are both 1.0 in fp64: the capped logits tie, but
+    the prediction is the larger stored logit (capping is increasing)."""
+    x = np.array([[500.0, 600.0, 0.0, -3.0]])
+    r = oracle.cross_entropy(x, np.array([1]), softcap=10.0)
+    assert r.argmax[0] == 1 and r.acc[0] == 1.0
+    assert r.stats[0, 0] == 10.0                       # both capped to s
+    assert r.stats[0, 1] == pytest.approx(1.0 + math.exp(-10.0) + math.exp(10 * math.tanh(-0.3) - 10))
+    assert np.all(np.isfinite(r.grad))
+    # the softcap factor 1/cosh^2 is below 1e-42 at 50 and 60
+    assert abs(r.grad[0, 0]) < 1e-40 and abs(r.grad[0, 1]) < 1e-40
