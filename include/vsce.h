@@ -15,7 +15,10 @@
  *                 - (1 - eps) w[y] [c == y]),   p = softmax(x),
  * computed in fp32 and rounded once to the buffer type.  The true-class term
  * is evaluated once per row from the live m, d' and x[y] and written with a
- * single store (no per-element compare, no read-modify-write).
+ * single store (no per-element compare, no read-modify-write).  Optionally
+ * the logits are soft-capped first (x -> s tanh(x / s), gradient times
+ * 1 - tanh^2) and a z-loss lambda lse^2 is added per valid row (its gradient
+ * 2 lambda lse p[c], scaled by 1 / valid rows under mean): see vsce_problem.
  *
  * Sources (page titles and sections):
  *  - Liger-Kernel PR #1268 "perf(ce): single-shot dx_y gradient correction":
@@ -100,6 +103,8 @@ enum {
 #define VSCE_WS_N_VALID 16   /* int64: rows whose target is in [0, vocab)     */
 #define VSCE_WS_N_INVALID 24 /* int64: rows with a bad target                 */
 #define VSCE_WS_STATUS 32    /* uint32: VSCE_STATUS_* bits of the last forward */
+#define VSCE_WS_INV_W 40     /* float: 1 / W, rounded once to fp32             */
+#define VSCE_WS_INV_N_VALID 44 /* float: 1 / (rows whose target is in range)   */
 #define VSCE_WS_HEADER_BYTES 256
 
 /* Bytes of workspace a problem with `rows` rows needs (0 if rows < 0). */
@@ -117,6 +122,22 @@ size_t vsce_workspace_bytes(int64_t rows);
  *  ignore_index    target value of rows to ignore (PyTorch default -100); it
  *                  is tested before the range check, so it may lie in [0, V)
  *  label_smoothing eps in [0, 1]
+ *  softcap         s >= 0, finite.  s > 0 replaces every logit x by the
+ *                  capped logit s * tanh(x / s) before anything else reads it
+ *                  (maximum, softmax, smoothing sum, statistics), and the
+ *                  gradient with respect to x takes the factor
+ *                  1 - tanh^2(x / s); s = 0 leaves the logits as they are.
+ *                  (Liger-Kernel PR #1268 names soft-capping among the CE
+ *                  features its target correction keeps, What changed and
+ *                  Correctness; this is the plain definition.)  The token
+ *                  accuracy compares the target with the maximum of the stored
+ *                  logits, which capping does not reorder.
+ *  z_loss          lambda >= 0, finite.  Adds lambda * lse^2 to the loss of
+ *                  every valid row, lse being the log-sum-exp of the (capped)
+ *                  logits (the z-loss that PR #1268 lists in its Correctness
+ *                  section).  It is not multiplied by class weights, and the
+ *                  mean reduction divides it by the number of valid rows
+ *                  (the cross-entropy part keeps W).  0: off.
  */
 typedef struct vsce_problem {
   int64_t rows;
@@ -128,6 +149,8 @@ typedef struct vsce_problem {
   const float *class_weight;
   int64_t ignore_index;
   float label_smoothing;
+  float softcap;
+  float z_loss;
   int32_t reserved; /* must be 0 */
 } vsce_problem;
 
@@ -139,12 +162,16 @@ typedef struct vsce_problem {
  *  token_acc  optional [rows]: 1 where the row is valid and the first index of
  *             its maximum equals the target, else 0.
  *  acc_mean   optional [1]: the mean of token_acc over valid rows (NaN if none).
+ *  z_loss     optional: the z-loss part of the loss alone, reduced like the
+ *             loss ([1] for mean, over valid rows, and sum; [rows] for none).
+ *             Zeros when the problem's z_loss is 0.
  */
 typedef struct vsce_outputs {
   float *loss;
   float *row_loss;
   float *token_acc;
   float *acc_mean;
+  float *z_loss;
 } vsce_outputs;
 
 /*
@@ -152,7 +179,8 @@ typedef struct vsce_outputs {
  * with the linkedin#1329 fp32 true-class fold; PR #1622 device-side
  * normalizers).  Reads every valid row once, writes the loss outputs, and
  * overwrites `logits_inout` (a [rows, row_stride] buffer of `dtype`) with the
- * gradient of the reduced loss for grad_output = 1: sigma = 1/W for mean, 1
+ * gradient of the reduced loss for grad_output = 1: sigma = 1/W for mean (and
+ * 1/valid rows for the z-loss part), 1
  * for sum and none.  Ignored and bad-target rows are overwritten with zeros.
  * Columns in [vocab, row_stride) are neither read nor written.  Apply a
  * grad_output other than 1 afterwards with ce_scale_grad.

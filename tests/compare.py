@@ -5,8 +5,17 @@ the buffer type of the oracle's exact value rounded once to that type
 (``strict``), or, where the gradient is a difference of nearly equal terms
 (label smoothing, fp32 buffers), within the error of evaluating that
 difference in fp32 (``floor``):
-    |g - g64| <= 2^-24 (|x_c - lse| + log2 V + 8) sigma (p_c |A| + eta |w_c|
-                 + (1 - eps) w_y [c == y])
+    |g - g64| <= 2^-24 (|xt_c - lse| + log2 V + 8 + 8 s + 4 |x_c| / s) k_c
+                 (p_c |sigma A + Z| + sigma eta |w_c| + sigma (1 - eps) w_y [c == y])
+with xt the (soft-capped) logits, s the cap (0 without; then the s terms
+drop), k_c the cap's slope 1 - tanh^2(x_c / s) (1 without), and
+Z = sigma_z 2 lambda lse the z-loss coefficient (0 without).  The 8 s term is
+the fp32 capped value's absolute error (a few units of 2^-24 s from exp,
+reciprocal and products), which enters exp(xt - m) through both xt_c and the
+capped maximum.  The 4 |x_c| / s term is the conditioning of the slope
+4 q / (1 + q)^2, q = exp(-2 |x_c| / s): the fp32 exponent argument carries a
+relative error of about 2^-23, so q (and the slope) carries one of about
+2 |x_c| / s * 2^-23 -- measured at up to 0.91 of this term on a fine grid.
 The strict fraction must be 1 for bf16/fp16 buffers without label smoothing;
 the floored fraction must be 1 everywhere.
 """
@@ -47,9 +56,12 @@ class GradReport:
 
 def grad_report(g: np.ndarray, g64: np.ndarray, dtype: str, x: np.ndarray, target: np.ndarray,
                 stats: np.ndarray, cls: np.ndarray, scale: np.ndarray, eps: float,
-                weight=None, sum_w=None) -> GradReport:
+                weight=None, sum_w=None, softcap: float = 0.0, z_loss: float = 0.0,
+                scale_z=None) -> GradReport:
     """g: GPU gradient (fp64 copy), g64: oracle exact scaled gradient, rows
-    aligned; x: logits; stats: oracle (m, d', x_y, S); scale: per-row sigma."""
+    aligned; x: stored logits; stats: oracle (m, d', x_y, S) of the capped
+    logits; scale / scale_z: per-row factors of the cross-entropy and z-loss
+    parts."""
     g = np.asarray(g, dtype=np.float64)
     rn = oracle.round_to(g64, dtype)
     u = ulp(rn, dtype)
@@ -68,13 +80,22 @@ def grad_report(g: np.ndarray, g64: np.ndarray, dtype: str, x: np.ndarray, targe
             continue
         m, dp = stats[r, 0], stats[r, 1]
         lse = m + math.log1p(dp)
-        p = np.exp(x[r] - lse)
+        if softcap > 0:
+            xt = softcap * np.tanh(x[r] / softcap)
+            slope = 1.0 / np.cosh(x[r] / softcap) ** 2
+            cap_terms = 8 * softcap + 4 * np.abs(x[r]) / softcap
+        else:
+            xt, slope, cap_terms = x[r], 1.0, 0.0
+        p = np.exp(xt - lse)
         y = int(target[r])
         wy = w[y]
         A = (1 - eps) * wy + eta * sw
-        mag = p * abs(A) + eta * np.abs(w)
-        mag[y] += (1 - eps) * wy
-        tol = 2.0 ** -24 * (np.abs(x[r] - lse) + math.log2(V) + 8) * abs(scale[r]) * mag
+        sz = 0.0 if scale_z is None else scale_z[r]
+        Z = sz * 2.0 * z_loss * lse
+        sg = abs(scale[r])
+        mag = p * abs(scale[r] * A + Z) + sg * eta * np.abs(w)
+        mag[y] += sg * (1 - eps) * wy
+        tol = 2.0 ** -24 * (np.abs(xt - lse) + math.log2(V) + 8 + cap_terms) * mag * slope
         floor_ok[r] |= np.abs(g[r] - g64[r]) <= tol + u[r]
     with np.errstate(invalid="ignore"):
         units = np.where(u > 0, diff / u, 0.0)

@@ -37,11 +37,12 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_workspace_size():
-    assert L.vsce_version() >= 100
+    assert L.vsce_version() >= 200
     assert L.vsce_workspace_bytes(-1) == 0
     assert L.vsce_workspace_bytes(0) == L.WS_HEADER_BYTES
-    assert L.vsce_workspace_bytes(1) == L.WS_HEADER_BYTES + 2 * 256
-    assert L.vsce_workspace_bytes(8192) == L.WS_HEADER_BYTES + 2 * 8192 * 4
+    # header, then [rows] fp32 scratch for row losses, accuracies and z-losses
+    assert L.vsce_workspace_bytes(1) == L.WS_HEADER_BYTES + 3 * 256
+    assert L.vsce_workspace_bytes(8192) == L.WS_HEADER_BYTES + 3 * 8192 * 4
 
 
 def test_header_constants_match_the_binding():
@@ -49,15 +50,26 @@ def test_header_constants_match_the_binding():
     defines = {m.group(1): int(m.group(2), 0)
                for m in re.finditer(r"^#define\s+VSCE_(\w+)\s+(\w+)", text, flags=re.M)
                if re.fullmatch(r"0x[0-9a-fA-F]+|\d+", m.group(2))}
-    for name in ("WS_W", "WS_SUM_W", "WS_N_VALID", "WS_N_INVALID", "WS_STATUS",
-                 "WS_HEADER_BYTES", "STATS_STRIDE"):
+    for name in ("WS_W", "WS_SUM_W", "WS_N_VALID", "WS_N_INVALID", "WS_STATUS", "WS_INV_W",
+                 "WS_INV_N_VALID", "WS_HEADER_BYTES", "STATS_STRIDE"):
         assert defines[name] == getattr(L, name), name
 
 
 def test_struct_layout_matches_the_header():
-    assert ctypes.sizeof(L.Problem) == 64
+    assert ctypes.sizeof(L.Problem) == 72
     assert L.Problem.label_smoothing.offset == 56
-    assert ctypes.sizeof(L.Outputs) == 32
+    assert L.Problem.softcap.offset == 60
+    assert L.Problem.z_loss.offset == 64
+    assert L.Problem.reserved.offset == 68
+    assert ctypes.sizeof(L.Outputs) == 40
+    assert L.Outputs.z_loss.offset == 32
+    # the header declares the fields in the same order
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct vsce_problem \{(.*?)\}", text, re.S).group(1)
+    names = re.findall(r"(\w+)\s*;", body)
+    assert names == [f[0] for f in L.Problem._fields_]
+    body = re.search(r"typedef struct vsce_outputs \{(.*?)\}", text, re.S).group(1)
+    assert re.findall(r"(\w+)\s*;", body) == [f[0] for f in L.Outputs._fields_]
 
 
 def _problem(**kw):
@@ -66,6 +78,7 @@ def _problem(**kw):
     p.dtype, p.reduction = L.BF16, L.REDUCTION_MEAN
     p.target, p.class_weight = FAKE, None
     p.ignore_index, p.label_smoothing, p.reserved = -100, 0.0, 0
+    p.softcap, p.z_loss = 0.0, 0.0
     for k, v in kw.items():
         setattr(p, k, v)
     return p
@@ -92,6 +105,8 @@ def _stats(p, stats=FAKE, logits=FAKE, ws=FAKE):
     ("rows", -1), ("vocab", 0), ("vocab", -3), ("row_stride", 63), ("dtype", 3), ("dtype", -1),
     ("reduction", 3), ("reserved", 1), ("label_smoothing", -0.1), ("label_smoothing", 1.5),
     ("label_smoothing", float("nan")), ("target", None),
+    ("softcap", -1.0), ("softcap", float("nan")), ("softcap", float("inf")),
+    ("z_loss", -1e-4), ("z_loss", float("nan")), ("z_loss", float("inf")),
 ])
 def test_bad_problem_fields_are_rejected(field, value):
     assert _fused(_problem(**{field: value})) == L.ERR_INVALID

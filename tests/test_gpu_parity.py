@@ -45,12 +45,13 @@ def _go_tensor(go, reduction, rows, dev):
 
 
 def run(wl, mode, reduction, go, accuracy=False, row_stride=None, check_rows=None,
-        x_host=None, tgt=None, inplace_backward=False):
+        x_host=None, tgt=None, inplace_backward=False, softcap=0.0, z_loss=0.0):
     """Runs one forward + backward through the C ABI and returns GPU results
     (host copies) next to the oracle's."""
     dev = _dev()
     _note(f"{wl.name} BT={wl.BT} V={wl.V} {wl.dtype} mode={mode} red={reduction} go={go} "
-          f"stride={row_stride}")
+          f"stride={row_stride} softcap={softcap} z_loss={z_loss}")
+    feat = dict(softcap=softcap, z_loss=z_loss)
     tgt = W.targets(wl) if tgt is None else tgt
     w = W.class_weights(wl)
     x_host = W.logits(wl, tgt) if x_host is None else x_host
@@ -66,14 +67,15 @@ def run(wl, mode, reduction, go, accuracy=False, row_stride=None, check_rows=Non
     go_t = _go_tensor(go, reduction, wl.BT, dev)
     if mode == "fused":
         res = vf.forward_fused_inplace(x, t, wt, -100, eps, reduction, row_loss=True,
-                                       accuracy=accuracy)
+                                       accuracy=accuracy, return_z_loss=True, **feat)
         vf.scale_grad(x, go_t, reduction)
         g = x
         stats = None
     else:
-        res = vf.forward_stats(x, t, wt, -100, eps, reduction, row_loss=True, accuracy=accuracy)
+        res = vf.forward_stats(x, t, wt, -100, eps, reduction, row_loss=True, accuracy=accuracy,
+                               return_z_loss=True, **feat)
         g = vf.backward_from_stats(x, t, res["stats"], go_t, res["workspace"], wt, -100, eps,
-                                   reduction, out=x if inplace_backward else None)
+                                   reduction, out=x if inplace_backward else None, **feat)
         stats = res["stats"].cpu().numpy().astype(np.float64)
     torch.cuda.synchronize()
     if stride > wl.V:
@@ -81,6 +83,7 @@ def run(wl, mode, reduction, go, accuracy=False, row_stride=None, check_rows=Non
     out = {
         "loss": res["loss"].cpu().numpy().astype(np.float64),
         "row_loss": res["row_loss"].cpu().numpy().astype(np.float64),
+        "z_loss": res["z_loss"].cpu().numpy().astype(np.float64),
         "stats": stats,
         "status": vf.status(res["workspace"]),
         "acc": None if not accuracy else res["token_acc"].cpu().numpy().astype(np.float64),
@@ -92,11 +95,13 @@ def run(wl, mode, reduction, go, accuracy=False, row_stride=None, check_rows=Non
     return out, x_host, tgt, w
 
 
-def reference(wl, x_host, tgt, w, reduction, go, rows=None):
+def reference(wl, x_host, tgt, w, reduction, go, rows=None, softcap=0.0, z_loss=0.0):
     """Oracle over all rows (losses, stats) and the gradient of `rows`."""
     BT = wl.BT
     nz = oracle.normalizer(tgt, wl.V, w)
+    feat = dict(softcap=softcap, z_loss=z_loss)
     loss_rows = np.empty(BT)
+    z_rows = np.empty(BT)
     stats = np.empty((BT, 4))
     am = np.empty(BT, np.int64)
     cls = np.empty(BT, np.int32)
@@ -104,33 +109,43 @@ def reference(wl, x_host, tgt, w, reduction, go, rows=None):
     for r0 in range(0, BT, chunk):
         r1 = min(BT, r0 + chunk)
         r = oracle.rows(W.as_f64(x_host[r0:r1]), tgt[r0:r1], w, -100, wl.label_smoothing,
-                        want_grad=False)
-        loss_rows[r0:r1], stats[r0:r1], am[r0:r1], cls[r0:r1] = r.loss, r.stats, r.argmax, r.cls
+                        want_grad=False, **feat)
+        loss_rows[r0:r1], z_rows[r0:r1] = r.loss, r.z
+        stats[r0:r1], am[r0:r1], cls[r0:r1] = r.stats, r.argmax, r.cls
     rows = np.arange(BT) if rows is None else np.asarray(rows)
     scale = oracle.grad_scale(reduction, nz.W, go, BT)
+    scale_z = oracle.grad_scale(reduction, float(nz.n_valid), go, BT)
     g64 = np.zeros((len(rows), wl.V))
     for i0 in range(0, len(rows), chunk):
         sel = rows[i0:i0 + chunk]
         r = oracle.rows(W.as_f64(x_host[torch.from_numpy(sel)]), tgt[sel], w, -100,
-                        wl.label_smoothing, want_grad=True)
-        gg = r.grad * scale[sel][:, None]
+                        wl.label_smoothing, want_grad=True, scale=scale[sel],
+                        scale_z=scale_z[sel], **feat)
+        gg = r.grad
         gg[r.cls != 0] = 0.0
         g64[i0:i0 + len(sel)] = gg
     acc, acc_mean = oracle.token_accuracy(am, tgt, cls)
     return {
-        "loss": oracle.reduce_loss(loss_rows, cls, nz.W, reduction),
+        "loss": oracle.reduce_loss(loss_rows, cls, nz.W, reduction, z_rows, nz.n_valid),
+        "z_loss": oracle.reduce_loss(z_rows, cls, float(nz.n_valid), reduction),
         "row_loss": loss_rows, "stats": stats, "cls": cls, "norm": nz, "scale": scale,
-        "rows": rows, "grad": g64, "acc": acc, "acc_mean": acc_mean,
+        "scale_z": scale_z, "rows": rows, "grad": g64, "acc": acc, "acc_mean": acc_mean,
+        "softcap": softcap, "z": z_loss,
     }
 
 
 def check(wl, out, ref, x_host, tgt, w, strict_bf16=None):
+    cap, lam = ref["softcap"], ref["z"]
     assert_loss_close(out["loss"], ref["loss"], 1e-5, "reduced loss")
     assert_loss_close(out["row_loss"], ref["row_loss"], 1e-5, "row loss")
+    if lam > 0:
+        assert_loss_close(out["z_loss"], ref["z_loss"], 1e-5, "z-loss")
+    else:
+        assert np.all((out["z_loss"] == 0) | np.isnan(np.asarray(ref["loss"]))), "z-loss without one"
     rows = ref["rows"]
     rep = grad_report(out["grad"], ref["grad"], wl.dtype, W.as_f64(x_host[torch.from_numpy(rows)]),
                       tgt[rows], ref["stats"][rows], ref["cls"][rows], ref["scale"][rows],
-                      wl.label_smoothing, w, ref["norm"].sum_w)
+                      wl.label_smoothing, w, ref["norm"].sum_w, cap, lam, ref["scale_z"][rows])
     print(f"  grad: n={rep.n} strict_fail={rep.strict_fail} floor_fail={rep.floor_fail} "
           f"max_ulp={rep.max_ulp:.2f}", flush=True)
     assert rep.floor_fail == 0, rep
@@ -139,11 +154,17 @@ def check(wl, out, ref, x_host, tgt, w, strict_bf16=None):
     if out["stats"] is not None:
         valid = ref["cls"] == 0
         s, r = out["stats"][valid], ref["stats"][valid]
-        np.testing.assert_array_equal(s[:, 0], r[:, 0])
-        np.testing.assert_array_equal(s[:, 2], r[:, 2])
+        if cap > 0:  # capped values: the fp32 cap is good to a few units of 2^-24 s
+            for k in (0, 2):
+                assert np.all(np.abs(s[:, k] - r[:, k]) <= 2.0 ** -24 * (8 * cap + np.abs(r[:, k])))
+        else:
+            np.testing.assert_array_equal(s[:, 0], r[:, 0])
+            np.testing.assert_array_equal(s[:, 2], r[:, 2])
         assert np.all(rel_err(s[:, 1], r[:, 1]) <= 1e-5), np.max(rel_err(s[:, 1], r[:, 1]))
         if wl.label_smoothing > 0:
             xa = np.abs(W.as_f64(x_host[torch.from_numpy(np.where(valid)[0])]))
+            if cap > 0:
+                xa = np.abs(cap * np.tanh(xa / cap)) + 8 * cap
             wa = np.ones(wl.V) if w is None else np.abs(w.astype(np.float64))
             bound = 64 * 2.0 ** -24 * (xa @ wa)
             assert np.all(np.abs(s[:, 3] - r[:, 3]) <= bound)
@@ -241,6 +262,76 @@ def test_wide_fp32_full_size():
     rows = _sample_rows(wl.BT, 16, 2)
     out, xh, tgt, w = run(wl, "split", "none", 1.0, accuracy=True, check_rows=rows)
     check(wl, out, reference(wl, xh, tgt, w, "none", 1.0, rows), xh, tgt, w)
+
+
+# ---------------------------------------------------------------- soft-capping and z-loss
+# Named by Liger-Kernel PR #1268 (What changed, Correctness) without formulas;
+# the oracle's plain definitions: capped logits s tanh(x / s) and lambda lse^2.
+
+FEATURES = [(30.0, 0.0), (0.0, 1e-4), (30.0, 1e-4)]
+
+
+@pytest.mark.parametrize("softcap,z_loss", FEATURES)
+@pytest.mark.parametrize("mode,go", [("fused", 1.0), ("split", 0.37)])
+def test_softcap_z_loss_llm_head_rows(softcap, z_loss, mode, go):
+    """The headline recipe (bf16, V = 128256, smoothing, ignored rows) on the
+    on-chip fused kernel and the split pair, every gradient element checked."""
+    wl = W.with_rows(W.WORKLOADS["llm_head"], 64)
+    kw = dict(softcap=softcap, z_loss=z_loss)
+    out, xh, tgt, w = run(wl, mode, "mean", go, accuracy=True, **kw)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", go, **kw), xh, tgt, w)
+
+
+@pytest.mark.parametrize("reduction,go", [("mean", 0.5), ("sum", 0.5), ("none", 0.5)])
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_softcap_z_loss_weighted_rows(reduction, go, mode):
+    """Class weights: the mean divides the cross-entropy by W and the z-loss by
+    the valid rows, so the two gradient scales differ."""
+    wl = W.with_rows(W.WORKLOADS["weighted"], 48)
+    kw = dict(softcap=15.0, z_loss=1e-3)
+    out, xh, tgt, w = run(wl, mode, reduction, go, **kw)
+    check(wl, out, reference(wl, xh, tgt, w, reduction, go, **kw), xh, tgt, w)
+
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_softcap_z_loss_wide_fp32_rows(mode):
+    """fp32 rows too long to keep on chip: the fused mode takes the streaming
+    kernel that reads the row twice."""
+    wl = W.with_rows(W.WORKLOADS["wide_fp32"], 24)
+    kw = dict(softcap=50.0, z_loss=1e-4)
+    out, xh, tgt, w = run(wl, mode, "none", 1.0, accuracy=True, **kw)
+    check(wl, out, reference(wl, xh, tgt, w, "none", 1.0, **kw), xh, tgt, w)
+
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_softcap_saturating_logits(mode, dtype):
+    """Logits far beyond a small cap: many capped values tie at +-s, the
+    slope underflows, and the accuracy still follows the stored logits."""
+    wl = _small("tiny", 40, 3000, dtype=dtype, sigma=40.0, ignore_frac=0.1, label_smoothing=0.1)
+    kw = dict(softcap=5.0, z_loss=0.05)
+    out, xh, tgt, w = run(wl, mode, "mean", 1.0, accuracy=True, **kw)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0, **kw), xh, tgt, w)
+
+
+@pytest.mark.parametrize("V", [7, 1001])
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_softcap_z_loss_scalar_path(V, mode):
+    """Row lengths that do not fill 16-byte vectors (per-element path)."""
+    wl = _small("llm_head", 21, V, ignore_frac=0.1)
+    kw = dict(softcap=20.0, z_loss=1e-2)
+    out, xh, tgt, w = run(wl, mode, "sum", 0.37, **kw)
+    check(wl, out, reference(wl, xh, tgt, w, "sum", 0.37, **kw), xh, tgt, w)
+
+
+def test_softcap_z_loss_llm_head_full_size():
+    """BT = 8192, V = 128256 bf16 with both features, fused: every row loss,
+    the reduced loss and z-loss, sampled gradient rows."""
+    wl = W.WORKLOADS["llm_head"]
+    rows = _sample_rows(wl.BT, 12, 3)
+    kw = dict(softcap=30.0, z_loss=1e-4)
+    out, xh, tgt, w = run(wl, "fused", "mean", 1.0, check_rows=rows, **kw)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0, rows, **kw), xh, tgt, w)
 
 
 # ---------------------------------------------------------------- edge cases

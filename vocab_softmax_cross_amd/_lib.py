@@ -22,6 +22,7 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_LAUNCH = 0, -1, -2, -3
 STATUS_BAD_TARGET = 1
 STATS_STRIDE = 4
 WS_W, WS_SUM_W, WS_N_VALID, WS_N_INVALID, WS_STATUS, WS_HEADER_BYTES = 0, 8, 16, 24, 32, 256
+WS_INV_W, WS_INV_N_VALID = 40, 44
 
 EXPORTS = ("vsce_workspace_bytes", "ce_forward_fused_inplace", "ce_forward_fused_inplace_timed",
            "ce_forward_stats",
@@ -40,6 +41,8 @@ class Problem(ctypes.Structure):
         ("class_weight", c_void_p),
         ("ignore_index", c_int64),
         ("label_smoothing", c_float),
+        ("softcap", c_float),
+        ("z_loss", c_float),
         ("reserved", c_int32),
     ]
 
@@ -51,6 +54,7 @@ class Outputs(ctypes.Structure):
         ("row_loss", c_void_p),
         ("token_acc", c_void_p),
         ("acc_mean", c_void_p),
+        ("z_loss", c_void_p),
     ]
 
 

@@ -28,9 +28,15 @@ SOURCES = [
     "stream_f32.hip",
     "stream_bf16.hip",
     "stream_f16.hip",
+    "stream_f32_cap.hip",
+    "stream_bf16_cap.hip",
+    "stream_f16_cap.hip",
     "fused_f32.hip",
     "fused_bf16.hip",
     "fused_f16.hip",
+    "fused_f32_cap.hip",
+    "fused_bf16_cap.hip",
+    "fused_f16_cap.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -39,6 +39,9 @@ int check_problem(const vsce_problem* pb, const void* logits, Prob& p) {
   if (pb->reserved != 0) return VSCE_ERR_INVALID;
   const float eps = pb->label_smoothing;
   if (!(eps >= 0.0f && eps <= 1.0f)) return VSCE_ERR_INVALID;  // also rejects NaN
+  const float cap = pb->softcap, zl = pb->z_loss;
+  if (!(cap >= 0.0f && cap <= 3.0e38f)) return VSCE_ERR_INVALID;  // finite, not NaN
+  if (!(zl >= 0.0f && zl <= 3.0e38f)) return VSCE_ERR_INVALID;
   if (pb->rows > 0 && (!pb->target || !logits)) return VSCE_ERR_INVALID;
   if (logits && !aligned(logits, static_cast<uintptr_t>(eb))) return VSCE_ERR_INVALID;
   if (pb->class_weight && !aligned(pb->class_weight, 4)) return VSCE_ERR_INVALID;
@@ -56,6 +59,8 @@ int check_problem(const vsce_problem* pb, const void* logits, Prob& p) {
   p.ignore_index = pb->ignore_index;
   p.eps = eps;
   p.eta = eps / static_cast<float>(pb->vocab);
+  p.cap = cap;
+  p.zl = zl;
   p.elem_bytes = eb;
   const int vec = 16 / eb;
   p.vec_ok = aligned(logits, 16) && (pb->row_stride * eb) % 16 == 0 && pb->vocab % vec == 0 &&
@@ -73,15 +78,8 @@ int check_outputs(const vsce_outputs* out) {
   return VSCE_OK;
 }
 
-// Per-row destinations of the forward kernels.
-RowArgs row_args(const Prob& p, void* x, const vsce_outputs* out, void* workspace) {
-  RowArgs a = {};
-  char* ws = static_cast<char*>(workspace);
-  float* loss_scratch = reinterpret_cast<float*>(ws + VSCE_WS_HEADER_BYTES);
-  float* acc_scratch =
-      reinterpret_cast<float*>(ws + VSCE_WS_HEADER_BYTES + align_up(4 * p.rows));
-  a.x = x;
-  a.g = x;
+// The problem's fields every per-row kernel reads.
+void problem_args(const Prob& p, RowArgs& a) {
   a.stride = p.stride;
   a.V = p.V;
   a.target = p.target;
@@ -89,15 +87,38 @@ RowArgs row_args(const Prob& p, void* x, const vsce_outputs* out, void* workspac
   a.ignore_index = p.ignore_index;
   a.eps = p.eps;
   a.eta = p.eta;
+  a.cap = p.cap;
+  a.cap_k = p.cap > 0.0f ? static_cast<float>(-2.0 * 1.4426950408889634 / p.cap) : 0.0f;
+  a.zl = p.zl;
   a.mean = (p.red == VSCE_REDUCTION_MEAN);
+  a.rows = p.rows;
+}
+
+// Per-row destinations of the forward kernels.  The workspace holds, after
+// its header, [rows] scratch for the row losses, the accuracies and the
+// z-losses (each used when the caller's outputs do not take its place).
+RowArgs row_args(const Prob& p, void* x, const vsce_outputs* out, void* workspace) {
+  RowArgs a = {};
+  char* ws = static_cast<char*>(workspace);
+  float* loss_scratch = reinterpret_cast<float*>(ws + VSCE_WS_HEADER_BYTES);
+  float* acc_scratch =
+      reinterpret_cast<float*>(ws + VSCE_WS_HEADER_BYTES + align_up(4 * p.rows));
+  float* z_scratch =
+      reinterpret_cast<float*>(ws + VSCE_WS_HEADER_BYTES + 2 * align_up(4 * p.rows));
+  a.x = x;
+  a.g = x;
+  problem_args(p, a);
   if (p.red == VSCE_REDUCTION_NONE) {
     a.loss_rows = out->loss;
     a.loss_rows2 = out->row_loss;
+    a.z_rows = out->z_loss;
   } else {
     a.loss_rows = out->row_loss ? out->row_loss : loss_scratch;
+    // The mean splits the loss into its parts; the sum only needs them for
+    // the z-loss output.
+    a.z_rows = (p.zl != 0.0f || out->z_loss) ? z_scratch : nullptr;
   }
   a.acc_rows = out->token_acc ? out->token_acc : (out->acc_mean ? acc_scratch : nullptr);
-  a.rows = p.rows;
   a.ws = reinterpret_cast<const WsHeader*>(ws);
   return a;
 }
@@ -119,7 +140,8 @@ int forward_common(const Prob& p, RowArgs a, const vsce_outputs* out, void* work
     if (rc != VSCE_OK) return rc;
   }
   if (ev_end && hipEventRecord(ev_end, stream) != hipSuccess) return VSCE_ERR_LAUNCH;
-  return launch_finalize(p, a.loss_rows, a.acc_rows, out->loss, out->acc_mean, hdr, stream);
+  return launch_finalize(p, a.loss_rows, a.acc_rows, a.z_rows, out->loss, out->acc_mean,
+                         p.red == VSCE_REDUCTION_NONE ? nullptr : out->z_loss, hdr, stream);
 }
 
 }  // namespace
@@ -127,20 +149,34 @@ int forward_common(const Prob& p, RowArgs a, const vsce_outputs* out, void* work
 int launch_fused_resident(const Prob& p, RowArgs a, hipStream_t s) {
   if (!p.vec_ok) return VSCE_ERR_UNSUPPORTED;
   a.nvec = p.V / (16 / p.elem_bytes);
+  const bool cap = p.cap > 0.0f;
   switch (p.dt) {
-    case VSCE_F32: return fused_resident_dt<VSCE_F32>(p, a, s);
-    case VSCE_BF16: return fused_resident_dt<VSCE_BF16>(p, a, s);
-    case VSCE_F16: return fused_resident_dt<VSCE_F16>(p, a, s);
+    case VSCE_F32:
+      return cap ? fused_resident_dt<VSCE_F32, true>(p, a, s)
+                 : fused_resident_dt<VSCE_F32, false>(p, a, s);
+    case VSCE_BF16:
+      return cap ? fused_resident_dt<VSCE_BF16, true>(p, a, s)
+                 : fused_resident_dt<VSCE_BF16, false>(p, a, s);
+    case VSCE_F16:
+      return cap ? fused_resident_dt<VSCE_F16, true>(p, a, s)
+                 : fused_resident_dt<VSCE_F16, false>(p, a, s);
     default: return VSCE_ERR_INVALID;
   }
 }
 
 namespace {
 int stream_any(int which, const Prob& p, const RowArgs& a, hipStream_t s) {
+  const bool cap = p.cap > 0.0f && which != kStreamScale;
   switch (p.dt) {
-    case VSCE_F32: return stream_dt<VSCE_F32>(which, p, a, s);
-    case VSCE_BF16: return stream_dt<VSCE_BF16>(which, p, a, s);
-    case VSCE_F16: return stream_dt<VSCE_F16>(which, p, a, s);
+    case VSCE_F32:
+      return cap ? stream_dt<VSCE_F32, true>(which, p, a, s)
+                 : stream_dt<VSCE_F32, false>(which, p, a, s);
+    case VSCE_BF16:
+      return cap ? stream_dt<VSCE_BF16, true>(which, p, a, s)
+                 : stream_dt<VSCE_BF16, false>(which, p, a, s);
+    case VSCE_F16:
+      return cap ? stream_dt<VSCE_F16, true>(which, p, a, s)
+                 : stream_dt<VSCE_F16, false>(which, p, a, s);
     default: return VSCE_ERR_INVALID;
   }
 }
@@ -167,7 +203,7 @@ extern "C" {
 
 size_t vsce_workspace_bytes(int64_t rows) {
   if (rows < 0) return 0;
-  return static_cast<size_t>(VSCE_WS_HEADER_BYTES + 2 * align_up(4 * rows));
+  return static_cast<size_t>(VSCE_WS_HEADER_BYTES + 3 * align_up(4 * rows));
 }
 
 int ce_forward_fused_inplace(const vsce_problem* problem, void* logits_inout,
@@ -223,18 +259,10 @@ int ce_backward_from_stats(const vsce_problem* problem, const void* logits, void
   RowArgs a = {};
   a.x = const_cast<void*>(logits);
   a.g = grad;
-  a.stride = p.stride;
-  a.V = p.V;
-  a.target = p.target;
-  a.weight = p.weight;
-  a.ignore_index = p.ignore_index;
-  a.eps = p.eps;
-  a.eta = p.eta;
-  a.mean = (p.red == VSCE_REDUCTION_MEAN);
+  problem_args(p, a);
   a.stats = const_cast<float*>(stats);
   a.go = grad_output;
   a.go_stride = grad_output_stride;
-  a.rows = p.rows;
   a.ws = static_cast<const WsHeader*>(workspace);
   return launch_backward(p, a, stream);
 }
@@ -276,6 +304,6 @@ const char* vsce_strerror(int code) {
   }
 }
 
-int vsce_version(void) { return 100; }
+int vsce_version(void) { return 200; }
 
 }  // extern "C"

@@ -26,12 +26,16 @@ struct WsHeader {
   int64_t n_invalid;  // rows with a target neither ignore_index nor in [0, V)
   uint32_t status;    // VSCE_STATUS_* bits
   uint32_t pad0;
+  float inv_W;        // 1 / W in fp32 (the mean's gradient scale)
+  float inv_n_valid;  // 1 / n_valid in fp32 (the mean's z-loss gradient scale)
 };
 static_assert(offsetof(WsHeader, W) == VSCE_WS_W, "header layout");
 static_assert(offsetof(WsHeader, sum_w) == VSCE_WS_SUM_W, "header layout");
 static_assert(offsetof(WsHeader, n_valid) == VSCE_WS_N_VALID, "header layout");
 static_assert(offsetof(WsHeader, n_invalid) == VSCE_WS_N_INVALID, "header layout");
 static_assert(offsetof(WsHeader, status) == VSCE_WS_STATUS, "header layout");
+static_assert(offsetof(WsHeader, inv_W) == VSCE_WS_INV_W, "header layout");
+static_assert(offsetof(WsHeader, inv_n_valid) == VSCE_WS_INV_N_VALID, "header layout");
 static_assert(sizeof(WsHeader) <= VSCE_WS_HEADER_BYTES, "header layout");
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -191,6 +195,48 @@ __device__ __forceinline__ int fresh_tid() {
   asm volatile("" : "+v"(t));
   return t;
 }
+
+// A kernel's single by-value argument, read again from the kernel-argument
+// segment (where it sits at offset 0).  The segment pointer goes through an
+// empty asm, so the fields are loaded (scalar loads) where they are used
+// after that point, instead of being loaded at kernel entry and held in
+// scalar registers through the whole kernel.
+template <class T>
+__device__ __forceinline__ T fresh_args() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using KT = const __attribute__((address_space(4))) T;
+  KT* p = __builtin_bit_cast(KT*, __builtin_amdgcn_kernarg_segment_ptr());
+  asm volatile("" : "+s"(p));
+  return *p;
+#else  // the host pass only parses device code
+  return T{};
+#endif
+}
+
+// ---------------------------------------------------------------- soft-capping
+// Logit soft-capping x -> s tanh(x / s) and its slope 1 - tanh^2(x / s), both
+// from q = exp(-2 |x| / s) in [0, 1] through the identities
+//   tanh(|x| / s) = (1 - q) / (1 + q),   1 - tanh^2(x / s) = 4 q / (1 + q)^2,
+// with one hardware exp and one reciprocal.  q keeps its relative accuracy
+// for every x, so the slope does too (no 1 - t^2 cancellation where the cap
+// saturates); the capped value is accurate to a few units of 2^-24 s.
+// A NaN logit stays NaN; +-inf caps to +-s with slope 0.
+struct SoftCap {
+  float s;  // the cap, > 0
+  float k;  // -2 log2(e) / s
+
+  __device__ __forceinline__ float value(float x) const {
+    const float q = __builtin_amdgcn_exp2f(__builtin_fabsf(x) * k);
+    const float t = (1.0f - q) * __builtin_amdgcn_rcpf(1.0f + q);
+    return __builtin_copysignf(s * t, x);
+  }
+  __device__ __forceinline__ float value(float x, float& slope) const {
+    const float q = __builtin_amdgcn_exp2f(__builtin_fabsf(x) * k);
+    const float r = __builtin_amdgcn_rcpf(1.0f + q);
+    slope = 4.0f * q * r * r;
+    return __builtin_copysignf(s * ((1.0f - q) * r), x);
+  }
+};
 
 // ---------------------------------------------------------------- XCD-aware order
 // The chip hands consecutive workgroups of a launch to its 8 XCDs in turn

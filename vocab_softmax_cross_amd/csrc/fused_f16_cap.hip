@@ -1,0 +1,6 @@
+// Resident fused kernels for one element type (f16), soft-capped logits.
+#include "fused_impl.h"
+
+namespace vsce {
+template int fused_resident_dt<VSCE_F16, true>(const Prob&, const RowArgs&, hipStream_t);
+}  // namespace vsce

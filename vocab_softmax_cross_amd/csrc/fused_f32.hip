@@ -1,6 +1,6 @@
-// Resident fused kernels for one element type (f32).
+// Resident fused kernels for one element type (f32), stored logits as they are.
 #include "fused_impl.h"
 
 namespace vsce {
-template int fused_resident_dt<VSCE_F32>(const Prob&, const RowArgs&, hipStream_t);
+template int fused_resident_dt<VSCE_F32, false>(const Prob&, const RowArgs&, hipStream_t);
 }  // namespace vsce

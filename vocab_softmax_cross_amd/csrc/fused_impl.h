@@ -33,7 +33,11 @@ namespace {
 // LDS_CAP: vectors of LDS actually allocated (<= NLDS * NT).  The last LDS
 // slot may be partial: the shape then serves rows of at most NT * NREG +
 // LDS_CAP vectors, and no lane past that ever touches LDS.
-template <int DT, int NT, int NREG, int NLDS, int LDS_CAP, bool WEIGHTED, int WPE>
+// CAP: soft-capped logits.  The row maximum, its ties and its first index
+// are taken on the stored logits (capping does not reorder them); every sum,
+// the loss and the gradient read the capped values, and each gradient element
+// is multiplied by the slope of the cap at its own stored logit.
+template <int DT, int NT, int NREG, int NLDS, int LDS_CAP, bool WEIGHTED, bool CAP, int WPE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
 void fused_resident_kernel(const RowArgs a) {
   using D = Dt<DT>;
@@ -45,6 +49,7 @@ void fused_resident_kernel(const RowArgs a) {
   __shared__ uint4 xl[NLDS > 0 ? LDS_CAP : 1];
   __shared__ float red_max[NW];
   __shared__ float4 red_sum[NW];
+  __shared__ float xy_sh;  // the stored target logit, posted by its owner lane
 
   const int tid = threadIdx.x;
   const int64_t n = xcd_contiguous(blockIdx.x, a.rows);
@@ -58,11 +63,13 @@ void fused_resident_kernel(const RowArgs a) {
   auto lane_off = [&](int k) { return in_row(k) ? voff : kOutOfRange; };
   const int64_t y = a.target[n];
   const int cls = row_class(y, a.V, a.ignore_index);
+  const SoftCap cap{a.cap, a.cap_k};
 
   if (cls != kValid) {  // uniform over the workgroup: zero gradient, no read
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
     static_for<NREG + NLDS>([&](auto k) { buf_store16(rsrc, lane_off(k), k * SLOT_BYTES, z); });
-    if (tid == 0) store_row(a, n, (cls == kIgnored) ? 0.0f : __builtin_nanf(""), 0.0f);
+    const float l = (cls == kIgnored) ? 0.0f : __builtin_nanf("");
+    if (tid == 0) store_row(a, n, l, 0.0f, l);
     return;
   }
 
@@ -81,9 +88,6 @@ void fused_resident_kernel(const RowArgs a) {
     });
   }
 
-  // The target logit: issued after the row's loads and consumed after pass 2,
-  // so its latency never holds up the row stream.
-  const float xy_lane = D::load1(rowb, y);
 
   // ---- pass 1: row maximum
   float mx = -__builtin_inff();
@@ -114,8 +118,33 @@ void fused_resident_kernel(const RowArgs a) {
       if (in_row(NREG + k)) max_vec(xl[k * NT + tid]);
     });
   }
-  const float M = block_max<NT>(mx, red_max);
-  const float ML = M * kLog2e;
+  // The lane that holds column y posts x[y] to LDS (read by every wavefront
+  // after the next barrier): no second load of it, and no register holding
+  // it through pass 2.
+  const int64_t jy = y / VEC;
+  const int ky = static_cast<int>(jy / NT);  // slot and lane owning the target
+  const int ty = static_cast<int>(jy % NT);
+  const int iy = static_cast<int>(y % VEC);
+  if (tid == ty) {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (ky < NREG) {
+      static_for<NREG>([&](auto k) {
+        if (k == ky) v = r[k];
+      });
+    } else if constexpr (NLDS > 0) {
+      v = xl[(ky - NREG) * NT + ty];
+    }
+    float f[VEC];
+    D::unpack(v, f);
+    float xv = f[0];
+#pragma unroll
+    for (int e = 1; e < VEC; ++e)
+      if (e == iy) xv = f[e];
+    xy_sh = xv;
+  }
+  const float M = block_max<NT>(mx, red_max);          // of the stored logits
+  const float Mc = CAP ? uniform(cap.value(M)) : M;    // of the logits the loss reads
+  const float ML = Mc * kLog2e;
 
   // ---- pass 2: sums below the maximum, ties, first index, logit sum
   RowSums rs = {0.0f, 0.0f, 0, 0x7fffffff};
@@ -128,7 +157,8 @@ void fused_resident_kernel(const RowArgs a) {
 #pragma unroll
       for (int e = 0; e < EPW; ++e) {
         const int i = q * EPW + e;  // element within the vector
-        const float ex = exp_shifted(f[e], ML);
+        const float fc = CAP ? cap.value(f[e]) : f[e];
+        const float ex = exp_shifted(fc, ML);
         if constexpr (decltype(careful)::value) {
           const bool eq = (f[e] == M);
           rs.s += eq ? 0.0f : ex;
@@ -137,8 +167,8 @@ void fused_resident_kernel(const RowArgs a) {
         } else {
           rs.s += ex;
         }
-        if constexpr (WEIGHTED) rs.S = __builtin_fmaf(a.weight[j * VEC + i], f[e], rs.S);
-        else rs.S += f[e];
+        if constexpr (WEIGHTED) rs.S = __builtin_fmaf(a.weight[j * VEC + i], fc, rs.S);
+        else rs.S += fc;
       }
     }
   };
@@ -157,24 +187,35 @@ void fused_resident_kernel(const RowArgs a) {
   rs = block_sums<NT>(rs, red_sum);
 
   const float dp = rs.s + static_cast<float>(rs.cnt - 1);  // d' = d - 1
-  const float xy = uniform(xy_lane);
+  // What only the row's end needs (normalizers, outputs, z-loss) is read from
+  // the arguments here rather than held in registers since the kernel began.
+  const RowArgs& a0 = a;
+  const RowArgs ra = fresh_args<RowArgs>();
+  {
+  const RowArgs& a = ra;
+  const float xy_stored = uniform(xy_sh);  // posted before the pass-1 barrier
+  const float xy = CAP ? uniform(cap.value(xy_stored)) : xy_stored;
   const float sum_w = uniform(static_cast<float>(a.ws->sum_w));
   const float wy = uniform(WEIGHTED ? a.weight[y] : 1.0f);
-  if (tid == 0)
-    store_row(a, n, row_loss(M, dp, xy, rs.S, wy, sum_w, a.eps, a.eta),
-              (static_cast<int64_t>(rs.first) == y) ? 1.0f : 0.0f);
+  const float lg = uniform(log1pf(dp));  // lse - m, once per row
+  if (tid == 0) {
+    const float zrow = row_z(Mc, lg, a.zl);
+    store_row(a, n, row_loss(Mc, lg, xy, rs.S, wy, sum_w, a.eps, a.eta) + zrow,
+              (static_cast<int64_t>(rs.first) == y) ? 1.0f : 0.0f, zrow);
+  }
 
   // ---- pass 3: gradient over the on-chip row, one store per vector
-  const float sigma = uniform(a.mean ? static_cast<float>(1.0 / a.ws->W) : 1.0f);
-  RowTerms t = row_terms(M, dp, xy, wy, sum_w, a.eps, a.eta, sigma);
+  const float sigma = uniform(a.mean ? a.ws->inv_W : 1.0f);
+  RowTerms t = row_terms(Mc, dp, lg, xy, wy, sum_w, a.eps, a.eta, sigma, a.zl, z_sigma(a));
+  if constexpr (CAP) {
+    float slope_y;
+    cap.value(xy_stored, slope_y);
+    t.dxy *= slope_y;  // the owner stores the finished value
+  }
   t.ML = uniform(t.ML);
   t.K = uniform(t.K);
   t.B = uniform(t.B);
   t.dxy = uniform(t.dxy);
-  const int64_t jy = y / VEC;
-  const int ky = static_cast<int>(jy / NT);  // slot and lane owning the target
-  const int ty = static_cast<int>(jy % NT);
-  const int iy = static_cast<int>(y % VEC);
   auto grad_vec = [&](const uint4 v, int k) {
     const int j = k * NT + tid;
     auto w = words(v);
@@ -185,7 +226,13 @@ void fused_resident_kernel(const RowArgs a) {
 #pragma unroll
       for (int e = 0; e < EPW; ++e) {
         const float b = WEIGHTED ? t.B * a.weight[j * VEC + q * EPW + e] : t.B;
-        f[e] = __builtin_fmaf(exp_shifted(f[e], t.ML), t.K, -b);
+        if constexpr (CAP) {
+          float slope;
+          const float fc = cap.value(f[e], slope);
+          f[e] = __builtin_fmaf(exp_shifted(fc, t.ML), t.K, -b) * slope;
+        } else {
+          f[e] = __builtin_fmaf(exp_shifted(f[e], t.ML), t.K, -b);
+        }
       }
       w.w[q] = D::pack_word(f);  // the result word replaces the input word
     }
@@ -214,6 +261,8 @@ void fused_resident_kernel(const RowArgs a) {
   static_for<NLDS>([&](auto k) {
     if (in_row(NREG + k)) grad_vec(xl[k * NT + tid], NREG + k);
   });
+  }
+  (void)a0;
 }
 
 // Shapes of the resident kernel: threads per workgroup, vectors per thread in
@@ -235,36 +284,31 @@ using Shapes = std::tuple<Shape<64, 4, 0, 4>,       // rows up to 256 vectors
                           Shape<1024, 16, 4, 4>,    // 20480 vectors
                           Shape<1024, 24, 8, 4>>;   // 32768 vectors
 
-template <int DT, bool W, class SH>
+template <int DT, bool W, bool CAP, class SH>
 int launch_shape(const Prob& p, const RowArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(
-      (fused_resident_kernel<DT, SH::NT, SH::NREG, SH::NLDS, SH::LDS_CAP, W, SH::WPE>),
+      (fused_resident_kernel<DT, SH::NT, SH::NREG, SH::NLDS, SH::LDS_CAP, W, CAP, SH::WPE>),
                      dim3(static_cast<unsigned>(p.rows)), dim3(SH::NT), 0, s, a);
   return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
 }
 
-template <int DT, bool W, size_t I = 0>
+template <int DT, bool W, bool CAP, size_t I = 0>
 int pick_shape(const Prob& p, const RowArgs& a, hipStream_t s) {
   if constexpr (I == std::tuple_size<Shapes>::value) {
     return VSCE_ERR_UNSUPPORTED;
   } else {
     using SH = std::tuple_element_t<I, Shapes>;
     if (a.nvec <= SH::CAPACITY)
-      return launch_shape<DT, W, SH>(p, a, s);
-    return pick_shape<DT, W, I + 1>(p, a, s);
+      return launch_shape<DT, W, CAP, SH>(p, a, s);
+    return pick_shape<DT, W, CAP, I + 1>(p, a, s);
   }
-}
-
-template <int DT>
-int dispatch_weighted(const Prob& p, const RowArgs& a, hipStream_t s) {
-  return p.weight ? pick_shape<DT, true>(p, a, s) : pick_shape<DT, false>(p, a, s);
 }
 
 }  // namespace
 
-template <int DT>
+template <int DT, bool CAP>
 int fused_resident_dt(const Prob& p, const RowArgs& a, hipStream_t s) {
-  return dispatch_weighted<DT>(p, a, s);
+  return p.weight ? pick_shape<DT, true, CAP>(p, a, s) : pick_shape<DT, false, CAP>(p, a, s);
 }
 
 }  // namespace vsce

@@ -24,6 +24,8 @@ struct Prob {
   int64_t ignore_index;
   float eps;
   float eta;       // eps / V
+  float cap;       // soft-cap s (0: off)
+  float zl;        // z-loss lambda (0: off)
   int elem_bytes;
   bool vec_ok;     // rows start 16-byte aligned and V fills whole 16-byte vectors
 };
@@ -40,10 +42,14 @@ struct RowArgs {
   int64_t ignore_index;
   float eps;
   float eta;
+  float cap;            // soft-cap s (the CAP kernels only)
+  float cap_k;          // -2 log2(e) / s
+  float zl;             // z-loss lambda (0: off)
   int mean;             // sigma = 1 / W (mean) else 1
   float* loss_rows;     // [rows] per-row loss (never null)
   float* loss_rows2;    // [rows] second copy of the per-row loss, or null
   float* acc_rows;      // [rows] or null
+  float* z_rows;        // [rows] per-row z-loss, or null
   float* stats;         // [rows][4] or null
   const float* go;      // grad_output (backward / scale)
   int64_t go_stride;    // 0 (scalar) or 1 (per row)
@@ -54,17 +60,18 @@ struct RowArgs {
 };
 
 int launch_prologue(const Prob& p, WsHeader* ws, hipStream_t s);
-int launch_finalize(const Prob& p, const float* loss_rows, const float* acc_rows, float* loss_out,
-                    float* acc_mean_out, const WsHeader* ws, hipStream_t s);
+int launch_finalize(const Prob& p, const float* loss_rows, const float* acc_rows,
+                    const float* z_rows, float* loss_out, float* acc_mean_out, float* z_out,
+                    const WsHeader* ws, hipStream_t s);
 
 // Row held on chip (registers + LDS) between its passes: one logits read and
 // one gradient write.  VSCE_ERR_UNSUPPORTED when the row does not fit.
 int launch_fused_resident(const Prob& p, RowArgs a, hipStream_t s);
-template <int DT>
+template <int DT, bool CAP>
 int fused_resident_dt(const Prob& p, const RowArgs& a, hipStream_t s);
 // Streaming kernels by element type; `which` is kStreamStats .. kStreamScale.
 enum { kStreamStats = 0, kStreamFused = 1, kStreamBackward = 2, kStreamScale = 3 };
-template <int DT>
+template <int DT, bool CAP>
 int stream_dt(int which, const Prob& p, const RowArgs& a, hipStream_t s);
 // Any row length: the row is streamed twice (statistics, then gradient).
 int launch_fused_stream(const Prob& p, RowArgs a, hipStream_t s);

@@ -6,10 +6,13 @@
 //                   multiplies; its Details note that avoiding the host sync
 //                   needs the count passed to the kernel as a device pointer,
 //                   which is what this header in the workspace is), plus the
-//                   bad-target status bit.
-//  finalize_kernel  the none / sum / mean reduction of the per-row losses and
-//                   the accuracy mean (accuracy divided by the count on the
-//                   device, same Summary).
+//                   bad-target status bit and the fp32 reciprocals of W and of
+//                   the valid count that the row kernels scale by.
+//  finalize_kernel  the none / sum / mean reduction of the per-row losses (a
+//                   mean divides the cross-entropy part by W and the z-loss
+//                   part by the valid-row count) and the accuracy mean
+//                   (accuracy divided by the count on the device, same
+//                   Summary).
 //
 // Both sum in fp64 in a fixed order (per-thread strided partial sums, then a
 // fixed tree), so results do not depend on scheduling and need no atomics.
@@ -67,26 +70,42 @@ __global__ __launch_bounds__(kSmallNT) void prologue_kernel(const int64_t* targe
     ws->n_invalid = static_cast<int64_t>(ni);
     ws->status = (ni > 0.0) ? VSCE_STATUS_BAD_TARGET : 0u;
     ws->pad0 = 0u;
+    // The row kernels' gradient scales, rounded once here rather than
+    // divided in every workgroup.
+    ws->inv_W = static_cast<float>(1.0 / W);
+    ws->inv_n_valid = static_cast<float>(1.0 / nv);
   }
 }
 
 __global__ __launch_bounds__(kSmallNT) void finalize_kernel(const float* loss_rows,
-                                                           const float* acc_rows, int64_t rows,
+                                                           const float* acc_rows,
+                                                           const float* z_rows, int64_t rows,
                                                            int red, float* loss_out,
-                                                           float* acc_mean_out,
+                                                           float* acc_mean_out, float* z_out,
                                                            const WsHeader* ws) {
   __shared__ double sh[kSmallNT / kWave];
   if (red != VSCE_REDUCTION_NONE) {
-    double t = 0.0;
+    double t = 0.0, z = 0.0;
 #pragma unroll 8
-    for (int64_t n = threadIdx.x; n < rows; n += kSmallNT) t += static_cast<double>(loss_rows[n]);
+    for (int64_t n = threadIdx.x; n < rows; n += kSmallNT) {
+      t += static_cast<double>(loss_rows[n]);
+      if (z_rows) z += static_cast<double>(z_rows[n]);
+    }
     t = block_sum_d(t, sh);
+    if (z_rows) z = block_sum_d(z, sh);
     if (threadIdx.x == 0) {
       if (red == VSCE_REDUCTION_MEAN) {
+        // Cross-entropy over W, z-loss over the valid rows (they differ only
+        // with class weights).
         const double W = ws->W;
-        loss_out[0] = static_cast<float>(W != 0.0 ? t / W : __builtin_nan(""));
+        const double nv = static_cast<double>(ws->n_valid);
+        const double ce = W != 0.0 ? (t - z) / W : __builtin_nan("");
+        const double zm = nv != 0.0 ? z / nv : __builtin_nan("");
+        loss_out[0] = static_cast<float>(z_rows ? ce + zm : ce);
+        if (z_out) z_out[0] = static_cast<float>(z_rows ? zm : 0.0);
       } else {
         loss_out[0] = static_cast<float>(t);
+        if (z_out) z_out[0] = static_cast<float>(z_rows ? z : 0.0);
       }
     }
   }
@@ -110,11 +129,13 @@ int launch_prologue(const Prob& p, WsHeader* ws, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
 }
 
-int launch_finalize(const Prob& p, const float* loss_rows, const float* acc_rows, float* loss_out,
-                    float* acc_mean_out, const WsHeader* ws, hipStream_t s) {
+int launch_finalize(const Prob& p, const float* loss_rows, const float* acc_rows,
+                    const float* z_rows, float* loss_out, float* acc_mean_out, float* z_out,
+                    const WsHeader* ws, hipStream_t s) {
   if (p.red == VSCE_REDUCTION_NONE && acc_mean_out == nullptr) return VSCE_OK;
-  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kSmallNT), 0, s, loss_rows, acc_rows, p.rows,
-                     p.red, loss_out, acc_mean_out, ws);
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kSmallNT), 0, s, loss_rows, acc_rows,
+                     p.red == VSCE_REDUCTION_NONE ? nullptr : z_rows, p.rows, p.red, loss_out,
+                     acc_mean_out, z_out, ws);
   return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
 }
 

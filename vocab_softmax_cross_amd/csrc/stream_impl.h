@@ -19,6 +19,11 @@
 // max M is known, the lanes whose own max equals M recompute their sum with
 // the elements equal to M left out (re-reading their share of the row), so
 // d' = d - 1 never loses the small terms to the leading 1.
+//
+// CAP (soft-capped logits): maxima, ties and the first index are taken on the
+// stored logits, sums on the capped ones (the shift of a lane's sum is the
+// capped value of its stored maximum), and every gradient element is
+// multiplied by the slope of the cap at its stored logit.
 #pragma once
 
 #include <tuple>
@@ -68,9 +73,10 @@ struct Grp {
   }
 };
 
-// Per-row statistics by streaming: returns (M, d', S, first) on every thread.
-// Must be called by the whole workgroup (it contains barriers).
-template <int DT, int NT, int U, bool WEIGHTED, bool VECP>
+// Per-row statistics by streaming: returns (M, d', S, first) on every thread,
+// M being the (capped) maximum the loss reads.  Must be called by the whole
+// workgroup (it contains barriers).
+template <int DT, int NT, int U, bool WEIGHTED, bool VECP, bool CAP>
 __device__ inline void stream_stats(const RowArgs& a, const char* row, float& M_out,
                                     float& dp_out, float& S_out, int& first_out, float* red_max,
                                     float4* red_sum) {
@@ -78,6 +84,8 @@ __device__ inline void stream_stats(const RowArgs& a, const char* row, float& M_
   constexpr int E = G::E;
   const int tid = threadIdx.x;
   const int64_t ng = a.nvec;
+  const SoftCap cap{a.cap, a.cap_k};
+  auto capped = [&](float v) { return CAP ? cap.value(v) : v; };
   float m = -__builtin_inff(), s = 0.0f, S = 0.0f;
 
   for (int64_t g0 = 0; g0 < ng; g0 += static_cast<int64_t>(NT) * U) {
@@ -96,26 +104,28 @@ __device__ inline void stream_stats(const RowArgs& a, const char* row, float& M_
       }
     });
     if (bm > m) {
-      s *= __builtin_amdgcn_exp2f((m - bm) * kLog2e);
+      s *= __builtin_amdgcn_exp2f((capped(m) - capped(bm)) * kLog2e);
       m = bm;
     }
-    const float ML = (m == -__builtin_inff()) ? 0.0f : m * kLog2e;
+    const float ML = (m == -__builtin_inff()) ? 0.0f : capped(m) * kLog2e;
     static_for<U>([&](auto u) {
       if (ok[u]) {
         float wv[E];
         if constexpr (WEIGHTED) G::weights(a.weight, g0 + u * NT + tid, wv);
 #pragma unroll
         for (int i = 0; i < E; ++i) {
-          s += exp_shifted(f[u][i], ML);
-          if constexpr (WEIGHTED) S = __builtin_fmaf(wv[i], f[u][i], S);
-          else S += f[u][i];
+          const float fc = capped(f[u][i]);
+          s += exp_shifted(fc, ML);
+          if constexpr (WEIGHTED) S = __builtin_fmaf(wv[i], fc, S);
+          else S += fc;
         }
       }
     });
   }
 
-  const float M = block_max<NT>(m, red_max);
-  const float ML = (M == -__builtin_inff()) ? 0.0f : M * kLog2e;
+  const float M = block_max<NT>(m, red_max);     // of the stored logits
+  const float Mc = capped(M);                    // of the logits the loss reads
+  const float ML = (M == -__builtin_inff()) ? 0.0f : Mc * kLog2e;
   RowSums rs = {0.0f, S, 0, 0x7fffffff};
   if (m == M) {
     // This lane holds the row maximum: recompute its share exactly.
@@ -128,7 +138,7 @@ __device__ inline void stream_stats(const RowArgs& a, const char* row, float& M_
 #pragma unroll
           for (int i = 0; i < E; ++i) {
             const bool eq = (f[i] == M);
-            rs.s += eq ? 0.0f : exp_shifted(f[i], ML);
+            rs.s += eq ? 0.0f : exp_shifted(capped(f[i]), ML);
             rs.cnt += eq ? 1 : 0;
             if (eq) rs.first = min(rs.first, static_cast<int>(g * E + i));
           }
@@ -136,23 +146,26 @@ __device__ inline void stream_stats(const RowArgs& a, const char* row, float& M_
       });
     }
   } else {
-    rs.s = (m == -__builtin_inff()) ? 0.0f : s * __builtin_amdgcn_exp2f((m - M) * kLog2e);
+    rs.s = (m == -__builtin_inff()) ? 0.0f
+                                    : s * __builtin_amdgcn_exp2f((capped(m) - Mc) * kLog2e);
   }
   rs = block_sums<NT>(rs, red_sum);
-  M_out = M;
+  M_out = Mc;
   dp_out = rs.s + static_cast<float>(rs.cnt - 1);
   S_out = rs.S;
   first_out = rs.first;
 }
 
 // Writes the gradient of one row segment [g_begin, g_end) of groups, with
-// the true-class element substituted by its owner.
-template <int DT, int NT, int U, bool WEIGHTED, bool VECP>
+// the true-class element substituted by its owner (t.dxy is final: under CAP
+// the caller has multiplied it by the slope at the stored x[y]).
+template <int DT, int NT, int U, bool WEIGHTED, bool VECP, bool CAP>
 __device__ inline void stream_grad(const RowArgs& a, const char* src, char* dst, int64_t g_begin,
                                    int64_t g_end, const RowTerms& t, int64_t y) {
   using G = Grp<DT, VECP>;
   constexpr int E = G::E;
   const int tid = threadIdx.x;
+  const SoftCap cap{a.cap, a.cap_k};
   const int64_t gy = y / E;
   const int iy = static_cast<int>(y % E);
   for (int64_t g0 = g_begin; g0 < g_end; g0 += static_cast<int64_t>(NT) * U) {
@@ -169,9 +182,15 @@ __device__ inline void stream_grad(const RowArgs& a, const char* src, char* dst,
 #pragma unroll
         for (int i = 0; i < E; ++i) {
           const float b = WEIGHTED ? t.B * wv[i] : t.B;
-          f[u][i] = __builtin_fmaf(exp_shifted(f[u][i], t.ML), t.K, -b);
+          if constexpr (CAP) {
+            float slope;
+            const float fc = cap.value(f[u][i], slope);
+            f[u][i] = __builtin_fmaf(exp_shifted(fc, t.ML), t.K, -b) * slope;
+          } else {
+            f[u][i] = __builtin_fmaf(exp_shifted(f[u][i], t.ML), t.K, -b);
+          }
         }
-        if (g == gy) {
+        if (g == gy) {  // the owner stores the finished true-class value
 #pragma unroll
           for (int i = 0; i < E; ++i)
             if (i == iy) f[u][i] = t.dxy;
@@ -195,7 +214,16 @@ __device__ inline float row_weight(const RowArgs& a, int64_t y, bool weighted) {
   return weighted ? a.weight[y] : 1.0f;
 }
 
-template <int DT, int NT, int U, bool WEIGHTED, bool VECP>
+// Slope of the soft-cap at the stored true-class logit (1 without CAP).
+template <bool CAP>
+__device__ inline float cap_slope(const RowArgs& a, float x) {
+  if constexpr (!CAP) return 1.0f;
+  float slope;
+  SoftCap{a.cap, a.cap_k}.value(x, slope);
+  return slope;
+}
+
+template <int DT, int NT, int U, bool WEIGHTED, bool VECP, bool CAP>
 __global__ __launch_bounds__(NT) void stats_kernel(const RowArgs a) {
   using D = Dt<DT>;
   __shared__ float red_max[NT / kWave];
@@ -206,25 +234,30 @@ __global__ __launch_bounds__(NT) void stats_kernel(const RowArgs a) {
   const int cls = row_class(y, a.V, a.ignore_index);
   if (cls != kValid) {
     if (threadIdx.x == 0) {
-      store_row(a, n, (cls == kIgnored) ? 0.0f : __builtin_nanf(""), 0.0f);
+      const float l = (cls == kIgnored) ? 0.0f : __builtin_nanf("");
+      store_row(a, n, l, 0.0f, l);
       if (a.stats) reinterpret_cast<float4*>(a.stats)[n] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     return;
   }
   float M, dp, S;
   int first;
-  stream_stats<DT, NT, U, WEIGHTED, VECP>(a, row, M, dp, S, first, red_max, red_sum);
+  stream_stats<DT, NT, U, WEIGHTED, VECP, CAP>(a, row, M, dp, S, first, red_max, red_sum);
   if (threadIdx.x == 0) {
-    const float xy = D::load1(row, y);
+    const float xs = D::load1(row, y);
+    const float xy = CAP ? SoftCap{a.cap, a.cap_k}.value(xs) : xs;
     const float sum_w = static_cast<float>(a.ws->sum_w);
-    store_row(a, n, row_loss(M, dp, xy, S, row_weight(a, y, WEIGHTED), sum_w, a.eps, a.eta),
-              (static_cast<int64_t>(first) == y) ? 1.0f : 0.0f);
+    const float lg = log1pf(dp);
+    const float zrow = row_z(M, lg, a.zl);
+    store_row(a, n,
+              row_loss(M, lg, xy, S, row_weight(a, y, WEIGHTED), sum_w, a.eps, a.eta) + zrow,
+              (static_cast<int64_t>(first) == y) ? 1.0f : 0.0f, zrow);
     if (a.stats)
       reinterpret_cast<float4*>(a.stats)[n] = make_float4(M, dp, xy, a.eps > 0.0f ? S : 0.0f);
   }
 }
 
-template <int DT, int NT, int U, bool WEIGHTED, bool VECP>
+template <int DT, int NT, int U, bool WEIGHTED, bool VECP, bool CAP>
 __global__ __launch_bounds__(NT) void fused_stream_kernel(const RowArgs a) {
   using D = Dt<DT>;
   __shared__ float red_max[NT / kWave];
@@ -235,29 +268,35 @@ __global__ __launch_bounds__(NT) void fused_stream_kernel(const RowArgs a) {
   const int cls = row_class(y, a.V, a.ignore_index);
   if (cls != kValid) {
     stream_zero<DT, VECP>(row, 0, a.nvec, NT, U);
-    if (threadIdx.x == 0) store_row(a, n, (cls == kIgnored) ? 0.0f : __builtin_nanf(""), 0.0f);
+    const float l = (cls == kIgnored) ? 0.0f : __builtin_nanf("");
+    if (threadIdx.x == 0) store_row(a, n, l, 0.0f, l);
     return;
   }
   float M, dp, S;
   int first;
-  stream_stats<DT, NT, U, WEIGHTED, VECP>(a, row, M, dp, S, first, red_max, red_sum);
-  const float xy = D::load1(row, y);
+  stream_stats<DT, NT, U, WEIGHTED, VECP, CAP>(a, row, M, dp, S, first, red_max, red_sum);
+  const float xs = D::load1(row, y);
+  const float xy = CAP ? SoftCap{a.cap, a.cap_k}.value(xs) : xs;
   const float sum_w = static_cast<float>(a.ws->sum_w);
   const float wy = row_weight(a, y, WEIGHTED);
-  if (threadIdx.x == 0)
-    store_row(a, n, row_loss(M, dp, xy, S, wy, sum_w, a.eps, a.eta),
-              (static_cast<int64_t>(first) == y) ? 1.0f : 0.0f);
+  const float lg = log1pf(dp);
+  if (threadIdx.x == 0) {
+    const float zrow = row_z(M, lg, a.zl);
+    store_row(a, n, row_loss(M, lg, xy, S, wy, sum_w, a.eps, a.eta) + zrow,
+              (static_cast<int64_t>(first) == y) ? 1.0f : 0.0f, zrow);
+  }
   // Every thread has read x[y] before any thread overwrites it: the block
   // reduction inside stream_stats ended with a barrier, and x[y] is re-read
   // here, so order the read before the first store of the gradient pass.
   __syncthreads();
-  const float sigma = a.mean ? static_cast<float>(1.0 / a.ws->W) : 1.0f;
-  const RowTerms t = row_terms(M, dp, xy, wy, sum_w, a.eps, a.eta, sigma);
-  stream_grad<DT, NT, U, WEIGHTED, VECP>(a, row, row, 0, a.nvec, t, y);
+  const float sigma = a.mean ? a.ws->inv_W : 1.0f;
+  RowTerms t = row_terms(M, dp, lg, xy, wy, sum_w, a.eps, a.eta, sigma, a.zl, z_sigma(a));
+  t.dxy *= cap_slope<CAP>(a, xs);
+  stream_grad<DT, NT, U, WEIGHTED, VECP, CAP>(a, row, row, 0, a.nvec, t, y);
 }
 
 // Split backward over (row, column chunk) workgroups.
-template <int DT, int NT, int U, bool WEIGHTED, bool VECP>
+template <int DT, int NT, int U, bool WEIGHTED, bool VECP, bool CAP>
 __global__ __launch_bounds__(NT) void backward_kernel(const RowArgs a) {
   using D = Dt<DT>;
   const int64_t b = xcd_contiguous(blockIdx.x, a.rows * a.chunks);
@@ -276,11 +315,18 @@ __global__ __launch_bounds__(NT) void backward_kernel(const RowArgs a) {
   }
   const float4 st = reinterpret_cast<const float4*>(a.stats)[n];
   const float go = a.go[n * a.go_stride];
-  const float sigma = (a.mean ? static_cast<float>(1.0 / a.ws->W) : 1.0f) * go;
+  const float sigma = (a.mean ? a.ws->inv_W : 1.0f) * go;
   const float sum_w = static_cast<float>(a.ws->sum_w);
-  const RowTerms t =
-      row_terms(st.x, st.y, st.z, row_weight(a, y, WEIGHTED), sum_w, a.eps, a.eta, sigma);
-  stream_grad<DT, NT, U, WEIGHTED, VECP>(a, src, dst, g_begin, g_end, t, y);
+  RowTerms t = row_terms(st.x, st.y, log1pf(st.y), st.z, row_weight(a, y, WEIGHTED), sum_w,
+                         a.eps, a.eta, sigma, a.zl, z_sigma(a) * go);
+  // The saved x[y] is capped; the slope needs the stored one.  Only the
+  // chunk that holds column y reads it (src is not yet overwritten: each
+  // workgroup writes its own chunk only, after this read).
+  if constexpr (CAP) {
+    const int64_t per_elems = static_cast<int64_t>(NT) * U * Grp<DT, VECP>::E;
+    if (y / per_elems == c) t.dxy *= cap_slope<CAP>(a, D::load1(src, y));
+  }
+  stream_grad<DT, NT, U, WEIGHTED, VECP, CAP>(a, src, dst, g_begin, g_end, t, y);
 }
 
 // Grid-stride over (row, column chunk) work items, so that a grad_output of
@@ -336,39 +382,43 @@ int launch(K kernel, int64_t grid, int nt, const RowArgs& a, hipStream_t s) {
 
 enum Which { kStats, kFusedStream, kBackward, kScale };
 
-template <int DT, bool W, bool VECP>
+template <int DT, bool W, bool VECP, bool CAP>
 int launch_which(Which which, const Prob& p, RowArgs a, hipStream_t s) {
   constexpr int NT = kStreamNT, U = kStreamU;
   a.nvec = groups<DT>(p);
   const int64_t per = static_cast<int64_t>(NT) * U;
   a.chunks = (a.nvec + per - 1) / per;
   switch (which) {
-    case kStats: return launch(stats_kernel<DT, NT, U, W, VECP>, p.rows, NT, a, s);
-    case kFusedStream: return launch(fused_stream_kernel<DT, NT, U, W, VECP>, p.rows, NT, a, s);
+    case kStats: return launch(stats_kernel<DT, NT, U, W, VECP, CAP>, p.rows, NT, a, s);
+    case kFusedStream:
+      return launch(fused_stream_kernel<DT, NT, U, W, VECP, CAP>, p.rows, NT, a, s);
     case kBackward:
-      return launch(backward_kernel<DT, NT, U, W, VECP>, p.rows * a.chunks, NT, a, s);
+      return launch(backward_kernel<DT, NT, U, W, VECP, CAP>, p.rows * a.chunks, NT, a, s);
     case kScale:
-      return launch(scale_kernel<DT, NT, U, VECP>, min(p.rows * a.chunks, kScaleGrid), NT, a, s);
+      if constexpr (CAP) return VSCE_ERR_INVALID;  // the scale does not depend on the cap
+      else
+        return launch(scale_kernel<DT, NT, U, VECP>, min(p.rows * a.chunks, kScaleGrid), NT, a,
+                      s);
   }
   return VSCE_ERR_INVALID;
 }
 
-template <int DT>
+template <int DT, bool CAP>
 int dispatch(Which which, const Prob& p, const RowArgs& a, hipStream_t s) {
   const bool w = p.weight != nullptr && which != kScale;
   if (p.vec_ok) {
-    return w ? launch_which<DT, true, true>(which, p, a, s)
-             : launch_which<DT, false, true>(which, p, a, s);
+    return w ? launch_which<DT, true, true, CAP>(which, p, a, s)
+             : launch_which<DT, false, true, CAP>(which, p, a, s);
   }
-  return w ? launch_which<DT, true, false>(which, p, a, s)
-           : launch_which<DT, false, false>(which, p, a, s);
+  return w ? launch_which<DT, true, false, CAP>(which, p, a, s)
+           : launch_which<DT, false, false, CAP>(which, p, a, s);
 }
 
 }  // namespace
 
-template <int DT>
+template <int DT, bool CAP>
 int stream_dt(int which, const Prob& p, const RowArgs& a, hipStream_t s) {
-  return dispatch<DT>(static_cast<Which>(which), p, a, s);
+  return dispatch<DT, CAP>(static_cast<Which>(which), p, a, s);
 }
 
 }  // namespace vsce

@@ -13,6 +13,11 @@ Two modes (the pages' two designs):
   statistics (m, d', x_y, S) and leaves the logits intact; the backward
   recomputes the gradient in fp32 from them and writes it in the input type.
 
+Both modes take the logit soft-cap ``softcap`` (x -> s tanh(x / s) before the
+loss reads the logits) and the z-loss weight ``z_loss`` (lambda lse^2 per
+valid row), the two CE features Liger-Kernel PR #1268 lists beside class
+weights and label smoothing.
+
 Nothing here synchronizes with the host: the normalizers and the loss
 reduction stay on the device.
 """
@@ -43,7 +48,8 @@ def _rows_view(logits: torch.Tensor) -> torch.Tensor:
 
 
 def make_problem(x2d: torch.Tensor, target: torch.Tensor, weight: Optional[torch.Tensor],
-                 ignore_index: int, label_smoothing: float, reduction: str) -> L.Problem:
+                 ignore_index: int, label_smoothing: float, reduction: str,
+                 softcap: float = 0.0, z_loss: float = 0.0) -> L.Problem:
     if x2d.dtype not in _DTYPES:
         raise TypeError(f"unsupported logits dtype {x2d.dtype}")
     if target.dtype != torch.int64 or target.device != x2d.device:
@@ -63,6 +69,8 @@ def make_problem(x2d: torch.Tensor, target: torch.Tensor, weight: Optional[torch
     p.class_weight = None if weight is None else weight.data_ptr()
     p.ignore_index = int(ignore_index)
     p.label_smoothing = float(label_smoothing)
+    p.softcap = float(softcap)
+    p.z_loss = float(z_loss)
     p.reserved = 0
     return p
 
@@ -71,22 +79,27 @@ def workspace_for(rows: int, device) -> torch.Tensor:
     return torch.empty(L.vsce_workspace_bytes(rows), dtype=torch.uint8, device=device)
 
 
-def _outputs(rows: int, reduction: str, device, row_loss: bool, accuracy: bool):
+def _outputs(rows: int, reduction: str, device, row_loss: bool, accuracy: bool,
+             z_loss: bool = False):
     f32 = dict(dtype=torch.float32, device=device)
-    loss = torch.empty(max(rows, 1) if reduction == "none" else 1, **f32)
-    rl = torch.empty(max(rows, 1), **f32) if row_loss else None
-    acc = torch.empty(max(rows, 1), **f32) if accuracy else None
+    per_row = max(rows, 1)
+    loss = torch.empty(per_row if reduction == "none" else 1, **f32)
+    rl = torch.empty(per_row, **f32) if row_loss else None
+    acc = torch.empty(per_row, **f32) if accuracy else None
     accm = torch.empty(1, **f32) if accuracy else None
+    zl = torch.empty(per_row if reduction == "none" else 1, **f32) if z_loss else None
     o = L.Outputs()
     o.loss = loss.data_ptr()
     o.row_loss = None if rl is None else rl.data_ptr()
     o.token_acc = None if acc is None else acc.data_ptr()
     o.acc_mean = None if accm is None else accm.data_ptr()
+    o.z_loss = None if zl is None else zl.data_ptr()
     res = {
         "loss": loss[:rows] if reduction == "none" else loss[0],
         "row_loss": None if rl is None else rl[:rows],
         "token_acc": None if acc is None else acc[:rows],
         "acc_mean": None if accm is None else accm[0],
+        "z_loss": None if zl is None else (zl[:rows] if reduction == "none" else zl[0]),
     }
     return o, res
 
@@ -95,13 +108,15 @@ def forward_fused_inplace(logits: torch.Tensor, target: torch.Tensor,
                           weight: Optional[torch.Tensor] = None, ignore_index: int = -100,
                           label_smoothing: float = 0.0, reduction: str = "mean",
                           row_loss: bool = False, accuracy: bool = False,
-                          workspace: Optional[torch.Tensor] = None) -> dict:
+                          workspace: Optional[torch.Tensor] = None, softcap: float = 0.0,
+                          z_loss: float = 0.0, return_z_loss: bool = False) -> dict:
     """ce_forward_fused_inplace: loss outputs; the logits buffer now holds the
     gradient of the reduced loss for grad_output = 1."""
     x = _rows_view(logits)
-    p = make_problem(x, target.reshape(-1), weight, ignore_index, label_smoothing, reduction)
+    p = make_problem(x, target.reshape(-1), weight, ignore_index, label_smoothing, reduction,
+                     softcap, z_loss)
     ws = workspace if workspace is not None else workspace_for(p.rows, x.device)
-    o, res = _outputs(p.rows, reduction, x.device, row_loss, accuracy)
+    o, res = _outputs(p.rows, reduction, x.device, row_loss, accuracy, return_z_loss)
     L.ce_forward_fused_inplace(p, x.data_ptr(), o, ws.data_ptr(), _stream(x))
     res["workspace"] = ws
     return res
@@ -111,13 +126,15 @@ def forward_stats(logits: torch.Tensor, target: torch.Tensor,
                   weight: Optional[torch.Tensor] = None, ignore_index: int = -100,
                   label_smoothing: float = 0.0, reduction: str = "mean",
                   row_loss: bool = False, accuracy: bool = False,
-                  workspace: Optional[torch.Tensor] = None) -> dict:
+                  workspace: Optional[torch.Tensor] = None, softcap: float = 0.0,
+                  z_loss: float = 0.0, return_z_loss: bool = False) -> dict:
     """ce_forward_stats: loss outputs plus the [rows, 4] statistics."""
     x = _rows_view(logits)
-    p = make_problem(x, target.reshape(-1), weight, ignore_index, label_smoothing, reduction)
+    p = make_problem(x, target.reshape(-1), weight, ignore_index, label_smoothing, reduction,
+                     softcap, z_loss)
     ws = workspace if workspace is not None else workspace_for(p.rows, x.device)
     stats = torch.empty((max(p.rows, 1), L.STATS_STRIDE), dtype=torch.float32, device=x.device)
-    o, res = _outputs(p.rows, reduction, x.device, row_loss, accuracy)
+    o, res = _outputs(p.rows, reduction, x.device, row_loss, accuracy, return_z_loss)
     L.ce_forward_stats(p, x.data_ptr(), stats.data_ptr(), o, ws.data_ptr(), _stream(x))
     res["stats"] = stats[:p.rows]
     res["workspace"] = ws
@@ -140,11 +157,13 @@ def backward_from_stats(logits: torch.Tensor, target: torch.Tensor, stats: torch
                         grad_output: torch.Tensor, workspace: torch.Tensor,
                         weight: Optional[torch.Tensor] = None, ignore_index: int = -100,
                         label_smoothing: float = 0.0, reduction: str = "mean",
-                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                        out: Optional[torch.Tensor] = None, softcap: float = 0.0,
+                        z_loss: float = 0.0) -> torch.Tensor:
     """ce_backward_from_stats: the gradient in the logits' type (``out`` may be
     the logits themselves for an in-place backward)."""
     x = _rows_view(logits)
-    p = make_problem(x, target.reshape(-1), weight, ignore_index, label_smoothing, reduction)
+    p = make_problem(x, target.reshape(-1), weight, ignore_index, label_smoothing, reduction,
+                     softcap, z_loss)
     g = (torch.empty_strided(x.size(), x.stride(), dtype=x.dtype, device=x.device)
          if out is None else _rows_view(out))
     if g.shape != x.shape or g.dtype != x.dtype or g.stride() != x.stride():
@@ -166,23 +185,35 @@ def scale_grad(grad: torch.Tensor, grad_output: torch.Tensor, reduction: str = "
     return grad
 
 
+def _returns(res: dict, ctx, return_z_loss: bool, accuracy: bool):
+    out = [res["loss"]]
+    extra = []
+    if return_z_loss:
+        extra.append(res["z_loss"])
+    if accuracy:
+        extra += [res["token_acc"], res["acc_mean"]]
+    if extra:
+        ctx.mark_non_differentiable(*extra)
+        return tuple(out + extra)
+    return res["loss"]
+
+
 class FusedCrossEntropy(torch.autograd.Function):
     """Fused mode: gradient computed in the forward, over the logits buffer."""
 
     @staticmethod
-    def forward(ctx, logits, target, weight, ignore_index, label_smoothing, reduction, accuracy):
+    def forward(ctx, logits, target, weight, ignore_index, label_smoothing, reduction, accuracy,
+                softcap, z_loss, return_z_loss):
         res = forward_fused_inplace(logits, target, weight, ignore_index, label_smoothing,
-                                    reduction, accuracy=accuracy)
+                                    reduction, accuracy=accuracy, softcap=softcap, z_loss=z_loss,
+                                    return_z_loss=return_z_loss)
         # The buffer now holds the gradient; it is written through raw pointers,
         # so autograd's version counter is untouched.
         ctx.save_for_backward(logits.detach())
         ctx.reduction = reduction
         ctx.grad_scaled_in_place = False
         ctx.workspace = res["workspace"]
-        if accuracy:
-            ctx.mark_non_differentiable(res["token_acc"], res["acc_mean"])
-            return res["loss"], res["token_acc"], res["acc_mean"]
-        return res["loss"]
+        return _returns(res, ctx, return_z_loss, accuracy)
 
     @staticmethod
     def backward(ctx, grad_loss, *unused):
@@ -192,7 +223,7 @@ class FusedCrossEntropy(torch.autograd.Function):
         ctx.grad_scaled_in_place = True
         (grad,) = ctx.saved_tensors
         scale_grad(grad, grad_loss, ctx.reduction, skip_if_one=True)
-        return grad, None, None, None, None, None, None
+        return (grad,) + (None,) * 9
 
 
 class SplitCrossEntropy(torch.autograd.Function):
@@ -200,46 +231,52 @@ class SplitCrossEntropy(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, logits, target, weight, ignore_index, label_smoothing, reduction, accuracy,
-                inplace_backward):
+                inplace_backward, softcap, z_loss, return_z_loss):
         res = forward_stats(logits, target, weight, ignore_index, label_smoothing, reduction,
-                            accuracy=accuracy)
+                            accuracy=accuracy, softcap=softcap, z_loss=z_loss,
+                            return_z_loss=return_z_loss)
         ctx.save_for_backward(logits, target, res["stats"], res["workspace"],
                               *([] if weight is None else [weight]))
-        ctx.args = (ignore_index, label_smoothing, reduction, weight is not None, inplace_backward)
-        if accuracy:
-            ctx.mark_non_differentiable(res["token_acc"], res["acc_mean"])
-            return res["loss"], res["token_acc"], res["acc_mean"]
-        return res["loss"]
+        ctx.args = (ignore_index, label_smoothing, reduction, weight is not None, inplace_backward,
+                    softcap, z_loss)
+        return _returns(res, ctx, return_z_loss, accuracy)
 
     @staticmethod
     def backward(ctx, grad_loss, *unused):
         logits, target, stats, ws, *w = ctx.saved_tensors
-        ignore_index, ls, reduction, weighted, inplace = ctx.args
+        ignore_index, ls, reduction, weighted, inplace, softcap, z_loss = ctx.args
         g = backward_from_stats(logits, target, stats, grad_loss, ws, w[0] if weighted else None,
                                 ignore_index, ls, reduction,
-                                out=logits.detach() if inplace else None)
-        return g, None, None, None, None, None, None, None
+                                out=logits.detach() if inplace else None, softcap=softcap,
+                                z_loss=z_loss)
+        return (g,) + (None,) * 10
 
 
 def cross_entropy(logits: torch.Tensor, target: torch.Tensor, weight: Optional[torch.Tensor] = None,
                   ignore_index: int = -100, label_smoothing: float = 0.0,
                   reduction: str = "mean", *, mode: str = "fused", return_accuracy: bool = False,
-                  inplace_backward: bool = False):
+                  inplace_backward: bool = False, softcap: float = 0.0, z_loss: float = 0.0,
+                  return_z_loss: bool = False):
     """Softmax cross-entropy over the last dimension of ``logits``.
 
     ``mode="fused"`` overwrites ``logits`` with the gradient during the
     forward; ``mode="split"`` keeps them (and with ``inplace_backward`` writes
-    the gradient over them in the backward).  With ``return_accuracy`` also
-    returns the per-token accuracy and its mean over non-ignored rows.
+    the gradient over them in the backward).  ``softcap`` > 0 caps the logits
+    at s tanh(x / s) first; ``z_loss`` > 0 adds lambda lse^2 per valid row
+    (averaged over the valid rows under "mean").  Returns the loss, then the
+    z-loss part when ``return_z_loss``, then the per-token accuracy and its
+    mean over non-ignored rows when ``return_accuracy``; the extra outputs are
+    not differentiable.
     """
     if reduction not in L.REDUCTIONS:
         raise ValueError(f"reduction must be one of {tuple(L.REDUCTIONS)}")
     if mode == "fused":
         return FusedCrossEntropy.apply(logits, target, weight, ignore_index, label_smoothing,
-                                       reduction, return_accuracy)
+                                       reduction, return_accuracy, softcap, z_loss, return_z_loss)
     if mode == "split":
         return SplitCrossEntropy.apply(logits, target, weight, ignore_index, label_smoothing,
-                                       reduction, return_accuracy, inplace_backward)
+                                       reduction, return_accuracy, inplace_backward, softcap,
+                                       z_loss, return_z_loss)
     raise ValueError("mode must be 'fused' or 'split'")
 
 
@@ -252,4 +289,6 @@ def status(workspace: torch.Tensor) -> dict:
         "n_valid": int(h[L.WS_N_VALID:L.WS_N_VALID + 8].view(torch.int64)[0]),
         "n_invalid": int(h[L.WS_N_INVALID:L.WS_N_INVALID + 8].view(torch.int64)[0]),
         "status": int(h[L.WS_STATUS:L.WS_STATUS + 4].view(torch.int32)[0]),
+        "inv_W": float(h[L.WS_INV_W:L.WS_INV_W + 4].view(torch.float32)[0]),
+        "inv_n_valid": float(h[L.WS_INV_N_VALID:L.WS_INV_N_VALID + 4].view(torch.float32)[0]),
     }
