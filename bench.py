@@ -180,31 +180,40 @@ def main():
     stream = torch.cuda.current_stream(dev).cuda_stream
     dt = {"f32": L.F32, "bf16": L.BF16, "f16": L.F16}[wl.dtype]
 
-    def problem(buf):
+    def problem(buf, softcap=0.0, z_loss=0.0):
         p = L.Problem()
         p.rows, p.vocab, p.row_stride = wl.BT, wl.V, wl.V
         p.dtype, p.reduction = dt, L.REDUCTIONS[red]
         p.target = t.data_ptr()
         p.class_weight = None if wt is None else wt.data_ptr()
         p.ignore_index, p.label_smoothing, p.reserved = -100, wl.label_smoothing, 0
+        p.softcap, p.z_loss = softcap, z_loss
         return p
 
     problems = [problem(b) for b in ring]
+    # the context mode with both optional features: a Gemma-style cap and a
+    # PaLM-style z-loss weight
+    CAP, ZL = 30.0, 1e-4
+    problems_cap = [problem(b, CAP, ZL) for b in ring]
     outs = L.Outputs()
     outs.loss = loss.data_ptr()
     hip = Hip()
     ev = [(hip.event(), hip.event()) for _ in range(K)]
 
-    def fused_step(i, go, timed_events=None):
-        b = ring[i % ring_n]
-        if timed_events is None:
-            L.ce_forward_fused_inplace(problems[i % ring_n], b.data_ptr(), outs, ws.data_ptr(),
-                                       stream)
-        else:
-            L.ce_forward_fused_inplace_timed(problems[i % ring_n], b.data_ptr(), outs,
-                                             ws.data_ptr(), stream, *timed_events)
-        L.ce_scale_grad(b.data_ptr(), wl.BT, wl.V, wl.V, dt, go.data_ptr(),
-                        1 if go.numel() > 1 else 0, 1, stream)
+    def fused_steps(probs):
+        def fused_step(i, go, timed_events=None):
+            b = ring[i % ring_n]
+            if timed_events is None:
+                L.ce_forward_fused_inplace(probs[i % ring_n], b.data_ptr(), outs, ws.data_ptr(),
+                                           stream)
+            else:
+                L.ce_forward_fused_inplace_timed(probs[i % ring_n], b.data_ptr(), outs,
+                                                 ws.data_ptr(), stream, *timed_events)
+            L.ce_scale_grad(b.data_ptr(), wl.BT, wl.V, wl.V, dt, go.data_ptr(),
+                            1 if go.numel() > 1 else 0, 1, stream)
+        return fused_step
+
+    fused_step = fused_steps(problems)
 
     def split_step(i, go):
         b = ring[i % ring_n]
@@ -214,21 +223,21 @@ def main():
                                  stats.data_ptr(), go.data_ptr(), 1 if go.numel() > 1 else 0,
                                  ws.data_ptr(), stream)
 
-    def timed(step_fn, go, events=False):
+    def timed(step_fn, go, events=None):
         refill()
         for i in range(Wu):
             step_fn(i, go)
         torch.cuda.synchronize()
         t_begin = time.perf_counter()
         for i in range(K):
-            if events:
-                step_fn(Wu + i, go, ev[i])
+            if events is not None:
+                step_fn(Wu + i, go, events[i])
             else:
                 step_fn(Wu + i, go)
         torch.cuda.synchronize()
         return time.perf_counter() - t_begin
 
-    wall = timed(fused_step, go_one, events=True)
+    wall = timed(fused_step, go_one, events=ev)
     kernel_ms = [hip.elapsed_ms(a, b) for a, b in ev]
     mean_kernel_s = float(np.mean(kernel_ms)) / 1e3
 
@@ -255,6 +264,21 @@ def main():
                               "alg_GBps": round((3 * n_valid * row_bytes
                                                  + (wl.BT - n_valid) * row_bytes) * K
                                                 / wsp / 1e9, 1)}
+        # soft-capped logits and a z-loss: same bytes, more arithmetic per
+        # element (the cap and its slope: one exp and one reciprocal each in
+        # the sum and gradient passes)
+        for a, b in ev:
+            hip.destroy(a)
+            hip.destroy(b)
+        ev[:] = [(hip.event(), hip.event()) for _ in range(K)]
+        wcap = timed(fused_steps(problems_cap), go_one, events=ev)
+        cap_kernel_s = float(np.mean([hip.elapsed_ms(a, b) for a, b in ev])) / 1e3
+        extra[f"fused_softcap{CAP:g}_zloss{ZL:g}"] = {
+            "ms_per_step": round(wcap / K * 1e3, 4),
+            "rows_per_s": round(wl.BT * K / wcap, 1),
+            "kernel_ms": round(cap_kernel_s * 1e3, 4),
+            "kernel_GBps": round(kernel_bytes / cap_kernel_s / 1e9, 1),
+            "kernel_frac_of_hbm_peak": round(kernel_bytes / cap_kernel_s / 1e9 / HBM_PEAK_GBPS, 4)}
 
     # Practical ceiling: the runtime's own device-to-device copy of one
     # logits buffer (reads and writes the same bytes as the row kernel's
