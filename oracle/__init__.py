@@ -73,6 +73,10 @@ def _load():
         d = ctypes.c_double
         lib.oracle_rows.argtypes = [i64, i64, p, p, p, i64, d, d, d, p, p, p, p, p, p, p, p]
         lib.oracle_rows.restype = None
+        lib.oracle_partials.argtypes = [i64, i64, i64, i64, p, p, p, i64, d, d, p]
+        lib.oracle_partials.restype = None
+        lib.oracle_merge.argtypes = [i64, i64, p, p, i64, i64, p, p]
+        lib.oracle_merge.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -162,6 +166,33 @@ def rows(x: np.ndarray, target: np.ndarray, weight: Optional[np.ndarray] = None,
                         float(label_smoothing), float(softcap), float(z_loss), _ptr(sc), _ptr(sz),
                         _ptr(loss), _ptr(z), _ptr(stats), _ptr(am), _ptr(cls), _ptr(grad))
     return Rows(loss, z, stats, am, cls, grad)
+
+
+def partials(x_shard: np.ndarray, target: np.ndarray, v0: int, V: int,
+             weight: Optional[np.ndarray] = None, ignore_index: int = -100,
+             label_smoothing: float = 0.0, softcap: float = 0.0) -> np.ndarray:
+    """One vocabulary shard's per-row record [n, 6]: (m_s, d'_s, x_y or 0,
+    S_s, max of the stored logits, its first global column); see
+    vsce_oracle.c."""
+    x = np.ascontiguousarray(x_shard, dtype=np.float64)
+    n, Vs = x.shape
+    t = np.ascontiguousarray(target, dtype=np.int64).reshape(n)
+    w = None if weight is None else np.ascontiguousarray(weight, dtype=np.float64).reshape(V)
+    out = np.empty((n, 6), np.float64)
+    _load().oracle_partials(n, Vs, v0, V, _ptr(x), _ptr(t), _ptr(w), ignore_index,
+                            float(label_smoothing), float(softcap), _ptr(out))
+    return out
+
+
+def merge(parts: np.ndarray, target: np.ndarray, V: int, ignore_index: int = -100):
+    """Shard records [P, n, 6] (column order) -> (stats [n, 4], argmax [n])."""
+    pa = np.ascontiguousarray(parts, dtype=np.float64)
+    P, n, _ = pa.shape
+    t = np.ascontiguousarray(target, dtype=np.int64).reshape(n)
+    stats = np.empty((n, 4), np.float64)
+    am = np.empty(n, np.int64)
+    _load().oracle_merge(n, P, _ptr(pa), _ptr(t), V, ignore_index, _ptr(stats), _ptr(am))
+    return stats, am
 
 
 def reduce_loss(row_loss: np.ndarray, cls: np.ndarray, W: float, reduction: str,

@@ -306,3 +306,109 @@ void oracle_rows(int64_t nrows, int64_t V, const double *x,
     free(xt);
   }
 }
+
+/*
+ * Vocab-parallel statistics ([TE2325] Greptile summary: with a process group
+ * of world_size > 1 each rank holds a slice of the vocabulary, and the per-row
+ * m_d_X_y record -- max, sum, target logit and, under label smoothing,
+ * scaled_x_sum as a 4th value -- is gathered from every rank; its review
+ * comment asks that the 4th value be gathered and summed too).
+ *
+ * oracle_partials: the record of one shard holding columns [v0, v0 + Vs) of a
+ * V-column vocabulary (x is the shard's [nrows, Vs] slice; targets and the
+ * class weights are global, weight has V entries or is NULL).  Per valid row,
+ * with xt the (soft-capped) logits of the shard:
+ *   [0] m_s   = max over the shard of xt;  cs = the first column attaining it
+ *   [1] d'_s  = sum over the shard's other columns of exp(xt[c] - m_s)
+ *   [2] xt[y] if the shard holds column y, else 0
+ *   [3] S_s   = sum over the shard of w[c] xt[c] (0 when eps == 0)
+ *   [4] the maximum of the stored logits x over the shard
+ *   [5] the global column of its first occurrence
+ * Rows that are not valid get zeros.
+ */
+void oracle_partials(int64_t nrows, int64_t Vs, int64_t v0, int64_t V, const double *x,
+                     const int64_t *target, const double *weight, int64_t ignore_index,
+                     double label_smoothing, double softcap, double *part /* [nrows][6] */) {
+  int64_t n;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (n = 0; n < nrows; ++n) {
+    const double *xr = x + n * Vs;
+    double *pr = part + 6 * n;
+    const int64_t y = target[n];
+    for (int k = 0; k < 6; ++k) pr[k] = 0.0;
+    if (row_class(y, V, ignore_index) != ORACLE_VALID) continue;
+    double m = -INFINITY, mx = -INFINITY;
+    int64_t cs = 0, am = 0;
+    for (int64_t c = 0; c < Vs; ++c) {
+      const double xt = (softcap > 0.0) ? softcap * tanh(xr[c] / softcap) : xr[c];
+      if (xt > m) {
+        m = xt;
+        cs = c;
+      }
+      if (xr[c] > mx) {
+        mx = xr[c];
+        am = c;
+      }
+    }
+    double dp = 0.0, S = 0.0;
+    for (int64_t c = 0; c < Vs; ++c) {
+      const double xt = (softcap > 0.0) ? softcap * tanh(xr[c] / softcap) : xr[c];
+      if (c != cs) dp += exp(xt - m);
+      S += (weight ? weight[v0 + c] : 1.0) * xt;
+    }
+    pr[0] = m;
+    pr[1] = dp;
+    if (y >= v0 && y < v0 + Vs)
+      pr[2] = (softcap > 0.0) ? softcap * tanh(xr[y - v0] / softcap) : xr[y - v0];
+    pr[3] = (label_smoothing > 0.0) ? S : 0.0;
+    pr[4] = mx;
+    pr[5] = (double)(v0 + am);
+  }
+}
+
+/*
+ * oracle_merge: the records of P shards (part[s] = [nrows][6], shards in
+ * increasing column order) into the full row's statistics and argmax:
+ *   m  = max_s m_s;  s* = the first shard attaining it
+ *   d' = d'_{s*} + sum over s != s* of (1 + d'_s) exp(m_s - m)
+ *   x[y] = sum_s of the shards' [2] (only the owner's is not 0)
+ *   S  = sum_s S_s
+ *   argmax = [5] of the first shard whose [4] attains the maximum of [4]
+ * (the first column of the global maximum, as the unsharded row has it).
+ * Rows that are not valid keep zeros.
+ */
+void oracle_merge(int64_t nrows, int64_t P, const double *part /* [P][nrows][6] */,
+                  const int64_t *target, int64_t V, int64_t ignore_index,
+                  double *stats /* [nrows][4] */, int64_t *argmax) {
+  for (int64_t n = 0; n < nrows; ++n) {
+    double *st = stats + 4 * n;
+    for (int k = 0; k < 4; ++k) st[k] = 0.0;
+    argmax[n] = 0;
+    if (row_class(target[n], V, ignore_index) != ORACLE_VALID) continue;
+    double m = -INFINITY, mx = -INFINITY;
+    int64_t sstar = 0, sarg = 0;
+    for (int64_t s = 0; s < P; ++s) {
+      const double *pr = part + (s * nrows + n) * 6;
+      if (pr[0] > m) {
+        m = pr[0];
+        sstar = s;
+      }
+      if (pr[4] > mx) {
+        mx = pr[4];
+        sarg = s;
+      }
+    }
+    double dp = part[(sstar * nrows + n) * 6 + 1], xy = 0.0, S = 0.0;
+    for (int64_t s = 0; s < P; ++s) {
+      const double *pr = part + (s * nrows + n) * 6;
+      if (s != sstar) dp += (1.0 + pr[1]) * exp(pr[0] - m);
+      xy += pr[2];
+      S += pr[3];
+    }
+    st[0] = m;
+    st[1] = dp;
+    st[2] = xy;
+    st[3] = S;
+    argmax[n] = (int64_t)part[(sarg * nrows + n) * 6 + 5];
+  }
+}

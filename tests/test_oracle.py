@@ -497,3 +497,69 @@ def test_accuracy_uses_the_stored_logits_when_the_cap_saturates():
     assert np.all(np.isfinite(r.grad))
     # the softcap factor 1/cosh^2 is below 1e-42 at 50 and 60
     assert abs(r.grad[0, 0]) < 1e-40 and abs(r.grad[0, 1]) < 1e-40
+
+
+# ---------------------------------------------------------------- vocab-parallel merge
+# TransformerEngine PR #2325: with a process group each rank holds a slice of
+# the vocabulary and the per-row (max, sum, target logit, scaled_x_sum) record
+# is gathered; its review comment asks that the 4th value be gathered and
+# summed too.  The merge of the shards' records must give the unsharded row's
+# statistics.
+
+def _shard_edges(V, P, seed):
+    if P == 1:
+        return [0, V]
+    rng = np.random.default_rng(seed)
+    cuts = np.sort(rng.choice(np.arange(1, V), size=P - 1, replace=False))
+    return [0, *cuts.tolist(), V]
+
+
+def _merged(x, t, w, eps, softcap, edges):
+    V = x.shape[1]
+    parts = np.stack([oracle.partials(x[:, a:b], t, a, V, w, -100, eps, softcap)
+                      for a, b in zip(edges[:-1], edges[1:])])
+    return oracle.merge(parts, t, V)
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 7])
+@pytest.mark.parametrize("weighted,eps,softcap", [(False, 0.0, 0.0), (True, 0.1, 0.0),
+                                                  (True, 0.1, 4.0)])
+def test_merged_shard_statistics_equal_the_unsharded_row(P, weighted, eps, softcap):
+    x, t, w = _problem(31, 20, 500, weighted=weighted, ignore_frac=0.2, sigma=3.0)
+    r = oracle.rows(x, t, w, label_smoothing=eps, softcap=softcap, want_grad=False)
+    stats, am = _merged(x, t, w, eps, softcap, _shard_edges(500, P, P))
+    valid = r.cls == 0
+    np.testing.assert_array_equal(stats[valid, 0], r.stats[valid, 0])   # the same element
+    np.testing.assert_array_equal(stats[valid, 2], r.stats[valid, 2])   # the owner's value
+    np.testing.assert_allclose(stats[valid, 1], r.stats[valid, 1], rtol=1e-13)
+    np.testing.assert_allclose(stats[valid, 3], r.stats[valid, 3], rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(am[valid], r.argmax[valid])
+    assert np.all(stats[~valid] == 0)
+
+
+def test_merge_with_the_maximum_tied_across_shards():
+    """The row maximum sits in two shards: the merge excludes one copy and
+    keeps the other (exp(0) = 1), and the argmax is the first occurrence."""
+    x, t, _ = _problem(32, 6, 40, sigma=1.0)
+    x[:, 7] = 5.0
+    x[:, 30] = 5.0
+    x[:, 31] = 5.0
+    r = oracle.rows(x, t, want_grad=False)
+    stats, am = _merged(x, t, None, 0.0, 0.0, [0, 10, 30, 40])
+    np.testing.assert_allclose(stats[:, 1], r.stats[:, 1], rtol=1e-14)
+    assert np.all(am == 7) and np.all(r.argmax == 7)
+    assert np.all(stats[:, 1] >= 2.0)  # the two other copies count as exp(0) each
+
+
+def test_dropping_the_summed_fourth_value_changes_it():
+    """Negative control for the review comment: the smoothing sum S taken from
+    one shard (not gathered and summed) differs from the row's S."""
+    x, t, w = _problem(33, 8, 300, weighted=True, sigma=2.0)
+    V = 300
+    edges = [0, 100, 200, 300]
+    parts = np.stack([oracle.partials(x[:, a:b], t, a, V, w, -100, 0.1)
+                      for a, b in zip(edges[:-1], edges[1:])])
+    r = oracle.rows(x, t, w, label_smoothing=0.1, want_grad=False)
+    stats, _ = oracle.merge(parts, t, V)
+    np.testing.assert_allclose(stats[:, 3], r.stats[:, 3], rtol=1e-12)
+    assert np.all(np.abs(parts[0, :, 3] - r.stats[:, 3]) > 1e-3)
