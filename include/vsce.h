@@ -90,6 +90,8 @@ enum {
 /* Floats per row of the saved statistics: (m, d', x[y], S); S = 0 when
    label_smoothing == 0; d' = d - 1 (the sum with the first maximum left out). */
 #define VSCE_STATS_STRIDE 4
+/* fp32 per row of a vocab-parallel shard record (ce_forward_stats_partial). */
+#define VSCE_PARTIAL_STRIDE 8
 
 /*
  * Workspace: caller-allocated device memory of vsce_workspace_bytes(rows)
@@ -138,6 +140,16 @@ size_t vsce_workspace_bytes(int64_t rows);
  *                  section).  It is not multiplied by class weights, and the
  *                  mean reduction divides it by the number of valid rows
  *                  (the cross-entropy part keeps W).  0: off.
+ *  vocab_offset    for one shard of a vocab-parallel layout (TransformerEngine
+ *                  PR #2325, dist_process_group): the global column of this
+ *  vocab_total     buffer's first column, and the full vocabulary size V
+ *                  (vocab_total = 0 means vocab, i.e. no sharding).  Targets
+ *                  are global class ids in [0, vocab_total); class_weight, if
+ *                  given, holds all vocab_total weights (one shard reads its
+ *                  slice and w[y]); eps is divided by vocab_total.  Only
+ *                  ce_forward_stats_partial and ce_backward_from_stats take a
+ *                  sharded problem; the other entry points require
+ *                  vocab_offset == 0 and vocab_total in {0, vocab}.
  */
 typedef struct vsce_problem {
   int64_t rows;
@@ -152,6 +164,8 @@ typedef struct vsce_problem {
   float softcap;
   float z_loss;
   int32_t reserved; /* must be 0 */
+  int64_t vocab_offset;
+  int64_t vocab_total;
 } vsce_problem;
 
 /*
@@ -212,6 +226,45 @@ int ce_forward_stats(const vsce_problem *problem, const void *logits,
                      hipStream_t stream);
 
 /*
+ * Vocab-parallel split forward, one shard (TransformerEngine PR #2325: each
+ * rank of the process group computes the per-row record of its vocabulary
+ * slice, to be gathered; the review asks that the 4th value be gathered and
+ * summed too).  `problem` describes the shard (vocab = its width,
+ * vocab_offset, vocab_total); `logits` is its [rows, row_stride] slice.
+ * Writes `partial`, [rows][VSCE_PARTIAL_STRIDE] fp32 (device), per valid row:
+ *   [0] m_s    the shard's maximum of the (capped) logits
+ *   [1] d'_s   sum over the shard's other columns of exp(x[c] - m_s)
+ *   [2] x[y] (capped) if the shard holds column y, else 0
+ *   [3] S_s    sum over the shard of w[c] x[c] (0 without label smoothing)
+ *   [4] the shard's maximum of the stored logits (capping does not reorder)
+ *   [5] the global column of its first occurrence, as int32 bits
+ *   [6], [7] 0
+ * Rows that are not valid get zeros.  No loss, no workspace: the records of
+ * all shards go to ce_merge_stats (gathered across devices by the caller, or
+ * stacked in one buffer on one device).
+ */
+int ce_forward_stats_partial(const vsce_problem *problem, const void *logits,
+                             float *partial, hipStream_t stream);
+
+/*
+ * Merge of `shards` partial records into the full rows' statistics:
+ * `partials` holds [shards][rows][VSCE_PARTIAL_STRIDE] fp32 (device), shards
+ * in increasing column order; `problem` is the full one (vocab = vocab_total,
+ * vocab_offset 0; logits unused).  Per valid row:
+ *   m = max_s m_s, s* the first shard attaining it,
+ *   d' = d'_{s*} + sum over s != s* of (1 + d'_s) exp(m_s - m),
+ *   x[y] from its owner, S = sum_s S_s, the argmax from [4] / [5];
+ * then writes `stats` ([rows][VSCE_STATS_STRIDE], as ce_forward_stats), the
+ * loss outputs and the workspace normalizers, exactly as ce_forward_stats
+ * would for the unsharded matrix.  Each shard's gradient then comes from
+ * ce_backward_from_stats with its sharded problem, these stats and this
+ * workspace.
+ */
+int ce_merge_stats(const vsce_problem *problem, const float *partials, int32_t shards,
+                   float *stats, const vsce_outputs *out, void *workspace,
+                   hipStream_t stream);
+
+/*
  * Split backward (TransformerEngine PR #2325 cross_entropy_backward_kernel):
  * from the logits and the saved stats, writes grad = RN(sigma * go[n] *
  * dl_n/dx) in fp32 with one rounding, with the true-class term folded in
@@ -219,8 +272,10 @@ int ce_forward_stats(const vsce_problem *problem, const void *logits,
  * (in place) but must not otherwise overlap it.  grad_output is fp32 device
  * memory: one value read at grad_output[0] when grad_output_stride == 0 (mean,
  * sum), or [rows] values at grad_output[n * grad_output_stride] when it is 1
- * (none).  `workspace` must be the one the matching ce_forward_stats wrote.
- * Ignored and bad-target rows get zeros.
+ * (none).  `workspace` must be the one the matching ce_forward_stats (or
+ * ce_merge_stats) wrote.  Ignored and bad-target rows get zeros.  With a
+ * sharded problem, `logits` and `grad` are the shard's slices and `stats` the
+ * merged ones; only the shard that holds column y writes the true-class value.
  */
 int ce_backward_from_stats(const vsce_problem *problem, const void *logits,
                            void *grad, const float *stats,

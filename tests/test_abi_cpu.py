@@ -51,16 +51,18 @@ def test_header_constants_match_the_binding():
                for m in re.finditer(r"^#define\s+VSCE_(\w+)\s+(\w+)", text, flags=re.M)
                if re.fullmatch(r"0x[0-9a-fA-F]+|\d+", m.group(2))}
     for name in ("WS_W", "WS_SUM_W", "WS_N_VALID", "WS_N_INVALID", "WS_STATUS", "WS_INV_W",
-                 "WS_INV_N_VALID", "WS_HEADER_BYTES", "STATS_STRIDE"):
+                 "WS_INV_N_VALID", "WS_HEADER_BYTES", "STATS_STRIDE", "PARTIAL_STRIDE"):
         assert defines[name] == getattr(L, name), name
 
 
 def test_struct_layout_matches_the_header():
-    assert ctypes.sizeof(L.Problem) == 72
+    assert ctypes.sizeof(L.Problem) == 88
     assert L.Problem.label_smoothing.offset == 56
     assert L.Problem.softcap.offset == 60
     assert L.Problem.z_loss.offset == 64
     assert L.Problem.reserved.offset == 68
+    assert L.Problem.vocab_offset.offset == 72
+    assert L.Problem.vocab_total.offset == 80
     assert ctypes.sizeof(L.Outputs) == 40
     assert L.Outputs.z_loss.offset == 32
     # the header declares the fields in the same order
@@ -79,6 +81,7 @@ def _problem(**kw):
     p.target, p.class_weight = FAKE, None
     p.ignore_index, p.label_smoothing, p.reserved = -100, 0.0, 0
     p.softcap, p.z_loss = 0.0, 0.0
+    p.vocab_offset, p.vocab_total = 0, 0
     for k, v in kw.items():
         setattr(p, k, v)
     return p
@@ -125,6 +128,43 @@ def test_bad_pointers_are_rejected():
     assert _fused(_problem(class_weight=FAKE + 2)) == L.ERR_INVALID
     assert _stats(_problem(), stats=None) == L.ERR_INVALID
     assert _stats(_problem(), stats=FAKE + 4) == L.ERR_INVALID
+
+
+def _partial(p, logits=FAKE, partial=FAKE):
+    return L.raw_call("ce_forward_stats_partial", ctypes.byref(p), logits, partial, None)
+
+
+def _merge(p, partials=FAKE, shards=2, stats=FAKE, out="default", ws=FAKE):
+    o = _outputs() if out == "default" else out
+    return L.raw_call("ce_merge_stats", ctypes.byref(p), partials, shards, stats,
+                      None if o is None else ctypes.byref(o), ws, None)
+
+
+@pytest.mark.parametrize("offset,total", [(-1, 128), (65, 128), (0, 63), (8, 64)])
+def test_bad_vocab_shards_are_rejected(offset, total):
+    p = _problem(vocab_offset=offset, vocab_total=total)
+    assert _partial(p) == L.ERR_INVALID
+    assert _backward(p) == L.ERR_INVALID
+
+
+def test_whole_row_entry_points_refuse_a_shard():
+    p = _problem(vocab_offset=64, vocab_total=128)
+    assert _fused(p) == L.ERR_INVALID
+    assert _stats(p) == L.ERR_INVALID
+    assert _merge(p) == L.ERR_INVALID
+
+
+def test_partial_and_merge_argument_checks():
+    shard = _problem(vocab_offset=64, vocab_total=128)
+    assert _partial(shard, partial=None) == L.ERR_INVALID
+    assert _partial(shard, partial=FAKE + 4) == L.ERR_INVALID       # 16-byte records
+    assert _partial(_problem(rows=0, vocab_offset=64, vocab_total=128), partial=None) == L.OK
+    full = _problem(vocab=128, row_stride=128)
+    assert _merge(full, shards=0) == L.ERR_INVALID
+    assert _merge(full, partials=None) == L.ERR_INVALID
+    assert _merge(full, stats=FAKE + 8) == L.ERR_INVALID
+    assert _merge(full, out=None) == L.ERR_INVALID
+    assert _merge(full, ws=FAKE + 8) == L.ERR_INVALID
 
 
 def test_unsupported_sizes():

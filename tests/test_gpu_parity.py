@@ -334,6 +334,117 @@ def test_softcap_z_loss_llm_head_full_size():
     check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0, rows, **kw), xh, tgt, w)
 
 
+# ---------------------------------------------------------------- vocab-parallel shards
+# TransformerEngine PR #2325 (dist_process_group): each rank holds a slice of
+# the vocabulary, the per-row record (max, sum, target logit, scaled_x_sum) is
+# gathered and merged, and the review asks that the 4th value be summed too.
+# On one GPU the shards are column slices of one buffer, their records stacked.
+
+def run_sharded(wl, edges, reduction, go, softcap=0.0, z_loss=0.0, x_host=None, tgt=None):
+    dev = _dev()
+    _note(f"{wl.name} BT={wl.BT} V={wl.V} {wl.dtype} shards={len(edges) - 1} red={reduction} "
+          f"go={go} softcap={softcap} z_loss={z_loss}")
+    tgt = W.targets(wl) if tgt is None else tgt
+    w = W.class_weights(wl)
+    x_host = W.logits(wl, tgt) if x_host is None else x_host
+    x = x_host.to(dev)
+    t = torch.from_numpy(tgt).to(dev)
+    wt = None if w is None else torch.from_numpy(w).to(dev)
+    eps, V, P = wl.label_smoothing, wl.V, len(edges) - 1
+    parts = torch.empty((P, wl.BT, 8), dtype=torch.float32, device=dev)
+    for s_, (a, b) in enumerate(zip(edges[:-1], edges[1:])):
+        vf.forward_stats_partial(x[:, a:b], t, a, V, wt, -100, eps, softcap, out=parts[s_])
+    res = vf.merge_stats(parts, t, V, wt, -100, eps, reduction, softcap, z_loss, row_loss=True,
+                         accuracy=True, return_z_loss=True, dtype=wl.torch_dtype)
+    go_t = _go_tensor(go, reduction, wl.BT, dev)
+    g = torch.empty_like(x)
+    for a, b in zip(edges[:-1], edges[1:]):
+        vf.backward_from_stats(x[:, a:b], t, res["stats"], go_t, res["workspace"], wt, -100, eps,
+                               reduction, out=g[:, a:b], softcap=softcap, z_loss=z_loss,
+                               vocab_offset=a, vocab_total=V)
+    torch.cuda.synchronize()
+    out = {
+        "loss": res["loss"].cpu().numpy().astype(np.float64),
+        "row_loss": res["row_loss"].cpu().numpy().astype(np.float64),
+        "z_loss": res["z_loss"].cpu().numpy().astype(np.float64),
+        "stats": res["stats"].cpu().numpy().astype(np.float64),
+        "status": vf.status(res["workspace"]),
+        "acc": res["token_acc"].cpu().numpy().astype(np.float64),
+        "acc_mean": float(res["acc_mean"].cpu()),
+        "grad": g.float().cpu().numpy().astype(np.float64),
+        "parts": parts.cpu().numpy(),
+    }
+    return out, x_host, tgt, w
+
+
+def check_parts(wl, out, x_host, tgt, w, edges, softcap):
+    """Each shard's record against the oracle's record of the same shard."""
+    xa = W.as_f64(x_host)
+    for s_, (a, b) in enumerate(zip(edges[:-1], edges[1:])):
+        ref = oracle.partials(xa[:, a:b], tgt, a, wl.V, w, -100, wl.label_smoothing, softcap)
+        got = out["parts"][s_].astype(np.float64)
+        valid = (tgt >= 0) & (tgt < wl.V)
+        first = out["parts"][s_][:, 5].view(np.int32)
+        np.testing.assert_array_equal(first[valid], ref[valid, 5].astype(np.int64))
+        np.testing.assert_array_equal(got[valid, 4], ref[valid, 4])
+        tol = 2.0 ** -24 * (8 * softcap + np.abs(ref[valid][:, [0, 2]])) if softcap else 0.0
+        assert np.all(np.abs(got[valid][:, [0, 2]] - ref[valid][:, [0, 2]]) <= tol)
+        assert np.all(rel_err(got[valid, 1], ref[valid, 1]) <= 1e-5)
+        assert np.all(got[~valid] == 0)
+
+
+# Shard edges: even halves, uneven quarters (all 16-byte aligned), and three
+# shards of which two start or end off a 16-byte boundary (per-element path).
+LLM_EDGES = {"halves": [0, 64128, 128256], "quarters": [0, 24000, 64000, 100008, 128256],
+             "ragged": [0, 40001, 90000, 128256]}
+
+
+@pytest.mark.parametrize("edges", list(LLM_EDGES))
+@pytest.mark.parametrize("reduction,go", [("mean", 1.0), ("none", 0.37)])
+def test_vocab_shards_llm_head_rows(edges, reduction, go):
+    wl = W.with_rows(W.WORKLOADS["llm_head"], 48)
+    e = LLM_EDGES[edges]
+    out, xh, tgt, w = run_sharded(wl, e, reduction, go)
+    check_parts(wl, out, xh, tgt, w, e, 0.0)
+    check(wl, out, reference(wl, xh, tgt, w, reduction, go), xh, tgt, w)
+
+
+@pytest.mark.parametrize("softcap,z_loss", [(0.0, 0.0), (15.0, 1e-3)])
+def test_vocab_shards_weighted_rows(softcap, z_loss):
+    """Class weights (all V given to every shard), smoothing, mean: W and the
+    class-weight sum come from the merge's normalizers."""
+    wl = W.with_rows(W.WORKLOADS["weighted"], 40)
+    e = [0, 50000, 100000, 151936]
+    kw = dict(softcap=softcap, z_loss=z_loss)
+    out, xh, tgt, w = run_sharded(wl, e, "mean", 0.5, **kw)
+    check_parts(wl, out, xh, tgt, w, e, softcap)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", 0.5, **kw), xh, tgt, w)
+
+
+def test_vocab_shards_wide_fp32_rows():
+    wl = W.with_rows(W.WORKLOADS["wide_fp32"], 16)
+    e = [0, 64000, 128000, 192000, 256000]
+    out, xh, tgt, w = run_sharded(wl, e, "sum", 1.0, softcap=50.0, z_loss=1e-4)
+    check_parts(wl, out, xh, tgt, w, e, 50.0)
+    check(wl, out, reference(wl, xh, tgt, w, "sum", 1.0, softcap=50.0, z_loss=1e-4), xh, tgt, w)
+
+
+def test_vocab_shards_maximum_tied_across_shards():
+    """Equal row maxima in two shards: the merge keeps the first shard's exact
+    d' and counts the second copy, and the accuracy follows the first copy."""
+    wl = _small("llm_head", 24, 4096, ignore_frac=0.0, label_smoothing=0.1)
+    tgt = W.targets(wl)
+    tgt[::2] = 100  # half the rows target the first copy of the maximum
+    xh = W.logits(wl, tgt).clone()
+    xh[:, 100] = 30.0
+    xh[:, 3000] = 30.0
+    e = [0, 2048, 4096]
+    out, xh, tgt, w = run_sharded(wl, e, "mean", 1.0, x_host=xh, tgt=tgt)
+    check_parts(wl, out, xh, tgt, w, e, 0.0)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0), xh, tgt, w)
+    assert np.all(out["acc"][::2] == 1.0) and np.all(out["acc"][1::2] == 0.0)
+
+
 # ---------------------------------------------------------------- edge cases
 
 def _small(name, BT, V, **kw):

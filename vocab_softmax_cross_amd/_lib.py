@@ -21,11 +21,12 @@ REDUCTIONS = {"none": REDUCTION_NONE, "mean": REDUCTION_MEAN, "sum": REDUCTION_S
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_LAUNCH = 0, -1, -2, -3
 STATUS_BAD_TARGET = 1
 STATS_STRIDE = 4
+PARTIAL_STRIDE = 8
 WS_W, WS_SUM_W, WS_N_VALID, WS_N_INVALID, WS_STATUS, WS_HEADER_BYTES = 0, 8, 16, 24, 32, 256
 WS_INV_W, WS_INV_N_VALID = 40, 44
 
 EXPORTS = ("vsce_workspace_bytes", "ce_forward_fused_inplace", "ce_forward_fused_inplace_timed",
-           "ce_forward_stats",
+           "ce_forward_stats", "ce_forward_stats_partial", "ce_merge_stats",
            "ce_backward_from_stats", "ce_scale_grad", "vsce_strerror", "vsce_version")
 
 
@@ -44,6 +45,8 @@ class Problem(ctypes.Structure):
         ("softcap", c_float),
         ("z_loss", c_float),
         ("reserved", c_int32),
+        ("vocab_offset", c_int64),
+        ("vocab_total", c_int64),
     ]
 
 
@@ -86,6 +89,11 @@ def load() -> ctypes.CDLL:
     lib.ce_forward_fused_inplace_timed.restype = ctypes.c_int
     lib.ce_forward_stats.argtypes = [P(Problem), c_void_p, c_void_p, P(Outputs), c_void_p, c_void_p]
     lib.ce_forward_stats.restype = ctypes.c_int
+    lib.ce_forward_stats_partial.argtypes = [P(Problem), c_void_p, c_void_p, c_void_p]
+    lib.ce_forward_stats_partial.restype = ctypes.c_int
+    lib.ce_merge_stats.argtypes = [P(Problem), c_void_p, c_int32, c_void_p, P(Outputs), c_void_p,
+                                   c_void_p]
+    lib.ce_merge_stats.restype = ctypes.c_int
     lib.ce_backward_from_stats.argtypes = [P(Problem), c_void_p, c_void_p, c_void_p, c_void_p,
                                            c_int64, c_void_p, c_void_p]
     lib.ce_backward_from_stats.restype = ctypes.c_int
@@ -130,6 +138,17 @@ def ce_forward_stats(problem: Problem, logits: int, stats: int, outputs: Outputs
                      workspace: int, stream: int) -> int:
     return _check("ce_forward_stats", load().ce_forward_stats(
         ctypes.byref(problem), logits, stats, ctypes.byref(outputs), workspace, stream))
+
+
+def ce_forward_stats_partial(problem: Problem, logits: int, partial: int, stream: int) -> int:
+    return _check("ce_forward_stats_partial", load().ce_forward_stats_partial(
+        ctypes.byref(problem), logits, partial, stream))
+
+
+def ce_merge_stats(problem: Problem, partials: int, shards: int, stats: int, outputs: Outputs,
+                   workspace: int, stream: int) -> int:
+    return _check("ce_merge_stats", load().ce_merge_stats(
+        ctypes.byref(problem), partials, shards, stats, ctypes.byref(outputs), workspace, stream))
 
 
 def ce_backward_from_stats(problem: Problem, logits: int, grad: int, stats: int,

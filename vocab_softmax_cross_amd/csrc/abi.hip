@@ -42,15 +42,20 @@ int check_problem(const vsce_problem* pb, const void* logits, Prob& p) {
   const float cap = pb->softcap, zl = pb->z_loss;
   if (!(cap >= 0.0f && cap <= 3.0e38f)) return VSCE_ERR_INVALID;  // finite, not NaN
   if (!(zl >= 0.0f && zl <= 3.0e38f)) return VSCE_ERR_INVALID;
+  const int64_t voff = pb->vocab_offset;
+  const int64_t Vt = pb->vocab_total == 0 ? pb->vocab : pb->vocab_total;
+  if (voff < 0 || Vt < pb->vocab || voff > Vt - pb->vocab) return VSCE_ERR_INVALID;
   if (pb->rows > 0 && (!pb->target || !logits)) return VSCE_ERR_INVALID;
   if (logits && !aligned(logits, static_cast<uintptr_t>(eb))) return VSCE_ERR_INVALID;
   if (pb->class_weight && !aligned(pb->class_weight, 4)) return VSCE_ERR_INVALID;
   // Row byte offsets are 32-bit in the kernels; grids are 31-bit.
-  if (pb->vocab * eb >= (int64_t(1) << 31)) return VSCE_ERR_UNSUPPORTED;
+  if (pb->vocab * eb >= (int64_t(1) << 31) || Vt >= (int64_t(1) << 31)) return VSCE_ERR_UNSUPPORTED;
   if (pb->rows > 0x7fffffffLL) return VSCE_ERR_UNSUPPORTED;
 
   p.rows = pb->rows;
   p.V = pb->vocab;
+  p.voff = voff;
+  p.Vt = Vt;
   p.stride = pb->row_stride;
   p.dt = pb->dtype;
   p.red = pb->reduction;
@@ -58,15 +63,18 @@ int check_problem(const vsce_problem* pb, const void* logits, Prob& p) {
   p.weight = pb->class_weight;
   p.ignore_index = pb->ignore_index;
   p.eps = eps;
-  p.eta = eps / static_cast<float>(pb->vocab);
+  p.eta = eps / static_cast<float>(Vt);
   p.cap = cap;
   p.zl = zl;
   p.elem_bytes = eb;
   const int vec = 16 / eb;
   p.vec_ok = aligned(logits, 16) && (pb->row_stride * eb) % 16 == 0 && pb->vocab % vec == 0 &&
-             (!pb->class_weight || aligned(pb->class_weight, 16));
+             (!pb->class_weight || aligned(pb->class_weight + voff, 16));
   return VSCE_OK;
 }
+
+// The entry points that see whole rows (loss, fused gradient) take no shard.
+bool whole_rows(const Prob& p) { return p.voff == 0 && p.Vt == p.V; }
 
 int check_workspace(const void* ws) {
   if (!ws || !aligned(ws, kAlign)) return VSCE_ERR_INVALID;
@@ -78,12 +86,15 @@ int check_outputs(const vsce_outputs* out) {
   return VSCE_OK;
 }
 
-// The problem's fields every per-row kernel reads.
+// The problem's fields every per-row kernel reads.  The kernels index the
+// weights by this buffer's columns, so a shard sees its slice of them.
 void problem_args(const Prob& p, RowArgs& a) {
   a.stride = p.stride;
   a.V = p.V;
+  a.voff = p.voff;
+  a.Vt = p.Vt;
   a.target = p.target;
-  a.weight = p.weight;
+  a.weight = p.weight ? p.weight + p.voff : nullptr;
   a.ignore_index = p.ignore_index;
   a.eps = p.eps;
   a.eta = p.eta;
@@ -210,6 +221,7 @@ int ce_forward_fused_inplace(const vsce_problem* problem, void* logits_inout,
                              const vsce_outputs* out, void* workspace, hipStream_t stream) {
   Prob p;
   int rc = check_problem(problem, logits_inout, p);
+  if (rc == VSCE_OK && !whole_rows(p)) rc = VSCE_ERR_INVALID;
   if (rc == VSCE_OK) rc = check_outputs(out);
   if (rc == VSCE_OK) rc = check_workspace(workspace);
   if (rc != VSCE_OK) return rc;
@@ -222,6 +234,7 @@ int ce_forward_fused_inplace_timed(const vsce_problem* problem, void* logits_ino
                                    hipEvent_t begin, hipEvent_t end) {
   Prob p;
   int rc = check_problem(problem, logits_inout, p);
+  if (rc == VSCE_OK && !whole_rows(p)) rc = VSCE_ERR_INVALID;
   if (rc == VSCE_OK) rc = check_outputs(out);
   if (rc == VSCE_OK) rc = check_workspace(workspace);
   if (rc != VSCE_OK) return rc;
@@ -233,6 +246,7 @@ int ce_forward_stats(const vsce_problem* problem, const void* logits, float* sta
                      const vsce_outputs* out, void* workspace, hipStream_t stream) {
   Prob p;
   int rc = check_problem(problem, logits, p);
+  if (rc == VSCE_OK && !whole_rows(p)) rc = VSCE_ERR_INVALID;
   if (rc == VSCE_OK) rc = check_outputs(out);
   if (rc == VSCE_OK) rc = check_workspace(workspace);
   if (rc == VSCE_OK && p.rows > 0 && (!stats || !aligned(stats, 16))) rc = VSCE_ERR_INVALID;
@@ -240,6 +254,41 @@ int ce_forward_stats(const vsce_problem* problem, const void* logits, float* sta
   RowArgs a = row_args(p, const_cast<void*>(logits), out, workspace);
   a.stats = stats;
   return forward_common(p, a, out, workspace, false, stream);
+}
+
+int ce_forward_stats_partial(const vsce_problem* problem, const void* logits, float* partial,
+                             hipStream_t stream) {
+  Prob p;
+  int rc = check_problem(problem, logits, p);
+  if (rc != VSCE_OK) return rc;
+  if (p.rows == 0) return VSCE_OK;
+  if (!partial || !aligned(partial, 16)) return VSCE_ERR_INVALID;
+  RowArgs a = {};
+  a.x = const_cast<void*>(logits);
+  problem_args(p, a);
+  a.partial = partial;
+  return launch_stats(p, a, stream);
+}
+
+int ce_merge_stats(const vsce_problem* problem, const float* partials, int32_t shards,
+                   float* stats, const vsce_outputs* out, void* workspace, hipStream_t stream) {
+  Prob p;
+  // The merge reads no logits: check the problem as if it had an aligned buffer.
+  int rc = check_problem(problem, reinterpret_cast<const void*>(uintptr_t{256}), p);
+  if (rc == VSCE_OK && !whole_rows(p)) rc = VSCE_ERR_INVALID;
+  if (rc == VSCE_OK) rc = check_outputs(out);
+  if (rc == VSCE_OK) rc = check_workspace(workspace);
+  if (rc != VSCE_OK) return rc;
+  if (shards < 1) return VSCE_ERR_INVALID;
+  if (p.rows > 0 && (!partials || !stats || !aligned(partials, 16) || !aligned(stats, 16)))
+    return VSCE_ERR_INVALID;
+  RowArgs a = row_args(p, nullptr, out, workspace);
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(workspace);
+  rc = launch_prologue(p, hdr, stream);
+  if (rc == VSCE_OK) rc = launch_merge(p, partials, shards, stats, a, stream);
+  if (rc != VSCE_OK) return rc;
+  return launch_finalize(p, a.loss_rows, a.acc_rows, a.z_rows, out->loss, out->acc_mean,
+                         p.red == VSCE_REDUCTION_NONE ? nullptr : out->z_loss, hdr, stream);
 }
 
 int ce_backward_from_stats(const vsce_problem* problem, const void* logits, void* grad,

@@ -62,7 +62,7 @@ void fused_resident_kernel(const RowArgs a) {
   // so the buffer range check drops them whether or not it counts soffset.
   auto lane_off = [&](int k) { return in_row(k) ? voff : kOutOfRange; };
   const int64_t y = a.target[n];
-  const int cls = row_class(y, a.V, a.ignore_index);
+  const int cls = row_class(y, a.Vt, a.ignore_index);
   const SoftCap cap{a.cap, a.cap_k};
 
   if (cls != kValid) {  // uniform over the workgroup: zero gradient, no read

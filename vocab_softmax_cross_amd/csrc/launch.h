@@ -15,7 +15,9 @@ struct WsHeader;
 // A validated problem with the derived quantities the launchers need.
 struct Prob {
   int64_t rows;
-  int64_t V;
+  int64_t V;       // columns of this buffer
+  int64_t voff;    // global column of its first column (vocab-parallel shard)
+  int64_t Vt;      // full vocabulary (= V unless sharded)
   int64_t stride;  // elements
   int dt;          // vsce_dtype
   int red;         // vsce_reduction
@@ -35,7 +37,9 @@ struct RowArgs {
   void* x;              // logits (the gradient is written here by the fused kernels)
   void* g;              // gradient output of the split backward (may equal x)
   int64_t stride;       // elements between rows
-  int64_t V;
+  int64_t V;            // columns of this buffer
+  int64_t voff;         // global column of its first column (shard), else 0
+  int64_t Vt;           // full vocabulary: targets are classes of [0, Vt)
   int64_t nvec;         // 16-byte vectors per row (vector path) or V (scalar path)
   const int64_t* target;
   const float* weight;  // [V] or null
@@ -51,6 +55,7 @@ struct RowArgs {
   float* acc_rows;      // [rows] or null
   float* z_rows;        // [rows] per-row z-loss, or null
   float* stats;         // [rows][4] or null
+  float* partial;       // [rows][8] shard records (partial statistics mode), or null
   const float* go;      // grad_output (backward / scale)
   int64_t go_stride;    // 0 (scalar) or 1 (per row)
   int skip_if_one;
@@ -79,6 +84,9 @@ int launch_fused_stream(const Prob& p, RowArgs a, hipStream_t s);
 int launch_stats(const Prob& p, RowArgs a, hipStream_t s);
 // Split backward: logits read + gradient write from the saved statistics.
 int launch_backward(const Prob& p, RowArgs a, hipStream_t s);
+// Merge of shard records into full statistics and row losses.
+int launch_merge(const Prob& p, const float* partials, int shards, float* stats,
+                 const RowArgs& a, hipStream_t s);
 // In-place grad_output scale.
 int launch_scale(const Prob& p, RowArgs a, hipStream_t s);
 

@@ -121,10 +121,74 @@ __global__ __launch_bounds__(kSmallNT) void finalize_kernel(const float* loss_ro
   }
 }
 
+// The merge of vocab-parallel shard records (TransformerEngine PR #2325: the
+// per-row max, sum, target logit and scaled_x_sum gathered from every rank,
+// the 4th value summed as its review asks), one thread per row:
+//   m = max_s m_s, s* the first shard attaining it,
+//   d' = d'_{s*} + sum over s != s* of (1 + d'_s) exp(m_s - m)
+// (the shard that holds the first maximum keeps its exact d'; the others
+// bring their maximum back as the 1), x[y] from its owner (the others hold
+// 0), S summed, and the argmax of the stored logits from [4] and [5].  Then
+// the row loss, z-loss and accuracy as the statistics kernel computes them.
+constexpr int kMergeNT = 256;
+
+__global__ __launch_bounds__(kMergeNT) void merge_kernel(const float* partials, int shards,
+                                                        float* stats, const RowArgs a) {
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * kMergeNT + threadIdx.x;
+  if (n >= a.rows) return;
+  const int64_t y = a.target[n];
+  const int cls = row_class(y, a.Vt, a.ignore_index);
+  float4* st = reinterpret_cast<float4*>(stats) + n;
+  if (cls != kValid) {
+    const float l = (cls == kIgnored) ? 0.0f : __builtin_nanf("");
+    store_row(a, n, l, 0.0f, l);
+    *st = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const int64_t shard_stride = a.rows * VSCE_PARTIAL_STRIDE;
+  auto rec = [&](int s, int k) { return partials[s * shard_stride + n * VSCE_PARTIAL_STRIDE + k]; };
+  float m = -__builtin_inff(), mx = -__builtin_inff();
+  int ss = 0, sa = 0;
+  for (int s = 0; s < shards; ++s) {
+    const float ms = rec(s, 0), xs = rec(s, 4);
+    if (ms > m) {
+      m = ms;
+      ss = s;
+    }
+    if (xs > mx) {
+      mx = xs;
+      sa = s;
+    }
+  }
+  float dp = rec(ss, 1), xy = 0.0f, S = 0.0f;
+  for (int s = 0; s < shards; ++s) {
+    if (s != ss) dp += (1.0f + rec(s, 1)) * __builtin_amdgcn_exp2f((rec(s, 0) - m) * kLog2e);
+    xy += rec(s, 2);
+    S += rec(s, 3);
+  }
+  const int first = __float_as_int(rec(sa, 5));
+  const float wy = a.weight ? a.weight[y] : 1.0f;
+  const float sum_w = static_cast<float>(a.ws->sum_w);
+  const float lg = log1pf(dp);
+  const float z = row_z(m, lg, a.zl);
+  store_row(a, n, row_loss(m, lg, xy, S, wy, sum_w, a.eps, a.eta) + z,
+            (static_cast<int64_t>(first) == y) ? 1.0f : 0.0f, z);
+  *st = make_float4(m, dp, xy, a.eps > 0.0f ? S : 0.0f);
+}
+
 }  // namespace
 
+int launch_merge(const Prob& p, const float* partials, int shards, float* stats,
+                 const RowArgs& a, hipStream_t s) {
+  if (p.rows == 0) return VSCE_OK;
+  const int64_t grid = (p.rows + kMergeNT - 1) / kMergeNT;
+  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(grid)), dim3(kMergeNT), 0, s,
+                     partials, shards, stats, a);
+  return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
+}
+
 int launch_prologue(const Prob& p, WsHeader* ws, hipStream_t s) {
-  hipLaunchKernelGGL(prologue_kernel, dim3(1), dim3(kSmallNT), 0, s, p.target, p.rows, p.V,
+  hipLaunchKernelGGL(prologue_kernel, dim3(1), dim3(kSmallNT), 0, s, p.target, p.rows, p.Vt,
                      p.weight, p.ignore_index, ws);
   return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
 }

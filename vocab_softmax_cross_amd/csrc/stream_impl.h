@@ -74,12 +74,13 @@ struct Grp {
 };
 
 // Per-row statistics by streaming: returns (M, d', S, first) on every thread,
-// M being the (capped) maximum the loss reads.  Must be called by the whole
-// workgroup (it contains barriers).
+// M being the (capped) maximum the loss reads, and the maximum of the stored
+// logits in *Mraw_out.  Must be called by the whole workgroup (it contains
+// barriers).
 template <int DT, int NT, int U, bool WEIGHTED, bool VECP, bool CAP>
 __device__ inline void stream_stats(const RowArgs& a, const char* row, float& M_out,
                                     float& dp_out, float& S_out, int& first_out, float* red_max,
-                                    float4* red_sum) {
+                                    float4* red_sum, float* Mraw_out = nullptr) {
   using G = Grp<DT, VECP>;
   constexpr int E = G::E;
   const int tid = threadIdx.x;
@@ -151,6 +152,7 @@ __device__ inline void stream_stats(const RowArgs& a, const char* row, float& M_
   }
   rs = block_sums<NT>(rs, red_sum);
   M_out = Mc;
+  if (Mraw_out) *Mraw_out = M;
   dp_out = rs.s + static_cast<float>(rs.cnt - 1);
   S_out = rs.S;
   first_out = rs.first;
@@ -166,8 +168,8 @@ __device__ inline void stream_grad(const RowArgs& a, const char* src, char* dst,
   constexpr int E = G::E;
   const int tid = threadIdx.x;
   const SoftCap cap{a.cap, a.cap_k};
-  const int64_t gy = y / E;
-  const int iy = static_cast<int>(y % E);
+  const int64_t gy = y >= 0 ? y / E : -1;  // y < 0: no element here owns the target
+  const int iy = static_cast<int>(y >= 0 ? y % E : 0);
   for (int64_t g0 = g_begin; g0 < g_end; g0 += static_cast<int64_t>(NT) * U) {
     float f[U][E];
     static_for<U>([&](auto u) {
@@ -210,8 +212,10 @@ __device__ inline void stream_zero(char* dst, int64_t g_begin, int64_t g_end, in
   for (int64_t g = g_begin + threadIdx.x; g < g_end; g += nt) G::store(dst, g, z);
 }
 
+// w[y] for a global class y (a.weight points at this buffer's first column
+// of the full weight vector).
 __device__ inline float row_weight(const RowArgs& a, int64_t y, bool weighted) {
-  return weighted ? a.weight[y] : 1.0f;
+  return weighted ? a.weight[y - a.voff] : 1.0f;
 }
 
 // Slope of the soft-cap at the stored true-class logit (1 without CAP).
@@ -231,18 +235,40 @@ __global__ __launch_bounds__(NT) void stats_kernel(const RowArgs a) {
   const int64_t n = xcd_contiguous(blockIdx.x, a.rows);
   const char* row = static_cast<const char*>(a.x) + n * a.stride * D::BYTES;
   const int64_t y = a.target[n];
-  const int cls = row_class(y, a.V, a.ignore_index);
+  const int cls = row_class(y, a.Vt, a.ignore_index);
   if (cls != kValid) {
     if (threadIdx.x == 0) {
+      if (a.partial) {
+        float4* pr = reinterpret_cast<float4*>(a.partial + n * VSCE_PARTIAL_STRIDE);
+        pr[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+        pr[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        return;
+      }
       const float l = (cls == kIgnored) ? 0.0f : __builtin_nanf("");
       store_row(a, n, l, 0.0f, l);
       if (a.stats) reinterpret_cast<float4*>(a.stats)[n] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     return;
   }
-  float M, dp, S;
+  float M, dp, S, Mraw;
   int first;
-  stream_stats<DT, NT, U, WEIGHTED, VECP, CAP>(a, row, M, dp, S, first, red_max, red_sum);
+  stream_stats<DT, NT, U, WEIGHTED, VECP, CAP>(a, row, M, dp, S, first, red_max, red_sum, &Mraw);
+  if (a.partial) {
+    // One shard's record (vocab-parallel): the target logit only where this
+    // shard holds column y, the first maximum as a global column.
+    if (threadIdx.x == 0) {
+      const int64_t yl = y - a.voff;
+      float xy = 0.0f;
+      if (yl >= 0 && yl < a.V) {
+        const float xs = D::load1(row, yl);
+        xy = CAP ? SoftCap{a.cap, a.cap_k}.value(xs) : xs;
+      }
+      float4* pr = reinterpret_cast<float4*>(a.partial + n * VSCE_PARTIAL_STRIDE);
+      pr[0] = make_float4(M, dp, xy, a.eps > 0.0f ? S : 0.0f);
+      pr[1] = make_float4(Mraw, __int_as_float(static_cast<int>(a.voff) + first), 0.f, 0.f);
+    }
+    return;
+  }
   if (threadIdx.x == 0) {
     const float xs = D::load1(row, y);
     const float xy = CAP ? SoftCap{a.cap, a.cap_k}.value(xs) : xs;
@@ -265,7 +291,7 @@ __global__ __launch_bounds__(NT) void fused_stream_kernel(const RowArgs a) {
   const int64_t n = xcd_contiguous(blockIdx.x, a.rows);
   char* row = static_cast<char*>(a.x) + n * a.stride * D::BYTES;
   const int64_t y = a.target[n];
-  const int cls = row_class(y, a.V, a.ignore_index);
+  const int cls = row_class(y, a.Vt, a.ignore_index);
   if (cls != kValid) {
     stream_zero<DT, VECP>(row, 0, a.nvec, NT, U);
     const float l = (cls == kIgnored) ? 0.0f : __builtin_nanf("");
@@ -308,7 +334,7 @@ __global__ __launch_bounds__(NT) void backward_kernel(const RowArgs a) {
   const char* src = static_cast<const char*>(a.x) + n * a.stride * D::BYTES;
   char* dst = static_cast<char*>(a.g) + n * a.stride * D::BYTES;
   const int64_t y = a.target[n];
-  const int cls = row_class(y, a.V, a.ignore_index);
+  const int cls = row_class(y, a.Vt, a.ignore_index);
   if (cls != kValid) {
     stream_zero<DT, VECP>(dst, g_begin, g_end, NT, U);
     return;
@@ -319,14 +345,17 @@ __global__ __launch_bounds__(NT) void backward_kernel(const RowArgs a) {
   const float sum_w = static_cast<float>(a.ws->sum_w);
   RowTerms t = row_terms(st.x, st.y, log1pf(st.y), st.z, row_weight(a, y, WEIGHTED), sum_w,
                          a.eps, a.eta, sigma, a.zl, z_sigma(a) * go);
+  // The target's column in this buffer (a vocab-parallel shard may not hold
+  // it: then no element of the row takes the true-class value).
+  const int64_t yl = (y - a.voff >= 0 && y - a.voff < a.V) ? y - a.voff : -1;
   // The saved x[y] is capped; the slope needs the stored one.  Only the
   // chunk that holds column y reads it (src is not yet overwritten: each
   // workgroup writes its own chunk only, after this read).
   if constexpr (CAP) {
     const int64_t per_elems = static_cast<int64_t>(NT) * U * Grp<DT, VECP>::E;
-    if (y / per_elems == c) t.dxy *= cap_slope<CAP>(a, D::load1(src, y));
+    if (yl >= 0 && yl / per_elems == c) t.dxy *= cap_slope<CAP>(a, D::load1(src, yl));
   }
-  stream_grad<DT, NT, U, WEIGHTED, VECP, CAP>(a, src, dst, g_begin, g_end, t, y);
+  stream_grad<DT, NT, U, WEIGHTED, VECP, CAP>(a, src, dst, g_begin, g_end, t, yl);
 }
 
 // Grid-stride over (row, column chunk) work items, so that a grad_output of

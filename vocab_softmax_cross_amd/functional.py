@@ -49,16 +49,19 @@ def _rows_view(logits: torch.Tensor) -> torch.Tensor:
 
 def make_problem(x2d: torch.Tensor, target: torch.Tensor, weight: Optional[torch.Tensor],
                  ignore_index: int, label_smoothing: float, reduction: str,
-                 softcap: float = 0.0, z_loss: float = 0.0) -> L.Problem:
+                 softcap: float = 0.0, z_loss: float = 0.0, vocab_offset: int = 0,
+                 vocab_total: int = 0) -> L.Problem:
     if x2d.dtype not in _DTYPES:
         raise TypeError(f"unsupported logits dtype {x2d.dtype}")
     if target.dtype != torch.int64 or target.device != x2d.device:
         raise TypeError("target must be an int64 tensor on the logits' device")
     if not target.is_contiguous() or target.numel() != x2d.shape[0]:
         raise ValueError("target must be contiguous with one entry per row")
+    V = vocab_total or x2d.shape[1]
     if weight is not None:
-        if weight.dtype != torch.float32 or not weight.is_contiguous() or weight.numel() != x2d.shape[1]:
-            raise ValueError("class weights must be a contiguous float32 [V] tensor")
+        if weight.dtype != torch.float32 or not weight.is_contiguous() or weight.numel() != V:
+            raise ValueError("class weights must be a contiguous float32 [V] tensor "
+                             "(all V of them for a vocabulary shard)")
     p = L.Problem()
     p.rows = x2d.shape[0]
     p.vocab = x2d.shape[1]
@@ -72,6 +75,8 @@ def make_problem(x2d: torch.Tensor, target: torch.Tensor, weight: Optional[torch
     p.softcap = float(softcap)
     p.z_loss = float(z_loss)
     p.reserved = 0
+    p.vocab_offset = int(vocab_offset)
+    p.vocab_total = int(vocab_total)
     return p
 
 
@@ -158,12 +163,15 @@ def backward_from_stats(logits: torch.Tensor, target: torch.Tensor, stats: torch
                         weight: Optional[torch.Tensor] = None, ignore_index: int = -100,
                         label_smoothing: float = 0.0, reduction: str = "mean",
                         out: Optional[torch.Tensor] = None, softcap: float = 0.0,
-                        z_loss: float = 0.0) -> torch.Tensor:
+                        z_loss: float = 0.0, vocab_offset: int = 0,
+                        vocab_total: int = 0) -> torch.Tensor:
     """ce_backward_from_stats: the gradient in the logits' type (``out`` may be
-    the logits themselves for an in-place backward)."""
+    the logits themselves for an in-place backward).  For one shard of a
+    vocab-parallel layout pass its ``vocab_offset``, the full ``vocab_total``,
+    the merged ``stats`` and the merge's workspace."""
     x = _rows_view(logits)
     p = make_problem(x, target.reshape(-1), weight, ignore_index, label_smoothing, reduction,
-                     softcap, z_loss)
+                     softcap, z_loss, vocab_offset, vocab_total)
     g = (torch.empty_strided(x.size(), x.stride(), dtype=x.dtype, device=x.device)
          if out is None else _rows_view(out))
     if g.shape != x.shape or g.dtype != x.dtype or g.stride() != x.stride():
@@ -172,6 +180,61 @@ def backward_from_stats(logits: torch.Tensor, target: torch.Tensor, stats: torch
     L.ce_backward_from_stats(p, x.data_ptr(), g.data_ptr(), stats.data_ptr(), go.data_ptr(),
                              stride, workspace.data_ptr(), _stream(x))
     return g.view(logits.shape) if out is None else out
+
+
+def forward_stats_partial(logits_shard: torch.Tensor, target: torch.Tensor, vocab_offset: int,
+                          vocab_total: int, weight: Optional[torch.Tensor] = None,
+                          ignore_index: int = -100, label_smoothing: float = 0.0,
+                          softcap: float = 0.0,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ce_forward_stats_partial: one vocabulary shard's per-row record
+    ([rows, 8] fp32; see include/vsce.h).  ``logits_shard`` holds columns
+    [vocab_offset, vocab_offset + width) of a ``vocab_total``-column
+    vocabulary; targets are global; ``weight`` holds all vocab_total weights.
+    ``out`` may be a slice of a stacked [shards, rows, 8] buffer."""
+    x = _rows_view(logits_shard)
+    p = make_problem(x, target.reshape(-1), weight, ignore_index, label_smoothing, "none",
+                     softcap, 0.0, vocab_offset, vocab_total)
+    part = out if out is not None else torch.empty((max(p.rows, 1), L.PARTIAL_STRIDE),
+                                                    dtype=torch.float32, device=x.device)
+    L.ce_forward_stats_partial(p, x.data_ptr(), part.data_ptr(), _stream(x))
+    return part[:p.rows]
+
+
+def merge_stats(partials: torch.Tensor, target: torch.Tensor, vocab_total: int,
+                weight: Optional[torch.Tensor] = None, ignore_index: int = -100,
+                label_smoothing: float = 0.0, reduction: str = "mean", softcap: float = 0.0,
+                z_loss: float = 0.0, row_loss: bool = False, accuracy: bool = False,
+                return_z_loss: bool = False, dtype: torch.dtype = torch.bfloat16) -> dict:
+    """ce_merge_stats: the shards' stacked records ([shards, rows, 8], column
+    order) -> the full rows' statistics, the loss outputs and the workspace,
+    as ce_forward_stats gives them for the unsharded matrix."""
+    if partials.dim() != 3 or partials.shape[2] != L.PARTIAL_STRIDE or not partials.is_contiguous():
+        raise ValueError("partials must be a contiguous [shards, rows, 8] float32 tensor")
+    shards, rows = partials.shape[0], partials.shape[1]
+    dev = partials.device
+    t = target.reshape(-1)
+    if t.dtype != torch.int64 or t.device != dev or not t.is_contiguous() or t.numel() != rows:
+        raise ValueError("target must be a contiguous int64 tensor with one entry per row")
+    if weight is not None and (weight.dtype != torch.float32 or not weight.is_contiguous()
+                               or weight.numel() != vocab_total):
+        raise ValueError("class weights must be a contiguous float32 [vocab_total] tensor")
+    p = L.Problem()
+    p.rows, p.vocab, p.row_stride = rows, vocab_total, vocab_total  # no logits are read
+    p.dtype, p.reduction = _DTYPES[dtype], L.REDUCTIONS[reduction]
+    p.target = t.data_ptr() or None
+    p.class_weight = None if weight is None else weight.data_ptr()
+    p.ignore_index, p.label_smoothing = int(ignore_index), float(label_smoothing)
+    p.softcap, p.z_loss, p.reserved = float(softcap), float(z_loss), 0
+    p.vocab_offset, p.vocab_total = 0, int(vocab_total)
+    ws = workspace_for(rows, dev)
+    stats = torch.empty((max(rows, 1), L.STATS_STRIDE), dtype=torch.float32, device=dev)
+    o, res = _outputs(rows, reduction, dev, row_loss, accuracy, return_z_loss)
+    L.ce_merge_stats(p, partials.data_ptr(), shards, stats.data_ptr(), o, ws.data_ptr(),
+                     torch.cuda.current_stream(dev).cuda_stream)
+    res["stats"] = stats[:rows]
+    res["workspace"] = ws
+    return res
 
 
 def scale_grad(grad: torch.Tensor, grad_output: torch.Tensor, reduction: str = "mean",
