@@ -74,6 +74,26 @@ class Hip:
     def destroy(self, e: int) -> None:
         self.lib.hipEventDestroy(e)
 
+    def record(self, e: int, stream: int) -> None:
+        if self.lib.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def launch_ms(self, fn, n: int, stream: int) -> float:
+        """Median GPU time of one launch of fn() over n launches, each between
+        its own pair of events on `stream` (host launch overhead excluded)."""
+        import numpy as np
+        evs = [(self.event(), self.event()) for _ in range(n)]
+        for a, b in evs:
+            self.record(a, stream)
+            fn()
+            self.record(b, stream)
+        self.lib.hipDeviceSynchronize()
+        ms = [self.elapsed_ms(a, b) for a, b in evs]
+        for a, b in evs:
+            self.destroy(a)
+            self.destroy(b)
+        return float(np.median(ms))
+
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
@@ -148,8 +168,14 @@ def main():
     import vocab_softmax_cross_amd._lib as L
     import workloads as W
 
-    L.load()
+    # Initialise the HIP runtime (through torch) before the library is loaded,
+    # so that the library registers its kernels with a running runtime, the
+    # order every test and smoke() use.
     dev = torch.device("cuda:0")
+    torch.cuda.init()
+    torch.empty(1, device=dev)
+    torch.cuda.synchronize()
+    L.load()
     wl = W.WORKLOADS[args.workload]
     K, Wu = args.steps, args.warmup
     tgt = W.targets(wl)
@@ -273,6 +299,46 @@ def main():
         ev[:] = [(hip.event(), hip.event()) for _ in range(K)]
         wcap = timed(fused_steps(problems_cap), go_one, events=ev)
         cap_kernel_s = float(np.mean([hip.elapsed_ms(a, b) for a, b in ev])) / 1e3
+        # One rank of an 8-way vocab-parallel layout at its real shape: the
+        # statistics of its [BT, V/8] slice, the merge of the 8 gathered
+        # records (here stacked on one device), its slice's backward.
+        P = 8
+        Vs = wl.V // P
+        shard = pristine[:, :Vs].contiguous()
+        grad_shard = torch.empty_like(shard)
+        parts = torch.empty((P, wl.BT, L.PARTIAL_STRIDE), dtype=torch.float32, device=dev)
+        merged = torch.empty((wl.BT, L.STATS_STRIDE), dtype=torch.float32, device=dev)
+
+        def shard_problem(width, offset, stride):
+            p = problem(None)
+            p.vocab, p.row_stride, p.vocab_offset, p.vocab_total = width, stride, offset, wl.V
+            return p
+
+        for s_ in range(P):  # every rank's record, so that the merge sees real data
+            a0 = s_ * Vs
+            b0 = wl.V if s_ == P - 1 else a0 + Vs
+            L.ce_forward_stats_partial(shard_problem(b0 - a0, a0, wl.V),
+                                       pristine[:, a0:b0].data_ptr(), parts[s_].data_ptr(), stream)
+        rank_p = shard_problem(Vs, 0, Vs)
+        full_p = problem(None)
+        merge_ws = torch.empty_like(ws)
+        t_stats = hip.launch_ms(lambda: L.ce_forward_stats_partial(
+            rank_p, shard.data_ptr(), parts[0].data_ptr(), stream), K, stream)
+        t_merge = hip.launch_ms(lambda: L.ce_merge_stats(
+            full_p, parts.data_ptr(), P, merged.data_ptr(), outs, merge_ws.data_ptr(), stream),
+            K, stream)
+        t_bwd = hip.launch_ms(lambda: L.ce_backward_from_stats(
+            rank_p, shard.data_ptr(), grad_shard.data_ptr(), merged.data_ptr(),
+            go_one.data_ptr(), 0, merge_ws.data_ptr(), stream), K, stream)
+        shard_row = Vs * wl.elem_bytes
+        extra["vocab_parallel_8_one_rank"] = {
+            "shard": [wl.BT, Vs],
+            "stats_ms": round(t_stats, 4),
+            "stats_GBps": round(n_valid * shard_row / t_stats / 1e6, 1),
+            "merge_ms": round(t_merge, 4),
+            "backward_ms": round(t_bwd, 4),
+            "backward_GBps": round((n_valid + wl.BT) * shard_row / t_bwd / 1e6, 1),
+            "rank_kernels_ms": round(t_stats + t_merge + t_bwd, 4)}
         extra[f"fused_softcap{CAP:g}_zloss{ZL:g}"] = {
             "ms_per_step": round(wcap / K * 1e3, 4),
             "rows_per_s": round(wl.BT * K / wcap, 1),
