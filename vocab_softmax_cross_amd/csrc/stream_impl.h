@@ -16,9 +16,10 @@
 //
 // Each thread keeps an online (max, sum) pair per lane: a batch of U vectors
 // raises the lane max once and rescales the sum once.  After the workgroup
-// max M is known, the lanes whose own max equals M recompute their sum with
-// the elements equal to M left out (re-reading their share of the row), so
-// d' = d - 1 never loses the small terms to the leading 1.
+// max M is known, the shares of the lanes whose own max equals M are summed
+// again with the elements equal to M left out (re-read by the whole
+// workgroup, one vector per thread), so d' = d - 1 never loses the small
+// terms to the leading 1.
 //
 // CAP (soft-capped logits): maxima, ties and the first index are taken on the
 // stored logits, sums on the capped ones (the shift of a lane's sum is the
@@ -128,27 +129,52 @@ __device__ inline void stream_stats(const RowArgs& a, const char* row, float& M_
   const float Mc = capped(M);                    // of the logits the loss reads
   const float ML = (M == -__builtin_inff()) ? 0.0f : Mc * kLog2e;
   RowSums rs = {0.0f, S, 0, 0x7fffffff};
-  if (m == M) {
-    // This lane holds the row maximum: recompute its share exactly.
-    for (int64_t g0 = 0; g0 < ng; g0 += static_cast<int64_t>(NT) * U) {
-      static_for<U>([&](auto u) {
-        const int64_t g = g0 + u * NT + tid;
-        if (g < ng) {
-          float f[E];
-          G::load(row, g, f);
-#pragma unroll
-          for (int i = 0; i < E; ++i) {
-            const bool eq = (f[i] == M);
-            rs.s += eq ? 0.0f : exp_shifted(capped(f[i]), ML);
-            rs.cnt += eq ? 1 : 0;
-            if (eq) rs.first = min(rs.first, static_cast<int>(g * E + i));
-          }
-        }
-      });
-    }
-  } else {
+  const bool owner = (m == M);  // this lane's share holds the row maximum
+  if (!owner)
     rs.s = (m == -__builtin_inff()) ? 0.0f
                                     : s * __builtin_amdgcn_exp2f((capped(m) - Mc) * kLog2e);
+  // The shares of the lanes that hold the maximum are summed again with every
+  // element equal to M left out -- by the whole workgroup, one vector per
+  // thread, so the second look costs one memory round trip rather than one per
+  // batch of the owner's share.  Owners are listed in lane order (a prefix
+  // count over the wavefronts' ballots), so the sum order is fixed.
+  constexpr int NW = NT / kWave;
+  __shared__ uint64_t owner_mask[NW];
+  __shared__ int owners[NT];
+  const int lane = tid & (kWave - 1), wave = uniform(tid / kWave);
+  const uint64_t ball = __ballot(owner);
+  if (lane == 0) owner_mask[wave] = ball;
+  lds_barrier();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int c = __builtin_popcountll(owner_mask[w]);
+    base += (w < wave) ? c : 0;
+    total += c;
+  }
+  if (owner) {
+    const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(ball >> 32),
+                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(ball), 0));
+    owners[base + below] = tid;
+  }
+  lds_barrier();
+  // Vectors of a lane's share: lane t holds groups t, t + NT, ... below ng.
+  const int share = static_cast<int>((ng + NT - 1) / NT);
+  const int items = total * share;
+  for (int w = tid; w < items; w += NT) {
+    const int o = w / share;
+    const int64_t g = owners[o] + static_cast<int64_t>(w - o * share) * NT;
+    if (g < ng) {
+      float f[E];
+      G::load(row, g, f);
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const bool eq = (f[i] == M);
+        rs.s += eq ? 0.0f : exp_shifted(capped(f[i]), ML);
+        rs.cnt += eq ? 1 : 0;
+        if (eq) rs.first = min(rs.first, static_cast<int>(g * E + i));
+      }
+    }
   }
   rs = block_sums<NT>(rs, red_sum);
   M_out = Mc;
