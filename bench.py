@@ -153,6 +153,63 @@ def cpu_baseline(wl, tgt, budget_s: float, threads: int = 0):
                       f"forward + gradient + rounding to {wl.dtype}, {spent:.1f} s"}
 
 
+def long_rows_mode(L, W, hip, dev, stream, K):
+    """The fused mode on rows too long to keep on chip (the wide fp32
+    workload, 8192 x 256000): each row is read twice and written once.  Both
+    kernel choices are timed per launch by events on the launch stream, each
+    launch on a fresh copy of the logits: the default pair (statistics, then
+    the gradient in place) and the one-launch LDS ring."""
+    import numpy as np
+    import torch
+    wl = W.WORKLOADS["wide_fp32"]
+    tgt = W.targets(wl)
+    pristine = W.logits(wl, tgt).to(dev)
+    n_buf = 4
+    bufs = [torch.empty_like(pristine) for _ in range(n_buf)]
+    t = torch.from_numpy(tgt).to(dev)
+    ws = torch.empty(L.vsce_workspace_bytes(wl.BT), dtype=torch.uint8, device=dev)
+    loss = torch.empty(wl.BT, dtype=torch.float32, device=dev)
+    outs = L.Outputs()
+    outs.loss = loss.data_ptr()
+    n_valid = int(np.sum((tgt >= 0) & (tgt < wl.V)))
+    row = wl.V * wl.elem_bytes
+    alg = 3 * n_valid * row + (wl.BT - n_valid) * row + 12 * wl.BT
+
+    def problem(flags):
+        p = L.Problem()
+        p.rows, p.vocab, p.row_stride = wl.BT, wl.V, wl.V
+        p.dtype, p.reduction = L.F32, L.REDUCTIONS[wl.reductions[0]]
+        p.target, p.class_weight = t.data_ptr(), None
+        p.ignore_index, p.label_smoothing, p.flags = -100, wl.label_smoothing, flags
+        p.softcap, p.z_loss = 0.0, 0.0
+        return p
+
+    res = {"workload": wl.name, "shape": [wl.BT, wl.V], "logits": wl.dtype,
+           "alg_bytes_per_launch": alg}
+    for name, flags in (("pair", 0), ("ring", L.FLAG_LONG_ROWS_RING)):
+        p = problem(flags)
+        ms = []
+        for r0 in range(0, K, n_buf):
+            for b in bufs:
+                b.copy_(pristine)
+            torch.cuda.synchronize()
+            evs = [(hip.event(), hip.event()) for _ in range(min(n_buf, K - r0))]
+            for b, (e0, e1) in zip(bufs, evs):
+                L.ce_forward_fused_inplace_timed(p, b.data_ptr(), outs, ws.data_ptr(), stream,
+                                                 e0, e1)
+            torch.cuda.synchronize()
+            ms += [hip.elapsed_ms(a, b) for a, b in evs]
+            for a, b in evs:
+                hip.destroy(a)
+                hip.destroy(b)
+        m = float(np.median(ms))
+        res[name] = {"ms": round(m, 4), "alg_GBps": round(alg / m / 1e6, 1),
+                     "frac_of_hbm_peak": round(alg / m / 1e6 / HBM_PEAK_GBPS, 4)}
+    del bufs, pristine
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -212,7 +269,7 @@ def main():
         p.dtype, p.reduction = dt, L.REDUCTIONS[red]
         p.target = t.data_ptr()
         p.class_weight = None if wt is None else wt.data_ptr()
-        p.ignore_index, p.label_smoothing, p.reserved = -100, wl.label_smoothing, 0
+        p.ignore_index, p.label_smoothing, p.flags = -100, wl.label_smoothing, 0
         p.softcap, p.z_loss = softcap, z_loss
         return p
 
@@ -339,6 +396,7 @@ def main():
             "backward_ms": round(t_bwd, 4),
             "backward_GBps": round((n_valid + wl.BT) * shard_row / t_bwd / 1e6, 1),
             "rank_kernels_ms": round(t_stats + t_merge + t_bwd, 4)}
+        extra["fused_long_rows"] = long_rows_mode(L, W, hip, dev, stream, K)
         extra[f"fused_softcap{CAP:g}_zloss{ZL:g}"] = {
             "ms_per_step": round(wcap / K * 1e3, 4),
             "rows_per_s": round(wl.BT * K / wcap, 1),

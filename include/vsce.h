@@ -93,12 +93,21 @@ enum {
 /* fp32 per row of a vocab-parallel shard record (ce_forward_stats_partial). */
 #define VSCE_PARTIAL_STRIDE 8
 
+/* vsce_problem.flags: in the fused forward, rows too long for the on-chip
+   kernel take one launch that streams each row twice through a ring of LDS
+   stages (direct-to-LDS loads), instead of the default two launches (the
+   statistics kernel, then the gradient kernel in place).  Only rows on
+   16-byte vectors without class weights can; the others keep the default. */
+#define VSCE_FLAG_LONG_ROWS_RING 1u
+
 /*
  * Workspace: caller-allocated device memory of vsce_workspace_bytes(rows)
  * bytes, 256-byte aligned.  Its first 256 bytes are a header the forward
  * writes and the backward reads (so a forward and its backward must get the
- * same workspace); its contents need no initialisation.  Header fields, at
- * these byte offsets:
+ * same workspace); after it come per-row scratch arrays (row losses,
+ * accuracies, z-losses, and the statistics of the fused mode's rows that are
+ * too long for the chip).  Its contents need no initialisation.  Header
+ * fields, at these byte offsets:
  */
 #define VSCE_WS_W 0          /* double: W, target-weight sum over valid rows  */
 #define VSCE_WS_SUM_W 8      /* double: class-weight sum (vocab if unweighted) */
@@ -140,6 +149,9 @@ size_t vsce_workspace_bytes(int64_t rows);
  *                  section).  It is not multiplied by class weights, and the
  *                  mean reduction divides it by the number of valid rows
  *                  (the cross-entropy part keeps W).  0: off.
+ *  flags           0 or VSCE_FLAG_LONG_ROWS_RING (a choice of kernels for the
+ *                  fused forward, see ce_forward_fused_inplace); other bits
+ *                  are rejected.
  *  vocab_offset    for one shard of a vocab-parallel layout (TransformerEngine
  *                  PR #2325, dist_process_group): the global column of this
  *  vocab_total     buffer's first column, and the full vocabulary size V
@@ -163,7 +175,7 @@ typedef struct vsce_problem {
   float label_smoothing;
   float softcap;
   float z_loss;
-  int32_t reserved; /* must be 0 */
+  uint32_t flags;   /* 0, or VSCE_FLAG_LONG_ROWS_RING */
   int64_t vocab_offset;
   int64_t vocab_total;
 } vsce_problem;
@@ -198,6 +210,12 @@ typedef struct vsce_outputs {
  * for sum and none.  Ignored and bad-target rows are overwritten with zeros.
  * Columns in [vocab, row_stride) are neither read nor written.  Apply a
  * grad_output other than 1 afterwards with ce_scale_grad.
+ * Rows of at most 32768 16-byte vectors (bf16 / fp16 vocab <= 262144, fp32
+ * vocab <= 131072) are held on chip: one read and one write.  Longer rows,
+ * and rows not on 16-byte vectors, are read twice: the statistics kernel
+ * saves (m, d', x[y], S) in the workspace and the gradient kernel writes in
+ * place (two launches), or, with VSCE_FLAG_LONG_ROWS_RING, one launch streams
+ * each row twice through an LDS ring.
  */
 int ce_forward_fused_inplace(const vsce_problem *problem, void *logits_inout,
                              const vsce_outputs *out, void *workspace,
@@ -206,9 +224,9 @@ int ce_forward_fused_inplace(const vsce_problem *problem, void *logits_inout,
 /*
  * Measurement variant of ce_forward_fused_inplace: identical work, plus
  * hipEventRecord(begin) and hipEventRecord(end) on `stream` immediately
- * before and after the launch of the row kernel (not the normalizer and
- * reduction launches around it), so that the caller can time that kernel
- * alone with hipEventElapsedTime.  The events are created and owned by the
+ * before and after the launch of the row kernel (both launches for rows read
+ * twice; not the normalizer and reduction launches around them), so that the
+ * caller can time the row work alone with hipEventElapsedTime.  The events are created and owned by the
  * caller; either may be NULL.  Returns VSCE_ERR_LAUNCH if recording fails.
  */
 int ce_forward_fused_inplace_timed(const vsce_problem *problem, void *logits_inout,

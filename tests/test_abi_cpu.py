@@ -40,18 +40,20 @@ def test_version_and_workspace_size():
     assert L.vsce_version() >= 200
     assert L.vsce_workspace_bytes(-1) == 0
     assert L.vsce_workspace_bytes(0) == L.WS_HEADER_BYTES
-    # header, then [rows] fp32 scratch for row losses, accuracies and z-losses
-    assert L.vsce_workspace_bytes(1) == L.WS_HEADER_BYTES + 3 * 256
-    assert L.vsce_workspace_bytes(8192) == L.WS_HEADER_BYTES + 3 * 8192 * 4
+    # header, then [rows] fp32 scratch for row losses, accuracies and z-losses,
+    # and [rows] float4 statistics of the fused mode's rows read twice
+    assert L.vsce_workspace_bytes(1) == L.WS_HEADER_BYTES + 4 * 256
+    assert L.vsce_workspace_bytes(8192) == L.WS_HEADER_BYTES + 3 * 8192 * 4 + 8192 * 16
 
 
 def test_header_constants_match_the_binding():
     text = open(HEADER).read()
     defines = {m.group(1): int(m.group(2), 0)
-               for m in re.finditer(r"^#define\s+VSCE_(\w+)\s+(\w+)", text, flags=re.M)
-               if re.fullmatch(r"0x[0-9a-fA-F]+|\d+", m.group(2))}
+               for m in re.finditer(r"^#define\s+VSCE_(\w+)\s+(0x[0-9a-fA-F]+|\d+)u?\b", text,
+                                    flags=re.M)}
     for name in ("WS_W", "WS_SUM_W", "WS_N_VALID", "WS_N_INVALID", "WS_STATUS", "WS_INV_W",
-                 "WS_INV_N_VALID", "WS_HEADER_BYTES", "STATS_STRIDE", "PARTIAL_STRIDE"):
+                 "WS_INV_N_VALID", "WS_HEADER_BYTES", "STATS_STRIDE", "PARTIAL_STRIDE",
+                 "FLAG_LONG_ROWS_RING"):
         assert defines[name] == getattr(L, name), name
 
 
@@ -60,7 +62,7 @@ def test_struct_layout_matches_the_header():
     assert L.Problem.label_smoothing.offset == 56
     assert L.Problem.softcap.offset == 60
     assert L.Problem.z_loss.offset == 64
-    assert L.Problem.reserved.offset == 68
+    assert L.Problem.flags.offset == 68
     assert L.Problem.vocab_offset.offset == 72
     assert L.Problem.vocab_total.offset == 80
     assert ctypes.sizeof(L.Outputs) == 40
@@ -79,7 +81,7 @@ def _problem(**kw):
     p.rows, p.vocab, p.row_stride = 8, 64, 64
     p.dtype, p.reduction = L.BF16, L.REDUCTION_MEAN
     p.target, p.class_weight = FAKE, None
-    p.ignore_index, p.label_smoothing, p.reserved = -100, 0.0, 0
+    p.ignore_index, p.label_smoothing, p.flags = -100, 0.0, 0
     p.softcap, p.z_loss = 0.0, 0.0
     p.vocab_offset, p.vocab_total = 0, 0
     for k, v in kw.items():
@@ -106,7 +108,8 @@ def _stats(p, stats=FAKE, logits=FAKE, ws=FAKE):
 
 @pytest.mark.parametrize("field,value", [
     ("rows", -1), ("vocab", 0), ("vocab", -3), ("row_stride", 63), ("dtype", 3), ("dtype", -1),
-    ("reduction", 3), ("reserved", 1), ("label_smoothing", -0.1), ("label_smoothing", 1.5),
+    ("reduction", 3), ("flags", 2), ("flags", 0x80000001), ("label_smoothing", -0.1),
+    ("label_smoothing", 1.5),
     ("label_smoothing", float("nan")), ("target", None),
     ("softcap", -1.0), ("softcap", float("nan")), ("softcap", float("inf")),
     ("z_loss", -1e-4), ("z_loss", float("nan")), ("z_loss", float("inf")),

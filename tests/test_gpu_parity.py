@@ -45,12 +45,13 @@ def _go_tensor(go, reduction, rows, dev):
 
 
 def run(wl, mode, reduction, go, accuracy=False, row_stride=None, check_rows=None,
-        x_host=None, tgt=None, inplace_backward=False, softcap=0.0, z_loss=0.0):
+        x_host=None, tgt=None, inplace_backward=False, softcap=0.0, z_loss=0.0,
+        long_rows_ring=False):
     """Runs one forward + backward through the C ABI and returns GPU results
     (host copies) next to the oracle's."""
     dev = _dev()
     _note(f"{wl.name} BT={wl.BT} V={wl.V} {wl.dtype} mode={mode} red={reduction} go={go} "
-          f"stride={row_stride} softcap={softcap} z_loss={z_loss}")
+          f"stride={row_stride} softcap={softcap} z_loss={z_loss} ring={long_rows_ring}")
     feat = dict(softcap=softcap, z_loss=z_loss)
     tgt = W.targets(wl) if tgt is None else tgt
     w = W.class_weights(wl)
@@ -67,7 +68,8 @@ def run(wl, mode, reduction, go, accuracy=False, row_stride=None, check_rows=Non
     go_t = _go_tensor(go, reduction, wl.BT, dev)
     if mode == "fused":
         res = vf.forward_fused_inplace(x, t, wt, -100, eps, reduction, row_loss=True,
-                                       accuracy=accuracy, return_z_loss=True, **feat)
+                                       accuracy=accuracy, return_z_loss=True,
+                                       long_rows_ring=long_rows_ring, **feat)
         vf.scale_grad(x, go_t, reduction)
         g = x
         stats = None
@@ -471,6 +473,72 @@ def test_every_resident_shape(V):
     (130560) and the headline row length (128256)."""
     wl = _small("llm_head", 9, V - 8 if V > 8 else V)
     out, xh, tgt, w = run(wl, "fused", "mean", 1.0, accuracy=True)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0), xh, tgt, w)
+
+
+# ---------------------------------------------------------------- rows longer than the chip
+# Fused rows past the largest on-chip shape (32768 vectors), and rows off
+# 16-byte vectors, are read twice: by default the statistics kernel and the
+# gradient kernel in place; with VSCE_FLAG_LONG_ROWS_RING, rows on 16-byte
+# vectors without class weights take the one-launch LDS ring instead (the
+# others keep the default).
+
+RING = pytest.mark.parametrize("ring", [False, True], ids=["pair", "ring"])
+
+
+@RING
+@pytest.mark.parametrize("V,dtype", [(262152, "bf16"), (300000, "bf16"), (262152, "f16"),
+                                     (131080, "f32")])
+@pytest.mark.parametrize("reduction,go", [("mean", 1.0), ("none", 0.37)])
+def test_long_rows(V, dtype, reduction, go, ring):
+    """Just past the largest on-chip shape (one vector in the last stage),
+    and a longer row; ignored rows, smoothing, accuracy."""
+    wl = _small("llm_head", 10, V, dtype=dtype, ignore_frac=0.2)
+    out, xh, tgt, w = run(wl, "fused", reduction, go, accuracy=True, long_rows_ring=ring)
+    check(wl, out, reference(wl, xh, tgt, w, reduction, go), xh, tgt, w)
+
+
+@RING
+def test_long_rows_softcap_z_loss(ring):
+    wl = _small("llm_head", 8, 270000, ignore_frac=0.1)
+    kw = dict(softcap=30.0, z_loss=1e-4)
+    out, xh, tgt, w = run(wl, "fused", "mean", 1.0, accuracy=True, long_rows_ring=ring, **kw)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0, **kw), xh, tgt, w)
+
+
+@RING
+def test_long_rows_maximum_tied_everywhere(ring):
+    """Rows whose maximum sits in many lanes' shares (every 97th column), one
+    row constant (every element is the maximum), one with its target at the
+    first copy: the shares of all owning lanes are re-read and summed."""
+    wl = _small("llm_head", 4, 262152, ignore_frac=0.0, label_smoothing=0.0)
+    tgt = W.targets(wl)
+    xh = W.logits(wl, tgt).clone()
+    xh[0, ::97] = 12.0
+    xh[1, :] = 1.5
+    xh[2, 5::97] = 12.0
+    tgt[2] = 5
+    out, xh, tgt, w = run(wl, "fused", "mean", 1.0, accuracy=True, x_host=xh, tgt=tgt,
+                          long_rows_ring=ring)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0), xh, tgt, w)
+    assert out["acc"][2] == 1.0  # the first copy of the maximum is the target
+
+
+@RING
+@pytest.mark.parametrize("wl_name,V", [("weighted", 262152), ("llm_head", 262153),
+                                       ("llm_head", 65541)])
+def test_long_rows_weighted_or_off_vectors(wl_name, V, ring):
+    """Class weights, and rows off 16-byte vectors (long and short): the pair
+    whether or not the ring is asked for."""
+    wl = _small(wl_name, 6, V, ignore_frac=0.2)
+    red = "sum" if wl.weighted else "mean"
+    out, xh, tgt, w = run(wl, "fused", red, 0.5, long_rows_ring=ring)
+    check(wl, out, reference(wl, xh, tgt, w, red, 0.5), xh, tgt, w)
+
+
+def test_ring_flag_leaves_rows_that_fit_on_chip():
+    wl = _small("llm_head", 12, 128256)
+    out, xh, tgt, w = run(wl, "fused", "mean", 1.0, accuracy=True, long_rows_ring=True)
     check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0), xh, tgt, w)
 
 

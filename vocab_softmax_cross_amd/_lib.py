@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import c_float, c_int32, c_int64, c_size_t, c_void_p
+from ctypes import c_float, c_int32, c_int64, c_size_t, c_uint32, c_void_p
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libvsce.so")
@@ -22,6 +22,7 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_LAUNCH = 0, -1, -2, -3
 STATUS_BAD_TARGET = 1
 STATS_STRIDE = 4
 PARTIAL_STRIDE = 8
+FLAG_LONG_ROWS_RING = 1
 WS_W, WS_SUM_W, WS_N_VALID, WS_N_INVALID, WS_STATUS, WS_HEADER_BYTES = 0, 8, 16, 24, 32, 256
 WS_INV_W, WS_INV_N_VALID = 40, 44
 
@@ -44,7 +45,7 @@ class Problem(ctypes.Structure):
         ("label_smoothing", c_float),
         ("softcap", c_float),
         ("z_loss", c_float),
-        ("reserved", c_int32),
+        ("flags", c_uint32),
         ("vocab_offset", c_int64),
         ("vocab_total", c_int64),
     ]

@@ -36,7 +36,7 @@ int check_problem(const vsce_problem* pb, const void* logits, Prob& p) {
   if (pb->rows < 0 || pb->vocab < 1 || pb->row_stride < pb->vocab) return VSCE_ERR_INVALID;
   if (pb->reduction < VSCE_REDUCTION_NONE || pb->reduction > VSCE_REDUCTION_SUM)
     return VSCE_ERR_INVALID;
-  if (pb->reserved != 0) return VSCE_ERR_INVALID;
+  if ((pb->flags & ~VSCE_FLAG_LONG_ROWS_RING) != 0) return VSCE_ERR_INVALID;
   const float eps = pb->label_smoothing;
   if (!(eps >= 0.0f && eps <= 1.0f)) return VSCE_ERR_INVALID;  // also rejects NaN
   const float cap = pb->softcap, zl = pb->z_loss;
@@ -67,6 +67,7 @@ int check_problem(const vsce_problem* pb, const void* logits, Prob& p) {
   p.cap = cap;
   p.zl = zl;
   p.elem_bytes = eb;
+  p.flags = pb->flags;
   const int vec = 16 / eb;
   p.vec_ok = aligned(logits, 16) && (pb->row_stride * eb) % 16 == 0 && pb->vocab % vec == 0 &&
              (!pb->class_weight || aligned(pb->class_weight + voff, 16));
@@ -105,9 +106,13 @@ void problem_args(const Prob& p, RowArgs& a) {
   a.rows = p.rows;
 }
 
-// Per-row destinations of the forward kernels.  The workspace holds, after
-// its header, [rows] scratch for the row losses, the accuracies and the
-// z-losses (each used when the caller's outputs do not take its place).
+// The workspace after its header: [rows] fp32 scratch for the row losses, the
+// accuracies and the z-losses (each used when the caller's outputs do not take
+// its place), then [rows] float4 statistics (the fused mode's rows that are
+// read twice).
+int64_t stats_scratch_offset(int64_t rows) { return VSCE_WS_HEADER_BYTES + 3 * align_up(4 * rows); }
+
+// Per-row destinations of the forward kernels.
 RowArgs row_args(const Prob& p, void* x, const vsce_outputs* out, void* workspace) {
   RowArgs a = {};
   char* ws = static_cast<char*>(workspace);
@@ -144,7 +149,22 @@ int forward_common(const Prob& p, RowArgs a, const vsce_outputs* out, void* work
   if (p.rows > 0) {
     if (fused) {
       rc = launch_fused_resident(p, a, stream);
-      if (rc == VSCE_ERR_UNSUPPORTED) rc = launch_fused_stream(p, a, stream);
+      if (rc == VSCE_ERR_UNSUPPORTED && (p.flags & VSCE_FLAG_LONG_ROWS_RING))
+        rc = launch_fused_ring(p, a, stream);
+      if (rc == VSCE_ERR_UNSUPPORTED) {
+        // Rows read twice: the statistics into the workspace, then the
+        // gradient in place (grad_output 1).
+        a.stats = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           stats_scratch_offset(p.rows));
+        rc = launch_stats(p, a, stream);
+        if (rc == VSCE_OK) {
+          RowArgs b = a;
+          b.g = a.x;
+          b.go = nullptr;
+          b.go_stride = 0;
+          rc = launch_backward(p, b, stream);
+        }
+      }
     } else {
       rc = launch_stats(p, a, stream);
     }
@@ -196,8 +216,9 @@ int stream_any(int which, const Prob& p, const RowArgs& a, hipStream_t s) {
 int launch_stats(const Prob& p, RowArgs a, hipStream_t s) {
   return stream_any(kStreamStats, p, a, s);
 }
-int launch_fused_stream(const Prob& p, RowArgs a, hipStream_t s) {
-  return stream_any(kStreamFused, p, a, s);
+int launch_fused_ring(const Prob& p, RowArgs a, hipStream_t s) {
+  if (!p.vec_ok || p.weight) return VSCE_ERR_UNSUPPORTED;
+  return stream_any(kStreamRing, p, a, s);
 }
 int launch_backward(const Prob& p, RowArgs a, hipStream_t s) {
   return stream_any(kStreamBackward, p, a, s);
@@ -214,7 +235,7 @@ extern "C" {
 
 size_t vsce_workspace_bytes(int64_t rows) {
   if (rows < 0) return 0;
-  return static_cast<size_t>(VSCE_WS_HEADER_BYTES + 3 * align_up(4 * rows));
+  return static_cast<size_t>(stats_scratch_offset(rows) + align_up(16 * rows));
 }
 
 int ce_forward_fused_inplace(const vsce_problem* problem, void* logits_inout,
@@ -353,6 +374,6 @@ const char* vsce_strerror(int code) {
   }
 }
 
-int vsce_version(void) { return 200; }
+int vsce_version(void) { return 300; }
 
 }  // extern "C"

@@ -30,6 +30,7 @@ struct Prob {
   float zl;        // z-loss lambda (0: off)
   int elem_bytes;
   bool vec_ok;     // rows start 16-byte aligned and V fills whole 16-byte vectors
+  uint32_t flags;  // VSCE_FLAG_* bits
 };
 
 // Arguments of every per-row kernel (passed by value).
@@ -56,7 +57,7 @@ struct RowArgs {
   float* z_rows;        // [rows] per-row z-loss, or null
   float* stats;         // [rows][4] or null
   float* partial;       // [rows][8] shard records (partial statistics mode), or null
-  const float* go;      // grad_output (backward / scale)
+  const float* go;      // grad_output (backward / scale); null: 1.0 (backward)
   int64_t go_stride;    // 0 (scalar) or 1 (per row)
   int skip_if_one;
   int64_t rows;
@@ -75,11 +76,13 @@ int launch_fused_resident(const Prob& p, RowArgs a, hipStream_t s);
 template <int DT, bool CAP>
 int fused_resident_dt(const Prob& p, const RowArgs& a, hipStream_t s);
 // Streaming kernels by element type; `which` is kStreamStats .. kStreamScale.
-enum { kStreamStats = 0, kStreamFused = 1, kStreamBackward = 2, kStreamScale = 3 };
+enum { kStreamStats = 0, kStreamRing = 1, kStreamBackward = 2, kStreamScale = 3 };
 template <int DT, bool CAP>
 int stream_dt(int which, const Prob& p, const RowArgs& a, hipStream_t s);
-// Any row length: the row is streamed twice (statistics, then gradient).
-int launch_fused_stream(const Prob& p, RowArgs a, hipStream_t s);
+// Fused, one launch, any row length on 16-byte vectors without class
+// weights: the row is streamed twice (statistics, then gradient) through an
+// LDS ring.  VSCE_ERR_UNSUPPORTED for other rows.
+int launch_fused_ring(const Prob& p, RowArgs a, hipStream_t s);
 // Split forward: one logits read, statistics + loss.
 int launch_stats(const Prob& p, RowArgs a, hipStream_t s);
 // Split backward: logits read + gradient write from the saved statistics.

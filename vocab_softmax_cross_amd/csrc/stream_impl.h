@@ -10,9 +10,12 @@
 //  scale_kernel      in-place grad_output scale of a saved gradient
 //                    (linkedin#1290 commit message; SKIP_IF_ONE of Liger-Kernel
 //                    PR #1622): returns at once where grad_output == 1.0.
-//  fused_stream_kernel  fused forward + gradient for rows too long to keep on
-//                    chip: the statistics pass, then the gradient pass reading
-//                    the row a second time.
+//  fused_ring_kernel fused forward + gradient in one launch for rows too long
+//                    to keep on chip: the statistics pass, then the gradient
+//                    pass reading the row a second time, both fed through a
+//                    ring of LDS stages filled by direct-to-LDS loads (16-byte
+//                    vector path, no class weights).  The default for such
+//                    rows is the stats_kernel + backward_kernel pair in place.
 //
 // Each thread keeps an online (max, sum) pair per lane: a batch of U vectors
 // raises the lane max once and rescales the sum once.  After the workgroup
@@ -74,57 +77,24 @@ struct Grp {
   }
 };
 
-// Per-row statistics by streaming: returns (M, d', S, first) on every thread,
-// M being the (capped) maximum the loss reads, and the maximum of the stored
-// logits in *Mraw_out.  Must be called by the whole workgroup (it contains
-// barriers).
-template <int DT, int NT, int U, bool WEIGHTED, bool VECP, bool CAP>
-__device__ inline void stream_stats(const RowArgs& a, const char* row, float& M_out,
-                                    float& dp_out, float& S_out, int& first_out, float* red_max,
-                                    float4* red_sum, float* Mraw_out = nullptr) {
+// The end of a row's statistics, once every lane holds its online (m, s, S)
+// over its share of the row (m the lane's maximum of the stored logits, s the
+// sum of exp(capped(x) - capped(m)) over its elements, S its logit sum):
+// returns (M, d', S, first) on every thread, M being the (capped) maximum the
+// loss reads, and the maximum of the stored logits in *Mraw_out (if given).
+// Lane t's share must be the groups t, t + NT, t + 2 NT, ... below a.nvec:
+// the owners' shares are re-read in that layout.  Must be called by the whole
+// workgroup (it contains barriers).
+template <int DT, int NT, bool VECP, bool CAP>
+__device__ inline void finish_stats(const RowArgs& a, const char* row, float m, float s, float S,
+                                    float& M_out, float& dp_out, float& S_out, int& first_out,
+                                    float* red_max, float4* red_sum, float* Mraw_out) {
   using G = Grp<DT, VECP>;
   constexpr int E = G::E;
   const int tid = threadIdx.x;
   const int64_t ng = a.nvec;
   const SoftCap cap{a.cap, a.cap_k};
   auto capped = [&](float v) { return CAP ? cap.value(v) : v; };
-  float m = -__builtin_inff(), s = 0.0f, S = 0.0f;
-
-  for (int64_t g0 = 0; g0 < ng; g0 += static_cast<int64_t>(NT) * U) {
-    float f[U][E];
-    bool ok[U];
-    static_for<U>([&](auto u) {
-      const int64_t g = g0 + u * NT + tid;
-      ok[u] = g < ng;
-      if (ok[u]) G::load(row, g, f[u]);
-    });
-    float bm = -__builtin_inff();
-    static_for<U>([&](auto u) {
-      if (ok[u]) {
-#pragma unroll
-        for (int i = 0; i < E; ++i) bm = fmaxf(bm, f[u][i]);
-      }
-    });
-    if (bm > m) {
-      s *= __builtin_amdgcn_exp2f((capped(m) - capped(bm)) * kLog2e);
-      m = bm;
-    }
-    const float ML = (m == -__builtin_inff()) ? 0.0f : capped(m) * kLog2e;
-    static_for<U>([&](auto u) {
-      if (ok[u]) {
-        float wv[E];
-        if constexpr (WEIGHTED) G::weights(a.weight, g0 + u * NT + tid, wv);
-#pragma unroll
-        for (int i = 0; i < E; ++i) {
-          const float fc = capped(f[u][i]);
-          s += exp_shifted(fc, ML);
-          if constexpr (WEIGHTED) S = __builtin_fmaf(wv[i], fc, S);
-          else S += fc;
-        }
-      }
-    });
-  }
-
   const float M = block_max<NT>(m, red_max);     // of the stored logits
   const float Mc = capped(M);                    // of the logits the loss reads
   const float ML = (M == -__builtin_inff()) ? 0.0f : Mc * kLog2e;
@@ -182,6 +152,61 @@ __device__ inline void stream_stats(const RowArgs& a, const char* row, float& M_
   dp_out = rs.s + static_cast<float>(rs.cnt - 1);
   S_out = rs.S;
   first_out = rs.first;
+}
+
+// Per-row statistics by streaming: returns (M, d', S, first) on every thread,
+// M being the (capped) maximum the loss reads, and the maximum of the stored
+// logits in *Mraw_out.  Must be called by the whole workgroup (it contains
+// barriers).
+template <int DT, int NT, int U, bool WEIGHTED, bool VECP, bool CAP>
+__device__ inline void stream_stats(const RowArgs& a, const char* row, float& M_out,
+                                    float& dp_out, float& S_out, int& first_out, float* red_max,
+                                    float4* red_sum, float* Mraw_out = nullptr) {
+  using G = Grp<DT, VECP>;
+  constexpr int E = G::E;
+  const int tid = threadIdx.x;
+  const int64_t ng = a.nvec;
+  const SoftCap cap{a.cap, a.cap_k};
+  auto capped = [&](float v) { return CAP ? cap.value(v) : v; };
+  float m = -__builtin_inff(), s = 0.0f, S = 0.0f;
+
+  for (int64_t g0 = 0; g0 < ng; g0 += static_cast<int64_t>(NT) * U) {
+    float f[U][E];
+    bool ok[U];
+    static_for<U>([&](auto u) {
+      const int64_t g = g0 + u * NT + tid;
+      ok[u] = g < ng;
+      if (ok[u]) G::load(row, g, f[u]);
+    });
+    float bm = -__builtin_inff();
+    static_for<U>([&](auto u) {
+      if (ok[u]) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) bm = fmaxf(bm, f[u][i]);
+      }
+    });
+    if (bm > m) {
+      s *= __builtin_amdgcn_exp2f((capped(m) - capped(bm)) * kLog2e);
+      m = bm;
+    }
+    const float ML = (m == -__builtin_inff()) ? 0.0f : capped(m) * kLog2e;
+    static_for<U>([&](auto u) {
+      if (ok[u]) {
+        float wv[E];
+        if constexpr (WEIGHTED) G::weights(a.weight, g0 + u * NT + tid, wv);
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const float fc = capped(f[u][i]);
+          s += exp_shifted(fc, ML);
+          if constexpr (WEIGHTED) S = __builtin_fmaf(wv[i], fc, S);
+          else S += fc;
+        }
+      }
+    });
+  }
+
+  finish_stats<DT, NT, VECP, CAP>(a, row, m, s, S, M_out, dp_out, S_out, first_out, red_max,
+                                  red_sum, Mraw_out);
 }
 
 // Writes the gradient of one row segment [g_begin, g_end) of groups, with
@@ -309,42 +334,163 @@ __global__ __launch_bounds__(NT) void stats_kernel(const RowArgs a) {
   }
 }
 
-template <int DT, int NT, int U, bool WEIGHTED, bool VECP, bool CAP>
-__global__ __launch_bounds__(NT) void fused_stream_kernel(const RowArgs a) {
+// ---------------------------------------------------------------- LDS ring
+// Waits until at most N vector-memory operations of this wavefront are still
+// outstanding.  The counter covers loads (those into LDS too) and stores, and
+// they leave it in the order they were issued.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "the counter holds 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16 bytes from LDS, complete on return.  The read is opaque to the compiler
+// (no wait for the direct-to-LDS loads it cannot tell apart), and it has
+// finished before the caller refills the slot.
+__device__ __forceinline__ uint4 lds_read16_now(const uint4* p) {
+  const uint32_t addr = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint4*)p));
+  u32x4_t v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Keeps the compiler from moving memory operations across this point, so the
+// order of loads and stores the wait counts assume is the issue order.
+__device__ __forceinline__ void issue_order() { asm volatile("" ::: "memory"); }
+
+// Fused forward + in-place gradient for rows too long to keep on chip, on the
+// 16-byte vector path without class weights: the statistics pass, then the
+// gradient pass, each fed through a ring of LDS stages.  Each wavefront owns
+// NS slots of 64 x 16 bytes and keeps its next NS stages in flight as
+// direct-to-LDS loads (buffer_load_dwordx4 ... lds) while it works on the
+// current one: the multi-stage, prologue-prefetched load ring that the
+// linkedin#1290 commit message (Liger-Kernel PR #1268, "Source of the gains vs
+// Triton", item 1) credits for hiding HBM latency, here without the register
+// cost of holding the stages in flight.  The gradient pass also keeps its
+// stores off the critical path: the wait for stage k counts exactly the loads
+// and stores issued after it, so the stores of the last NS stages stay in
+// flight (a wait on a load would otherwise also wait for every older store).
+//
+// Stage k of wavefront w holds vectors (k NW + w) 64 + lane, so thread t holds
+// vectors t, t + NT, t + 2 NT, ... as finish_stats expects.  Stages past the
+// row (the last stages of some wavefronts, and the NS stages each pass loads
+// beyond its end) are dropped by the buffer range check: no memory is read.
+template <int DT, int NT, int NS, bool CAP>
+__global__ __launch_bounds__(NT) void fused_ring_kernel(const RowArgs a) {
   using D = Dt<DT>;
-  __shared__ float red_max[NT / kWave];
-  __shared__ float4 red_sum[NT / kWave];
+  constexpr int E = D::VEC;
+  constexpr int NW = NT / kWave;
+  static_assert((NS & (NS - 1)) == 0 && 2 * NS - 1 <= 63, "NS: a power of 2, at most 32");
+  __shared__ uint4 ring[NW * NS * kWave];
+  __shared__ float red_max[NW];
+  __shared__ float4 red_sum[NW];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = uniform(tid / kWave);
   const int64_t n = xcd_contiguous(blockIdx.x, a.rows);
   char* row = static_cast<char*>(a.x) + n * a.stride * D::BYTES;
+  const auto rsrc = make_rsrc(row, static_cast<uint32_t>(a.V * D::BYTES));
   const int64_t y = a.target[n];
   const int cls = row_class(y, a.Vt, a.ignore_index);
   if (cls != kValid) {
-    stream_zero<DT, VECP>(row, 0, a.nvec, NT, U);
+    stream_zero<DT, true>(row, 0, a.nvec, NT, 1);
     const float l = (cls == kIgnored) ? 0.0f : __builtin_nanf("");
-    if (threadIdx.x == 0) store_row(a, n, l, 0.0f, l);
+    if (tid == 0) store_row(a, n, l, 0.0f, l);
     return;
   }
-  float M, dp, S;
+  const int nvec = static_cast<int>(a.nvec);
+  const int stages = (nvec + NT - 1) / NT;
+  uint4* const mine = ring + wave * NS * kWave;
+  auto slot = [&](int k) { return mine + (k & (NS - 1)) * kWave; };
+  auto vec = [&](int k) { return (k * NW + wave) * kWave + lane; };
+  auto fetch = [&](int k) {
+    buf_load16_lds(rsrc, slot(k), static_cast<uint32_t>(vec(k)) * 16u, 0);
+  };
+  const SoftCap cap{a.cap, a.cap_k};
+  auto capped = [&](float v) { return CAP ? cap.value(v) : v; };
+
+  // ---- pass 1: online (max, sum, logit sum) per lane
+  float m = -__builtin_inff(), s = 0.0f, S = 0.0f;
+  for (int k = 0; k < NS; ++k) fetch(k);
+  for (int k = 0; k < stages; ++k) {
+    wait_vm<NS - 1>();  // stage k has landed; NS - 1 later loads may not have
+    const uint4 v = lds_read16_now(slot(k) + lane);
+    fetch(k + NS);
+    issue_order();
+    if (vec(k) < nvec) {
+      float f[E];
+      D::unpack(v, f);
+      float bm = f[0];
+#pragma unroll
+      for (int i = 1; i < E; ++i) bm = fmaxf(bm, f[i]);
+      if (bm > m) {
+        s *= __builtin_amdgcn_exp2f((capped(m) - capped(bm)) * kLog2e);
+        m = bm;
+      }
+      const float ML = (m == -__builtin_inff()) ? 0.0f : capped(m) * kLog2e;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const float fc = capped(f[i]);
+        s += exp_shifted(fc, ML);
+        S += fc;
+      }
+    }
+  }
+  wait_vm<0>();  // the loads past the end write their (empty) slots too
+
+  float M, dp, Sr;
   int first;
-  stream_stats<DT, NT, U, WEIGHTED, VECP, CAP>(a, row, M, dp, S, first, red_max, red_sum);
+  finish_stats<DT, NT, true, CAP>(a, row, m, s, S, M, dp, Sr, first, red_max, red_sum, nullptr);
   const float xs = D::load1(row, y);
-  const float xy = CAP ? SoftCap{a.cap, a.cap_k}.value(xs) : xs;
+  const float xy = CAP ? cap.value(xs) : xs;
   const float sum_w = static_cast<float>(a.ws->sum_w);
-  const float wy = row_weight(a, y, WEIGHTED);
   const float lg = log1pf(dp);
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     const float zrow = row_z(M, lg, a.zl);
-    store_row(a, n, row_loss(M, lg, xy, S, wy, sum_w, a.eps, a.eta) + zrow,
+    store_row(a, n, row_loss(M, lg, xy, Sr, 1.0f, sum_w, a.eps, a.eta) + zrow,
               (static_cast<int64_t>(first) == y) ? 1.0f : 0.0f, zrow);
   }
-  // Every thread has read x[y] before any thread overwrites it: the block
-  // reduction inside stream_stats ended with a barrier, and x[y] is re-read
-  // here, so order the read before the first store of the gradient pass.
-  __syncthreads();
   const float sigma = a.mean ? a.ws->inv_W : 1.0f;
-  RowTerms t = row_terms(M, dp, lg, xy, wy, sum_w, a.eps, a.eta, sigma, a.zl, z_sigma(a));
+  RowTerms t = row_terms(M, dp, lg, xy, 1.0f, sum_w, a.eps, a.eta, sigma, a.zl, z_sigma(a));
   t.dxy *= cap_slope<CAP>(a, xs);
-  stream_grad<DT, NT, U, WEIGHTED, VECP, CAP>(a, row, row, 0, a.nvec, t, y);
+  // Every thread has its x[y] (used above) before any thread overwrites the
+  // row.
+  __syncthreads();
+
+  // ---- pass 2: the gradient, stage by stage, stored over the logits
+  const int jy = static_cast<int>(y / E);  // vector, stage and thread holding column y
+  const int ky = jy / NT, ty = jy % NT, iy = static_cast<int>(y % E);
+  for (int k = 0; k < NS; ++k) fetch(k);
+  for (int k = 0; k < stages; ++k) {
+    // Issued after stage k: the rest of the prologue and two operations per
+    // earlier iteration (at least NS - 1 while k < NS), or stage k's own
+    // iteration's store and two per later one (exactly 2 NS - 1).
+    if (k < NS) wait_vm<NS - 1>();
+    else wait_vm<2 * NS - 1>();
+    const uint4 v = lds_read16_now(slot(k) + lane);
+    fetch(k + NS);
+    issue_order();
+    float f[E];
+    D::unpack(v, f);
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      if constexpr (CAP) {
+        float slope;
+        const float fc = cap.value(f[i], slope);
+        f[i] = __builtin_fmaf(exp_shifted(fc, t.ML), t.K, -t.B) * slope;
+      } else {
+        f[i] = __builtin_fmaf(exp_shifted(f[i], t.ML), t.K, -t.B);
+      }
+    }
+    if (k == ky && tid == ty) {
+#pragma unroll
+      for (int i = 0; i < E; ++i)
+        if (i == iy) f[i] = t.dxy;
+    }
+    buf_store16(rsrc, static_cast<uint32_t>(vec(k)) * 16u, 0, D::pack(f));
+    issue_order();
+  }
+  wait_vm<0>();  // no direct-to-LDS write may land after the workgroup ends
 }
 
 // Split backward over (row, column chunk) workgroups.
@@ -366,7 +512,7 @@ __global__ __launch_bounds__(NT) void backward_kernel(const RowArgs a) {
     return;
   }
   const float4 st = reinterpret_cast<const float4*>(a.stats)[n];
-  const float go = a.go[n * a.go_stride];
+  const float go = a.go ? a.go[n * a.go_stride] : 1.0f;  // null: the fused mode's pair
   const float sigma = (a.mean ? a.ws->inv_W : 1.0f) * go;
   const float sum_w = static_cast<float>(a.ws->sum_w);
   RowTerms t = row_terms(st.x, st.y, log1pf(st.y), st.z, row_weight(a, y, WEIGHTED), sum_w,
@@ -420,6 +566,10 @@ __global__ __launch_bounds__(NT) void scale_kernel(const RowArgs a) {
 
 constexpr int kStreamNT = 256;
 constexpr int kStreamU = 4;
+// The LDS ring: 256 threads, 8 stages of 1 KB per wavefront (32 KB of LDS
+// per row, five rows per CU).
+constexpr int kRingNT = 256;
+constexpr int kRingNS = 8;
 constexpr int64_t kScaleGrid = 2048;  // 8 workgroups per CU
 
 template <int DT>
@@ -435,7 +585,7 @@ int launch(K kernel, int64_t grid, int nt, const RowArgs& a, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
 }
 
-enum Which { kStats, kFusedStream, kBackward, kScale };
+enum Which { kStats, kRing, kBackward, kScale };
 
 template <int DT, bool W, bool VECP, bool CAP>
 int launch_which(Which which, const Prob& p, RowArgs a, hipStream_t s) {
@@ -445,8 +595,13 @@ int launch_which(Which which, const Prob& p, RowArgs a, hipStream_t s) {
   a.chunks = (a.nvec + per - 1) / per;
   switch (which) {
     case kStats: return launch(stats_kernel<DT, NT, U, W, VECP, CAP>, p.rows, NT, a, s);
-    case kFusedStream:
-      return launch(fused_stream_kernel<DT, NT, U, W, VECP, CAP>, p.rows, NT, a, s);
+    case kRing:
+      // The ring needs whole 16-byte vectors; per-element class weights would
+      // add loads the ring's wait counts do not cover.
+      if constexpr (VECP && !W)
+        return launch(fused_ring_kernel<DT, kRingNT, kRingNS, CAP>, p.rows, kRingNT, a, s);
+      else
+        return VSCE_ERR_UNSUPPORTED;
     case kBackward:
       return launch(backward_kernel<DT, NT, U, W, VECP, CAP>, p.rows * a.chunks, NT, a, s);
     case kScale:

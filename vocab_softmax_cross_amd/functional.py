@@ -74,7 +74,7 @@ def make_problem(x2d: torch.Tensor, target: torch.Tensor, weight: Optional[torch
     p.label_smoothing = float(label_smoothing)
     p.softcap = float(softcap)
     p.z_loss = float(z_loss)
-    p.reserved = 0
+    p.flags = 0
     p.vocab_offset = int(vocab_offset)
     p.vocab_total = int(vocab_total)
     return p
@@ -114,12 +114,15 @@ def forward_fused_inplace(logits: torch.Tensor, target: torch.Tensor,
                           label_smoothing: float = 0.0, reduction: str = "mean",
                           row_loss: bool = False, accuracy: bool = False,
                           workspace: Optional[torch.Tensor] = None, softcap: float = 0.0,
-                          z_loss: float = 0.0, return_z_loss: bool = False) -> dict:
+                          z_loss: float = 0.0, return_z_loss: bool = False,
+                          long_rows_ring: bool = False) -> dict:
     """ce_forward_fused_inplace: loss outputs; the logits buffer now holds the
-    gradient of the reduced loss for grad_output = 1."""
+    gradient of the reduced loss for grad_output = 1.  long_rows_ring sets
+    VSCE_FLAG_LONG_ROWS_RING (one launch for rows too long for the chip)."""
     x = _rows_view(logits)
     p = make_problem(x, target.reshape(-1), weight, ignore_index, label_smoothing, reduction,
                      softcap, z_loss)
+    p.flags = L.FLAG_LONG_ROWS_RING if long_rows_ring else 0
     ws = workspace if workspace is not None else workspace_for(p.rows, x.device)
     o, res = _outputs(p.rows, reduction, x.device, row_loss, accuracy, return_z_loss)
     L.ce_forward_fused_inplace(p, x.data_ptr(), o, ws.data_ptr(), _stream(x))
@@ -225,7 +228,7 @@ def merge_stats(partials: torch.Tensor, target: torch.Tensor, vocab_total: int,
     p.target = t.data_ptr() or None
     p.class_weight = None if weight is None else weight.data_ptr()
     p.ignore_index, p.label_smoothing = int(ignore_index), float(label_smoothing)
-    p.softcap, p.z_loss, p.reserved = float(softcap), float(z_loss), 0
+    p.softcap, p.z_loss, p.flags = float(softcap), float(z_loss), 0
     p.vocab_offset, p.vocab_total = 0, int(vocab_total)
     ws = workspace_for(rows, dev)
     stats = torch.empty((max(rows, 1), L.STATS_STRIDE), dtype=torch.float32, device=dev)
