@@ -283,3 +283,42 @@ def cross_entropy(x: np.ndarray, target: np.ndarray, weight: Optional[np.ndarray
         if dtype is not None:
             res.grad_rn = round_to(res.grad, dtype)
     return res
+
+
+# ---------------------------------------------------------------- FLCE
+# The linear head fused with the cross-entropy (Liger-Kernel PR #1622
+# "perf(flce): drop host syncs that do not feed the computation": the FLCE
+# forward computes the loss and both gradients; the #1554 row compaction it
+# mentions skips the projection products for ignored rows, which leaves every
+# result unchanged).  Written as the definition:
+#   z = h W^T                  (logits, [BT, V])
+#   L = cross_entropy(z)       (the oracle above)
+#   G = dL/dz                  (scaled by the reduction and grad_output)
+#   dL/dh = G W,   dL/dW = G^T h
+# in fp64 throughout, from the stored (bf16) h and W upcast exactly.
+
+@dataclass
+class FlceResult:
+    ce: Result                 # the cross-entropy of z (loss, row losses, accuracy, G)
+    logits: np.ndarray         # z = h W^T, fp64 [BT, V]
+    grad_hidden: np.ndarray    # dL/dh, fp64 [BT, H]
+    grad_weight: np.ndarray    # dL/dW, fp64 [V, H]
+
+
+def matmul_nt(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """a b^T in fp64 ([M, K] x [N, K] -> [M, N]): the library product."""
+    return np.asarray(a, np.float64) @ np.asarray(b, np.float64).T
+
+
+def flce(hidden: np.ndarray, weight: np.ndarray, target: np.ndarray,
+         class_weight: Optional[np.ndarray] = None, ignore_index: int = -100,
+         label_smoothing: float = 0.0, reduction: str = "mean", grad_output=1.0,
+         softcap: float = 0.0, z_loss: float = 0.0) -> FlceResult:
+    """Loss and gradients of cross_entropy(hidden @ weight^T) in fp64."""
+    h = np.asarray(hidden, np.float64)
+    w = np.asarray(weight, np.float64)
+    z = matmul_nt(h, w)
+    ce = cross_entropy(z, target, class_weight, ignore_index, label_smoothing, reduction,
+                       grad_output, None, True, softcap, z_loss)
+    g = ce.grad
+    return FlceResult(ce, z, g @ w, g.T @ h)

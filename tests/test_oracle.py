@@ -563,3 +563,95 @@ def test_dropping_the_summed_fourth_value_changes_it():
     stats, _ = oracle.merge(parts, t, V)
     np.testing.assert_allclose(stats[:, 3], r.stats[:, 3], rtol=1e-12)
     assert np.all(np.abs(parts[0, :, 3] - r.stats[:, 3]) > 1e-3)
+
+
+# ---------------------------------------------------------------- FLCE
+# The linear head fused with the cross-entropy (Liger-Kernel PR #1622, the
+# FLCE forward computing the loss and both gradients; #1554 compacts ignored
+# rows out of the projection products without changing any result).
+
+def _flce_problem(seed, BT, H, V, ignore_frac=0.25, weighted=False):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((BT, H))
+    W = rng.standard_normal((V, H)) / math.sqrt(H) * 3.0
+    t = rng.integers(0, V, BT).astype(np.int64)
+    t[rng.permutation(BT)[: int(round(ignore_frac * BT))]] = -100
+    cw = rng.uniform(0.5, 1.5, V) if weighted else None
+    return h, W, t, cw
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+@pytest.mark.parametrize("weighted,eps,softcap,z_loss", [(False, 0.0, 0.0, 0.0),
+                                                         (True, 0.1, 0.0, 0.0),
+                                                         (False, 0.1, 20.0, 1e-3)])
+def test_flce_matches_torch_linear_cross_entropy_autograd(reduction, weighted, eps, softcap,
+                                                          z_loss):
+    h, W, t, cw = _flce_problem(41, 20, 24, 150, weighted=weighted)
+    go = np.linspace(0.5, 1.5, 20) if reduction == "none" else 0.6
+    r = oracle.flce(h, W, t, cw, -100, eps, reduction, go, softcap, z_loss)
+    ht = torch.tensor(h, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    z = F.linear(ht, Wt)
+    zc = softcap * torch.tanh(z / softcap) if softcap > 0 else z
+    tt = torch.tensor(t)
+    valid = tt != -100
+    ce = F.cross_entropy(zc, tt, weight=None if cw is None else torch.tensor(cw),
+                         ignore_index=-100, label_smoothing=eps, reduction=reduction)
+    zr = z_loss * torch.logsumexp(zc, dim=1) ** 2 * valid
+    if reduction == "none":
+        loss = ce + zr
+        loss.backward(torch.tensor(go))
+        np.testing.assert_allclose(r.ce.loss, loss.detach().numpy(), rtol=1e-12, atol=1e-14)
+    else:
+        loss = ce + (zr.sum() / valid.sum() if reduction == "mean" else zr.sum())
+        (loss * go).backward()
+        assert r.ce.loss == pytest.approx(float(loss), rel=1e-12)
+    np.testing.assert_allclose(r.grad_hidden, ht.grad.numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(r.grad_weight, Wt.grad.numpy(), rtol=1e-10, atol=1e-14)
+
+
+def test_flce_gradients_are_finite_differences_of_the_loss():
+    h, W, t, cw = _flce_problem(42, 6, 8, 40, weighted=True)
+    kw = dict(class_weight=cw, label_smoothing=0.1, reduction="mean", softcap=10.0, z_loss=0.01)
+    r = oracle.flce(h, W, t, **kw)
+    d = 1e-5
+    for (i, j) in [(0, 0), (2, 5), (5, 7)]:
+        hp, hm = h.copy(), h.copy()
+        hp[i, j] += d
+        hm[i, j] -= d
+        fd = (oracle.flce(hp, W, t, **kw).ce.loss - oracle.flce(hm, W, t, **kw).ce.loss) / (2 * d)
+        assert fd == pytest.approx(r.grad_hidden[i, j], rel=1e-6, abs=1e-10)
+    for (v, j) in [(0, 0), (int(t[t >= 0][0]), 3), (39, 7)]:
+        Wp, Wm = W.copy(), W.copy()
+        Wp[v, j] += d
+        Wm[v, j] -= d
+        fd = (oracle.flce(h, Wp, t, **kw).ce.loss - oracle.flce(h, Wm, t, **kw).ce.loss) / (2 * d)
+        assert fd == pytest.approx(r.grad_weight[v, j], rel=1e-6, abs=1e-10)
+
+
+def test_flce_ignored_rows_do_not_reach_the_gradients():
+    """An ignored row's hidden state changes nothing: zero dL/dh row, the same
+    loss and dL/dW (what makes skipping its products exact)."""
+    h, W, t, _ = _flce_problem(43, 12, 16, 64, ignore_frac=0.5)
+    r = oracle.flce(h, W, t, label_smoothing=0.1)
+    ign = np.where(t == -100)[0]
+    assert np.all(r.grad_hidden[ign] == 0.0)
+    h2 = h.copy()
+    h2[ign] = np.random.default_rng(0).standard_normal((len(ign), 16)) * 100
+    r2 = oracle.flce(h2, W, t, label_smoothing=0.1)
+    assert r2.ce.loss == r.ce.loss
+    np.testing.assert_array_equal(r2.grad_weight, r.grad_weight)
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_flce_on_the_compacted_rows_is_the_same(reduction):
+    """Keeping only the valid rows (the compaction) gives the same loss, the
+    same dL/dW and the valid rows' dL/dh."""
+    h, W, t, cw = _flce_problem(44, 16, 8, 30, weighted=True)
+    kw = dict(class_weight=cw, label_smoothing=0.05, reduction=reduction, grad_output=0.8)
+    r = oracle.flce(h, W, t, **kw)
+    keep = t != -100
+    rc = oracle.flce(h[keep], W, t[keep], **kw)
+    assert rc.ce.loss == pytest.approx(r.ce.loss, rel=1e-14)
+    np.testing.assert_allclose(rc.grad_weight, r.grad_weight, rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(rc.grad_hidden, r.grad_hidden[keep], rtol=1e-13, atol=1e-16)
