@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 RING_CAP_BYTES = 120 << 30  # HBM for pre-filled logits copies
 PROFILE = os.path.join(ROOT, "profiles", "traffic_fused_resident_llm_head.md")
 KERNEL_SOURCES = ["common.h", "rowmath.h", "fused_impl.h", "fused_bf16.hip"]
@@ -206,6 +207,68 @@ def long_rows_mode(L, W, hip, dev, stream, K):
         res[name] = {"ms": round(m, 4), "alg_GBps": round(alg / m / 1e6, 1),
                      "frac_of_hbm_peak": round(alg / m / 1e6 / HBM_PEAK_GBPS, 4)}
     del bufs, pristine
+    torch.cuda.empty_cache()
+    return res
+
+
+def flce_mode(L, W, hip, dev, stream, K):
+    """The linear head fused with the cross-entropy at the pages' FLCE size
+    (BT=8192, H=4096, V=128256 bf16; the headline workload's targets, 410
+    ignored rows, smoothing 0.1, mean): flce_forward_backward per call, and
+    each of its three products alone.  Bound by the matrix cores: the
+    algorithmic work is 3 products of 2 n H V flops over the n kept rows."""
+    import numpy as np
+    import torch
+    import vocab_softmax_cross_amd.functional as vf
+    wl = W.WORKLOADS["llm_head"]
+    BT, H, V = wl.BT, 4096, wl.V
+    g = torch.Generator(device=dev)
+    g.manual_seed(20)
+    hidden = torch.randn((BT, H), generator=g, device=dev).to(torch.bfloat16)
+    weight = (torch.randn((V, H), generator=g, device=dev) * (2.0 / H ** 0.5)).to(torch.bfloat16)
+    tgt = W.targets(wl)
+    t = torch.from_numpy(tgt).to(dev)
+    n = int(np.sum(tgt != -100))
+    p = vf.flce_problem(hidden, weight, t, None, -100, wl.label_smoothing, "mean")
+    ws = torch.empty(L.vsce_flce_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    gh = torch.empty_like(hidden)
+    gw = torch.empty((V, H), dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    outs = L.Outputs()
+    outs.loss = loss.data_ptr()
+
+    def call():
+        L.flce_forward_backward(p, hidden.data_ptr(), weight.data_ptr(), outs, None, 0,
+                                gh.data_ptr(), gw.data_ptr(), ws.data_ptr(), stream)
+
+    call()
+    torch.cuda.synchronize()
+    reps = max(3, min(K, 10))
+    ms = hip.launch_ms(call, reps, stream)
+    flops = 3 * 2.0 * n * H * V
+    res = {"shape": {"BT": BT, "H": H, "V": V, "kept_rows": n}, "ms": round(ms, 3),
+           "TFLOPs": round(flops / ms / 1e9, 1),
+           "frac_of_bf16_mfma_peak": round(flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    # The three products alone, at the same shapes (bf16 operands of the right
+    # sizes; their values do not change the work).
+    a = torch.empty((BT, V), dtype=torch.bfloat16, device=dev).normal_(generator=g)
+    wt = torch.empty((H, V), dtype=torch.bfloat16, device=dev).normal_(generator=g)
+    at = torch.empty((V, BT), dtype=torch.bfloat16, device=dev).normal_(generator=g)
+    ht = torch.empty((H, BT), dtype=torch.bfloat16, device=dev).normal_(generator=g)
+    zl = torch.empty((BT, V), dtype=torch.bfloat16, device=dev)
+    dh = torch.empty((BT, H), dtype=torch.bfloat16, device=dev)
+    products = {
+        "z=hW^T": lambda: vf.gemm_bf16_nt(hidden, weight, out=zl),
+        "dh=GW": lambda: vf.gemm_bf16_nt(a, wt, out=dh),
+        "dW=G^Th": lambda: vf.gemm_bf16_nt(at, ht, out=gw),
+    }
+    one = 2.0 * BT * H * V
+    for name, fn in products.items():
+        fn()
+        torch.cuda.synchronize()
+        t_ms = hip.launch_ms(fn, reps, stream)
+        res[name] = {"ms": round(t_ms, 3), "TFLOPs": round(one / t_ms / 1e9, 1)}
+    del a, wt, at, ht, zl, dh, ws, gw, gh, weight, hidden
     torch.cuda.empty_cache()
     return res
 
@@ -397,6 +460,7 @@ def main():
             "backward_GBps": round((n_valid + wl.BT) * shard_row / t_bwd / 1e6, 1),
             "rank_kernels_ms": round(t_stats + t_merge + t_bwd, 4)}
         extra["fused_long_rows"] = long_rows_mode(L, W, hip, dev, stream, K)
+        extra["flce"] = flce_mode(L, W, hip, dev, stream, K)
         extra[f"fused_softcap{CAP:g}_zloss{ZL:g}"] = {
             "ms_per_step": round(wcap / K * 1e3, 4),
             "rows_per_s": round(wl.BT * K / wcap, 1),

@@ -312,6 +312,78 @@ int ce_scale_grad(void *grad, int64_t rows, int64_t vocab, int64_t row_stride,
                   int64_t grad_output_stride, int32_t skip_if_one,
                   hipStream_t stream);
 
+/* ---------------------------------------------------------------- FLCE
+ * The linear head fused with the cross-entropy (Liger-Kernel PR #1622
+ * "perf(flce): drop host syncs that do not feed the computation": the FLCE
+ * forward computes the loss and both gradients, chunk by chunk of rows; the
+ * #1554 compaction of ignored rows out of the projection products that its
+ * Details discuss is done on the device, with no host read of the count).
+ */
+
+/* bf16 GEMM on the matrix cores, used by the FLCE and callable on its own:
+ * C[m][n] = sum_k A[m][k] B[n][k] with fp32 accumulation.  A is [M][lda] and B
+ * [N][ldb] bf16, both contiguous along k, 16-byte aligned, lda and ldb
+ * multiples of 8 with K <= lda, ldb <= 2^23; K a multiple of 64.  C is
+ * [M][ldc], 16-byte aligned, N and ldc multiples of 4, ldc >= N.  out_mode:
+ * VSCE_GEMM_OUT_BF16 (C bf16, each value rounded once to nearest even),
+ * VSCE_GEMM_OUT_F32 (C fp32), VSCE_GEMM_OUT_F32_ADD (C fp32, the product added
+ * to it).  Returns VSCE_ERR_INVALID for shapes outside these rules. */
+#define VSCE_GEMM_OUT_BF16 0
+#define VSCE_GEMM_OUT_F32 1
+#define VSCE_GEMM_OUT_F32_ADD 2
+int vsce_gemm_bf16_nt(const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
+                      int64_t ldc, int64_t M, int64_t N, int64_t K, int32_t out_mode,
+                      hipStream_t stream);
+
+/*
+ * An FLCE problem: hidden states h [rows][hidden] and the head's weight W
+ * [vocab][hidden], both bf16 row-major (nn.Linear's layout), the logits
+ * z = h W^T and the cross-entropy of z with the options of vsce_problem.
+ *  rows          BT >= 0
+ *  hidden        H: a multiple of 64
+ *  vocab         V >= 1
+ *  chunk_rows    rows whose logits are held at once (rounded up to a multiple
+ *                of 64); 0: all rows in one chunk
+ *  target .. z_loss, reduction   as in vsce_problem (no vocab sharding)
+ */
+typedef struct vsce_flce_problem {
+  int64_t rows;
+  int64_t hidden;
+  int64_t vocab;
+  int64_t chunk_rows;
+  const int64_t *target;
+  const float *class_weight;
+  int64_t ignore_index;
+  float label_smoothing;
+  float softcap;
+  float z_loss;
+  int32_t reduction;
+} vsce_flce_problem;
+
+/* Bytes of workspace flce_forward_backward needs for this problem (256-byte
+ * aligned device memory; 0 if the problem is invalid).  It holds the chunk's
+ * logits and their transposed gradient (2 C V bytes each, C = chunk rows),
+ * W^T (2 H V bytes) and the compacted hidden states and their gradient. */
+size_t vsce_flce_workspace_bytes(const vsce_flce_problem *problem);
+
+/*
+ * Loss outputs (as ce_forward_fused_inplace: loss, and optionally row_loss,
+ * token_acc, acc_mean, z_loss, all in the caller's row order) and both
+ * gradients: grad_hidden [rows][hidden] bf16 (dL/dh, zero rows for ignored
+ * rows; 16-byte aligned) and grad_weight [vocab][hidden] fp32 (dL/dW,
+ * overwritten).  grad_output (device fp32) scales both gradients: one value at
+ * grad_output[0] when grad_output_stride == 0, or one per row when it is 1
+ * (reduction none); NULL means 1.  The logits are bf16 (each rounded once from
+ * the fp32 product) and the cross-entropy's gradient G = dL/dz is bf16 when
+ * it enters the two gradient products, as in the FLCE the page describes.
+ * hidden and weight are 16-byte aligned; nothing is allocated and nothing
+ * synchronizes.
+ */
+int flce_forward_backward(const vsce_flce_problem *problem, const void *hidden,
+                          const void *weight, const vsce_outputs *out, const float *grad_output,
+                          int64_t grad_output_stride, void *grad_hidden, float *grad_weight,
+                          void *workspace, hipStream_t stream);
+
 /* Human-readable name of a return code (static string). */
 const char *vsce_strerror(int code);
 

@@ -218,3 +218,83 @@ def test_binding_raises_on_error_codes():
     with pytest.raises(L.VsceError) as e:
         L.ce_forward_fused_inplace(_problem(vocab=0), FAKE, _outputs(), FAKE, 0)
     assert e.value.code == L.ERR_INVALID
+
+
+# ---------------------------------------------------------------- FLCE and its GEMM
+
+def test_flce_problem_layout_matches_the_header():
+    assert ctypes.sizeof(L.FlceProblem) == 72
+    assert L.FlceProblem.target.offset == 32
+    assert L.FlceProblem.label_smoothing.offset == 56
+    assert L.FlceProblem.reduction.offset == 68
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct vsce_flce_problem \{(.*?)\}", text, re.S).group(1)
+    assert re.findall(r"(\w+)\s*;", body) == [f[0] for f in L.FlceProblem._fields_]
+
+
+def _flce_problem(**kw):
+    p = L.FlceProblem()
+    p.rows, p.hidden, p.vocab, p.chunk_rows = 100, 128, 1000, 0
+    p.target, p.class_weight, p.ignore_index = FAKE, None, -100
+    p.label_smoothing, p.softcap, p.z_loss, p.reduction = 0.0, 0.0, 0.0, L.REDUCTION_MEAN
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _flce(p, hidden=FAKE, weight=FAKE, out="default", go=None, go_stride=0, gh=FAKE, gw=FAKE,
+          ws=FAKE):
+    o = _outputs() if out == "default" else out
+    return L.raw_call("flce_forward_backward", ctypes.byref(p), hidden, weight,
+                      None if o is None else ctypes.byref(o), go, go_stride, gh, gw, ws, None)
+
+
+def test_flce_workspace_size():
+    # chunk logits and their transposed gradient, W^T, compacted hidden states
+    # and their gradient, per-row scratch
+    p = _flce_problem(rows=8192, hidden=4096, vocab=128256)
+    b = L.vsce_flce_workspace_bytes(p)
+    assert b >= 2 * 2 * 8192 * 128256 + 2 * 4096 * 128256 + 2 * 2 * 8192 * 4096
+    assert b < 6e9
+    chunked = L.vsce_flce_workspace_bytes(_flce_problem(rows=8192, hidden=4096, vocab=128256,
+                                                        chunk_rows=1024))
+    assert chunked < b - 3e9  # the logits of one chunk only
+    assert L.vsce_flce_workspace_bytes(_flce_problem(hidden=100)) == 0
+
+
+@pytest.mark.parametrize("field,value", [("rows", -1), ("hidden", 100), ("hidden", 0),
+                                         ("vocab", 0), ("chunk_rows", -5), ("reduction", 4),
+                                         ("label_smoothing", 2.0), ("softcap", -1.0),
+                                         ("z_loss", float("nan")), ("target", None)])
+def test_flce_bad_problem_fields_are_rejected(field, value):
+    assert _flce(_flce_problem(**{field: value})) == L.ERR_INVALID
+
+
+def test_flce_bad_pointers_are_rejected():
+    p = _flce_problem()
+    assert _flce(p, weight=None) == L.ERR_INVALID
+    assert _flce(p, gw=None) == L.ERR_INVALID
+    assert _flce(p, ws=None) == L.ERR_INVALID
+    assert _flce(p, ws=FAKE + 16) == L.ERR_INVALID    # 256-byte aligned workspace
+    assert _flce(p, hidden=FAKE + 2) == L.ERR_INVALID  # 16-byte aligned operands
+    assert _flce(p, gh=None) == L.ERR_INVALID
+    assert _flce(p, out=None) == L.ERR_INVALID
+    assert _flce(p, out=_outputs(loss=None)) == L.ERR_INVALID
+    assert _flce(p, go=FAKE, go_stride=2) == L.ERR_INVALID
+
+
+def _gemm(M=128, N=128, K=64, lda=64, ldb=64, ldc=128, mode=0, A=FAKE, B=FAKE, C=FAKE):
+    return L.raw_call("vsce_gemm_bf16_nt", A, lda, B, ldb, C, ldc, M, N, K, mode, None)
+
+
+@pytest.mark.parametrize("kw", [dict(K=96, lda=96, ldb=96), dict(lda=32), dict(ldb=40),
+                                dict(lda=68), dict(N=126, ldc=128), dict(ldc=126),
+                                dict(ldc=64), dict(mode=3), dict(M=-1), dict(A=FAKE + 8),
+                                dict(C=None), dict(lda=(1 << 23) + 8, ldb=64)])
+def test_gemm_argument_checks(kw):
+    assert _gemm(**kw) == L.ERR_INVALID
+
+
+def test_gemm_empty_is_a_no_op():
+    assert _gemm(M=0) == L.OK
+    assert _gemm(N=0) == L.OK

@@ -1,0 +1,259 @@
+"""The linear head fused with the cross-entropy (FLCE) on the GPU, through the
+C ABI, against the fp64 oracle.
+
+The chain of checks:
+* the bf16 GEMM against fp64 products, within the fp32-accumulation bound
+  |c - c64| <= K 2^-24 sum_k |a b| (plus half a bf16 ulp when C is bf16);
+* flce_forward_backward equals, bit for bit, the same stages composed from
+  the public entry points (vsce_gemm_bf16_nt for z = h W^T, the fused
+  cross-entropy on z, vsce_gemm_bf16_nt for G W and G^T h), with the ignored
+  rows dropped on the host;
+* each stage of that composition against the oracle on the stage's own
+  inputs: the cross-entropy against oracle.cross_entropy of the bf16 logits
+  (the cross-entropy tests' bars), the gradient products against fp64
+  products of the bf16 G;
+* end to end against oracle.flce (fp64, no intermediate rounding), within the
+  first-order effect of rounding z to bf16;
+* chunked runs against the unchunked one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.compare import assert_loss_close, grad_report
+
+pytestmark = pytest.mark.gpu
+
+vf = pytest.importorskip("vocab_softmax_cross_amd.functional")
+
+U32 = 2.0 ** -24
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _note(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _bf16(rng, shape, scale, dev):
+    return torch.from_numpy((rng.standard_normal(shape) * scale).astype(np.float32)).to(
+        torch.bfloat16).to(dev)
+
+
+def _f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _ulp_bf16(v):
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.exp2(np.maximum(e, -126) - 7)
+
+
+def _check_product(got, a64, b64, bf16_out, what, add=None):
+    exact = a64 @ b64.T + (0.0 if add is None else add)
+    err = a64.shape[1] * U32 * (np.abs(a64) @ np.abs(b64).T)
+    tol = err + (0.5 * _ulp_bf16(np.abs(exact) + err) if bf16_out else 0.0)
+    bad = np.abs(got - exact) > tol
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outside the bound"
+
+
+# ---------------------------------------------------------------- the GEMM
+
+@pytest.mark.parametrize("M,N,K", [(128, 128, 64), (300, 260, 192), (64, 1000, 128),
+                                   (1000, 4, 64), (257, 516, 4096)])
+@pytest.mark.parametrize("mode", ["bf16", "f32", "f32_add"])
+def test_gemm_matches_fp64(M, N, K, mode):
+    dev = _dev()
+    _note(f"gemm M={M} N={N} K={K} {mode}")
+    rng = np.random.default_rng(M * 7 + N + K)
+    a = _bf16(rng, (M, K), 1.0, dev)
+    b = _bf16(rng, (N, K), 1.0, dev)
+    if mode == "bf16":
+        c = vf.gemm_bf16_nt(a, b)
+        add = None
+    else:
+        c0 = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32)).to(dev)
+        c = c0.clone()
+        vf.gemm_bf16_nt(a, b, out=c, accumulate=(mode == "f32_add"))
+        add = _f64(c0) if mode == "f32_add" else None
+    torch.cuda.synchronize()
+    _check_product(_f64(c), _f64(a), _f64(b), mode == "bf16", "gemm", add)
+
+
+def test_gemm_leaves_padding_alone():
+    """Strided operands and output: columns past N of C are not written."""
+    dev = _dev()
+    rng = np.random.default_rng(5)
+    abuf = _bf16(rng, (96, 200), 1.0, dev)
+    bbuf = _bf16(rng, (40, 200), 1.0, dev)
+    a, b = abuf[:, :128], bbuf[:, :128]
+    cbuf = torch.full((96, 48), 7.0, dtype=torch.float32, device=dev)
+    c = cbuf[:, :40]
+    vf.gemm_bf16_nt(a, b, out=c)
+    torch.cuda.synchronize()
+    assert torch.all(cbuf[:, 40:] == 7.0)
+    _check_product(_f64(c), _f64(a), _f64(b), False, "strided gemm")
+
+
+# ---------------------------------------------------------------- FLCE
+
+def _problem(seed, BT, H, V, ignore_frac=0.2, weighted=False):
+    dev = _dev()
+    rng = np.random.default_rng(seed)
+    h = _bf16(rng, (BT, H), 1.0, dev)
+    W = _bf16(rng, (V, H), 2.0 / np.sqrt(H), dev)
+    t = rng.integers(0, V, BT).astype(np.int64)
+    t[rng.permutation(BT)[: int(round(ignore_frac * BT))]] = -100
+    cw = rng.uniform(0.5, 1.5, V).astype(np.float32) if weighted else None
+    return h, W, t, cw
+
+
+def _compose(h, W, t, cw, eps, reduction, softcap=0.0, z_loss=0.0):
+    """The FLCE's stages through the public entry points, one chunk, the
+    ignored rows dropped on the host: returns the stage inputs and outputs."""
+    dev = h.device
+    BT, H = h.shape
+    V = W.shape[0]
+    Vp = (V + 63) // 64 * 64
+    keep = np.where(t != -100)[0]
+    n = len(keep)
+    C = (max(BT, 1) + 63) // 64 * 64
+    xc = torch.zeros((C, H), dtype=torch.bfloat16, device=dev)
+    xc[:n] = h[torch.from_numpy(keep).to(dev)]
+    tc = np.full(C, -100, np.int64)
+    tc[:n] = t[keep]
+    Wp = torch.zeros((Vp, H), dtype=torch.bfloat16, device=dev)
+    Wp[:V] = W
+    z = torch.zeros((C, Vp), dtype=torch.bfloat16, device=dev)
+    vf.gemm_bf16_nt(xc, Wp, out=z)
+    z_bf = z.clone()
+    zv = z[:, :V]
+    cwt = None if cw is None else torch.from_numpy(cw).to(dev)
+    res = vf.forward_fused_inplace(zv, torch.from_numpy(tc).to(dev), cwt, -100, eps, reduction,
+                                   row_loss=True, softcap=softcap, z_loss=z_loss)
+    G = z  # the gradient, in place, zero columns past V
+    dxc = vf.gemm_bf16_nt(G, Wp.t().contiguous())
+    dW = torch.empty((Vp, H), dtype=torch.float32, device=dev)
+    vf.gemm_bf16_nt(G.t().contiguous(), xc.t().contiguous(), out=dW)
+    torch.cuda.synchronize()
+    return dict(keep=keep, n=n, tc=tc, z=z_bf, G=G, dxc=dxc, dW=dW[:V], res=res, xc=xc)
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+@pytest.mark.parametrize("weighted,eps", [(False, 0.0), (True, 0.1)])
+def test_flce_equals_its_stages_and_each_stage_the_oracle(reduction, weighted, eps):
+    h, W, t, cw = _problem(11, 300, 256, 1000, weighted=weighted)
+    _note(f"flce BT=300 H=256 V=1000 red={reduction} weighted={weighted} eps={eps}")
+    dev = h.device
+    cwt = None if cw is None else torch.from_numpy(cw).to(dev)
+    out = vf.flce_forward_backward(h, W, torch.from_numpy(t).to(dev), cwt, -100, eps, reduction,
+                                   row_loss=True)
+    st = _compose(h, W, t, cw, eps, reduction)
+    torch.cuda.synchronize()
+    keep, n = st["keep"], st["n"]
+    # 1. The whole equals its stages, bit for bit.
+    assert float(out["loss"]) == float(st["res"]["loss"])
+    rl = np.zeros(300, np.float32)
+    rl[keep] = st["res"]["row_loss"][:n].cpu().numpy()
+    np.testing.assert_array_equal(out["row_loss"].cpu().numpy(), rl)
+    gh = torch.zeros_like(h)
+    gh[torch.from_numpy(keep).to(dev)] = st["dxc"][:n]
+    assert torch.equal(out["grad_hidden"], gh)
+    assert torch.equal(out["grad_weight"], st["dW"])
+    # 2. The logits product against fp64.
+    _check_product(_f64(st["z"][:n, :1000]), _f64(h)[keep], _f64(W), True, "z = h W^T")
+    # 3. The cross-entropy stage against the oracle on the same bf16 logits.
+    z64 = _f64(st["z"][:, :1000])
+    ref = oracle.cross_entropy(z64, st["tc"], cw, -100, eps, reduction, 1.0, "bf16")
+    assert_loss_close(float(st["res"]["loss"]), ref.loss, 1e-5, "chunk loss")
+    g = _f64(st["G"][:, :1000])
+    rep = grad_report(g, ref.grad, "bf16", z64, st["tc"], ref.stats, ref.cls, ref.scale, eps,
+                      cw, ref.norm.sum_w)
+    assert rep.floor_fail == 0, rep
+    # 4. The gradient products against fp64 products of the bf16 G.
+    g_n = g[:n]
+    _check_product(_f64(st["dxc"][:n]), g_n, _f64(W).T, True, "dL/dh = G W")
+    _check_product(_f64(st["dW"]), g_n.T, _f64(h)[keep].T, False, "dL/dW = G^T h")
+    # 5. Ignored rows get zero dL/dh.
+    assert torch.all(out["grad_hidden"][torch.from_numpy(np.where(t == -100)[0]).to(dev)] == 0)
+
+
+@pytest.mark.parametrize("softcap,z_loss,reduction", [(0.0, 0.0, "mean"), (30.0, 1e-3, "sum"),
+                                                       (15.0, 0.0, "none")])
+def test_flce_end_to_end_against_the_fp64_oracle(softcap, z_loss, reduction):
+    """The row losses within the first-order effect of rounding each logit to
+    bf16 (|dl| <= sum_c |dl/dz_c| |dz_c| <= 2 max_c |dz_c|), the gradients
+    within a bound of the same origin."""
+    h, W, t, cw = _problem(12, 200, 512, 2048, weighted=True)
+    eps = 0.05
+    _note(f"flce end to end softcap={softcap} z_loss={z_loss} red={reduction}")
+    dev = h.device
+    go = torch.linspace(0.5, 1.5, 200, device=dev) if reduction == "none" else \
+        torch.tensor(0.7, device=dev)
+    out = vf.flce_forward_backward(h, W, torch.from_numpy(t).to(dev),
+                                   torch.from_numpy(cw).to(dev), -100, eps, reduction, softcap,
+                                   z_loss, grad_output=go, row_loss=True, accuracy=True,
+                                   return_z_loss=True)
+    torch.cuda.synchronize()
+    h64, W64 = _f64(h), _f64(W)
+    ref = oracle.flce(h64, W64, t, cw.astype(np.float64), -100, eps, reduction,
+                      go.cpu().numpy().astype(np.float64) if reduction == "none" else 0.7,
+                      softcap, z_loss)
+    z = ref.logits
+    dz = 0.5 * _ulp_bf16(np.abs(z)) + 512 * U32 * (np.abs(h64) @ np.abs(W64).T)
+    lse_term = 2.0 * z_loss * (np.abs(z).max(axis=1) + np.log(2048.0)) + 2.0
+    row_tol = lse_term * 1.5 * dz.max(axis=1) + 1e-5 * np.abs(ref.ce.row_loss)
+    valid = t != -100
+    got = out["row_loss"].cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref.ce.row_loss)[valid] <= row_tol[valid])
+    assert np.all(got[~valid] == 0.0)
+    # dL/dh and dL/dW move by the logits' rounding through p and by G's bf16
+    # rounding; both are well inside a few per cent of the row's scale.
+    gh = _f64(out["grad_hidden"])
+    scale_h = np.abs(ref.grad_hidden).max() + 1e-30
+    assert np.max(np.abs(gh - ref.grad_hidden)) <= 0.05 * scale_h
+    gw = out["grad_weight"].cpu().numpy().astype(np.float64)
+    scale_w = np.abs(ref.grad_weight).max() + 1e-30
+    assert np.max(np.abs(gw - ref.grad_weight)) <= 0.05 * scale_w
+    np.testing.assert_array_equal(out["token_acc"].cpu().numpy()[~valid], 0.0)
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 192])
+def test_flce_chunked_equals_unchunked(chunk):
+    """Chunks change nothing but the order of dL/dW's fp32 sums over rows."""
+    h, W, t, cw = _problem(13, 500, 128, 640, weighted=False, ignore_frac=0.3)
+    _note(f"flce chunk={chunk}")
+    dev = h.device
+    tt = torch.from_numpy(t).to(dev)
+    a = vf.flce_forward_backward(h, W, tt, None, -100, 0.1, "mean", row_loss=True)
+    b = vf.flce_forward_backward(h, W, tt, None, -100, 0.1, "mean", row_loss=True,
+                                 chunk_rows=chunk)
+    torch.cuda.synchronize()
+    assert float(a["loss"]) == float(b["loss"])
+    assert torch.equal(a["row_loss"], b["row_loss"])
+    assert torch.equal(a["grad_hidden"], b["grad_hidden"])
+    # dL/dW: two fp32 sums over the same n rows in different orders, each
+    # within n 2^-24 sum_k |G||h| of the exact one (G from the stages, which
+    # equal the unchunked run bit for bit).
+    st = _compose(h, W, t, None, 0.1, "mean")
+    n = st["n"]
+    assert torch.equal(a["grad_weight"], st["dW"])
+    g = np.abs(_f64(st["G"][:n, :640]))
+    bound = 2 * n * U32 * (g.T @ np.abs(_f64(h)[st["keep"]]))
+    diff = np.abs(_f64(a["grad_weight"]) - _f64(b["grad_weight"]))
+    assert np.all(diff <= bound), float((diff - bound).max())
+
+
+def test_flce_all_rows_ignored():
+    h, W, t, _ = _problem(14, 70, 64, 128, ignore_frac=1.0)
+    dev = h.device
+    out = vf.flce_forward_backward(h, W, torch.from_numpy(t).to(dev), None, -100, 0.0, "sum")
+    torch.cuda.synchronize()
+    assert float(out["loss"]) == 0.0
+    assert torch.all(out["grad_hidden"] == 0) and torch.all(out["grad_weight"] == 0)

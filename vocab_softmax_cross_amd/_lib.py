@@ -28,7 +28,9 @@ WS_INV_W, WS_INV_N_VALID = 40, 44
 
 EXPORTS = ("vsce_workspace_bytes", "ce_forward_fused_inplace", "ce_forward_fused_inplace_timed",
            "ce_forward_stats", "ce_forward_stats_partial", "ce_merge_stats",
-           "ce_backward_from_stats", "ce_scale_grad", "vsce_strerror", "vsce_version")
+           "ce_backward_from_stats", "ce_scale_grad", "vsce_gemm_bf16_nt",
+           "vsce_flce_workspace_bytes", "flce_forward_backward", "vsce_strerror", "vsce_version")
+GEMM_OUT_BF16, GEMM_OUT_F32, GEMM_OUT_F32_ADD = 0, 1, 2
 
 
 class Problem(ctypes.Structure):
@@ -48,6 +50,23 @@ class Problem(ctypes.Structure):
         ("flags", c_uint32),
         ("vocab_offset", c_int64),
         ("vocab_total", c_int64),
+    ]
+
+
+class FlceProblem(ctypes.Structure):
+    """struct vsce_flce_problem."""
+    _fields_ = [
+        ("rows", c_int64),
+        ("hidden", c_int64),
+        ("vocab", c_int64),
+        ("chunk_rows", c_int64),
+        ("target", c_void_p),
+        ("class_weight", c_void_p),
+        ("ignore_index", c_int64),
+        ("label_smoothing", c_float),
+        ("softcap", c_float),
+        ("z_loss", c_float),
+        ("reduction", c_int32),
     ]
 
 
@@ -101,6 +120,15 @@ def load() -> ctypes.CDLL:
     lib.ce_scale_grad.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_int32, c_void_p, c_int64,
                                   c_int32, c_void_p]
     lib.ce_scale_grad.restype = ctypes.c_int
+    lib.vsce_gemm_bf16_nt.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
+                                      c_int64, c_int64, c_int64, c_int32, c_void_p]
+    lib.vsce_gemm_bf16_nt.restype = ctypes.c_int
+    lib.vsce_flce_workspace_bytes.argtypes = [P(FlceProblem)]
+    lib.vsce_flce_workspace_bytes.restype = c_size_t
+    lib.flce_forward_backward.argtypes = [P(FlceProblem), c_void_p, c_void_p, P(Outputs),
+                                          c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
+                                          c_void_p]
+    lib.flce_forward_backward.restype = ctypes.c_int
     lib.vsce_strerror.argtypes = [ctypes.c_int]
     lib.vsce_strerror.restype = ctypes.c_char_p
     lib.vsce_version.argtypes = []
@@ -172,3 +200,21 @@ def raw_call(name: str, *args) -> int:
     """Call an entry point and return its code without raising (tests of the
     argument checks)."""
     return int(getattr(load(), name)(*args))
+
+
+def vsce_gemm_bf16_nt(A: int, lda: int, B: int, ldb: int, C: int, ldc: int, M: int, N: int, K: int,
+                      out_mode: int, stream: int) -> int:
+    return _check("vsce_gemm_bf16_nt", load().vsce_gemm_bf16_nt(A, lda, B, ldb, C, ldc, M, N, K,
+                                                                 out_mode, stream))
+
+
+def vsce_flce_workspace_bytes(problem: FlceProblem) -> int:
+    return int(load().vsce_flce_workspace_bytes(ctypes.byref(problem)))
+
+
+def flce_forward_backward(problem: FlceProblem, hidden: int, weight: int, outputs: Outputs,
+                          grad_output, grad_output_stride: int, grad_hidden: int,
+                          grad_weight: int, workspace: int, stream: int) -> int:
+    return _check("flce_forward_backward", load().flce_forward_backward(
+        ctypes.byref(problem), hidden, weight, ctypes.byref(outputs), grad_output,
+        grad_output_stride, grad_hidden, grad_weight, workspace, stream))

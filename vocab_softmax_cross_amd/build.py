@@ -37,6 +37,8 @@ SOURCES = [
     "fused_f32_cap.hip",
     "fused_bf16_cap.hip",
     "fused_f16_cap.hip",
+    "gemm.hip",
+    "flce.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -28,6 +28,8 @@ int elem_bytes(int dt) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+}  // namespace
+
 // Checks a problem descriptor and fills the derived fields.
 int check_problem(const vsce_problem* pb, const void* logits, Prob& p) {
   if (!pb) return VSCE_ERR_INVALID;
@@ -74,19 +76,6 @@ int check_problem(const vsce_problem* pb, const void* logits, Prob& p) {
   return VSCE_OK;
 }
 
-// The entry points that see whole rows (loss, fused gradient) take no shard.
-bool whole_rows(const Prob& p) { return p.voff == 0 && p.Vt == p.V; }
-
-int check_workspace(const void* ws) {
-  if (!ws || !aligned(ws, kAlign)) return VSCE_ERR_INVALID;
-  return VSCE_OK;
-}
-
-int check_outputs(const vsce_outputs* out) {
-  if (!out || !out->loss) return VSCE_ERR_INVALID;
-  return VSCE_OK;
-}
-
 // The problem's fields every per-row kernel reads.  The kernels index the
 // weights by this buffer's columns, so a shard sees its slice of them.
 void problem_args(const Prob& p, RowArgs& a) {
@@ -104,6 +93,21 @@ void problem_args(const Prob& p, RowArgs& a) {
   a.zl = p.zl;
   a.mean = (p.red == VSCE_REDUCTION_MEAN);
   a.rows = p.rows;
+}
+
+namespace {
+
+// The entry points that see whole rows (loss, fused gradient) take no shard.
+bool whole_rows(const Prob& p) { return p.voff == 0 && p.Vt == p.V; }
+
+int check_workspace(const void* ws) {
+  if (!ws || !aligned(ws, kAlign)) return VSCE_ERR_INVALID;
+  return VSCE_OK;
+}
+
+int check_outputs(const vsce_outputs* out) {
+  if (!out || !out->loss) return VSCE_ERR_INVALID;
+  return VSCE_OK;
 }
 
 // The workspace after its header: [rows] fp32 scratch for the row losses, the

@@ -65,6 +65,12 @@ struct RowArgs {
   const WsHeader* ws;
 };
 
+// Checks a problem descriptor (with the logits pointer it will be used
+// with) and fills the derived fields; VSCE_OK or the error to return.
+int check_problem(const vsce_problem* pb, const void* logits, Prob& p);
+// The problem's fields every per-row kernel reads.
+void problem_args(const Prob& p, RowArgs& a);
+
 int launch_prologue(const Prob& p, WsHeader* ws, hipStream_t s);
 int launch_finalize(const Prob& p, const float* loss_rows, const float* acc_rows,
                     const float* z_rows, float* loss_out, float* acc_mean_out, float* z_out,
@@ -92,5 +98,28 @@ int launch_merge(const Prob& p, const float* partials, int shards, float* stats,
                  const RowArgs& a, hipStream_t s);
 // In-place grad_output scale.
 int launch_scale(const Prob& p, RowArgs a, hipStream_t s);
+
+// bf16 GEMM on the matrix cores: C[m, n] = sum_k A[m, k] B[n, k] with fp32
+// accumulation.  A is [M, K] and B [N, K], both contiguous along k (leading
+// dimensions lda, ldb in elements, multiples of 8, at most 2^23), 16-byte
+// aligned; K a multiple of 64; N and ldc multiples of 4.  Device-side counts
+// (optional) narrow the work without a host read: rows m >= *m_count are
+// neither computed nor stored, and k runs to *k_count rounded up to 64 (the
+// caller keeps A and B zero between the count and that bound).
+struct GemmArgs {
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  void* C;
+  int64_t ldc;
+  int M, N, K;
+  int a_rows, b_rows;     // rows of A and B in memory (rows past them read as zeros)
+  int group_m;            // m-tiles per group of the tile order (>= 1)
+  const int* m_count;     // device, or null (all M rows)
+  const int* k_count;     // device, or null (all K)
+};
+enum { kGemmOutBf16 = 0, kGemmOutF32 = 1, kGemmOutF32Add = 2 };
+int launch_gemm_nt(int out, const GemmArgs& g, hipStream_t s);
 
 }  // namespace vsce

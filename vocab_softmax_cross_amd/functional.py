@@ -358,3 +358,88 @@ def status(workspace: torch.Tensor) -> dict:
         "inv_W": float(h[L.WS_INV_W:L.WS_INV_W + 4].view(torch.float32)[0]),
         "inv_n_valid": float(h[L.WS_INV_N_VALID:L.WS_INV_N_VALID + 4].view(torch.float32)[0]),
     }
+
+
+# ---------------------------------------------------------------- FLCE
+
+def gemm_bf16_nt(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 accumulate: bool = False, out_dtype=torch.bfloat16) -> torch.Tensor:
+    """vsce_gemm_bf16_nt: a @ b.T for bf16 a [M, K] and b [N, K] (contiguous
+    rows, K a multiple of 64) on the matrix cores; bf16 or fp32 out, or added
+    to an fp32 `out` when accumulate."""
+    if a.dtype != torch.bfloat16 or b.dtype != torch.bfloat16 or a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D bfloat16 tensors")
+    if a.shape[1] != b.shape[1] or a.stride(1) != 1 or b.stride(1) != 1:
+        raise ValueError("a and b must share K and be contiguous along it")
+    M, K = a.shape
+    N = b.shape[0]
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an fp32 out")
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    mode = (L.GEMM_OUT_F32_ADD if accumulate else L.GEMM_OUT_F32) \
+        if out.dtype == torch.float32 else L.GEMM_OUT_BF16
+    if out.dtype not in (torch.float32, torch.bfloat16) or out.shape != (M, N) or out.stride(1) != 1:
+        raise ValueError("out must be a [M, N] float32 or bfloat16 tensor with contiguous rows")
+    L.vsce_gemm_bf16_nt(a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0), out.data_ptr(),
+                        out.stride(0), M, N, K, mode, _stream(a))
+    return out
+
+
+def flce_problem(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
+                 class_weight: Optional[torch.Tensor] = None, ignore_index: int = -100,
+                 label_smoothing: float = 0.0, reduction: str = "mean", softcap: float = 0.0,
+                 z_loss: float = 0.0, chunk_rows: int = 0):
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise ValueError("hidden and weight must be bfloat16")
+    if hidden.dim() != 2 or weight.dim() != 2 or hidden.shape[1] != weight.shape[1]:
+        raise ValueError("hidden [BT, H] and weight [V, H] must share H")
+    if not hidden.is_contiguous() or not weight.is_contiguous():
+        raise ValueError("hidden and weight must be contiguous")
+    t = target.reshape(-1)
+    if t.dtype != torch.int64 or not t.is_contiguous() or t.numel() != hidden.shape[0]:
+        raise ValueError("target must be a contiguous int64 tensor with one entry per row")
+    V = weight.shape[0]
+    if class_weight is not None and (class_weight.dtype != torch.float32 or
+                                     not class_weight.is_contiguous() or
+                                     class_weight.numel() != V):
+        raise ValueError("class weights must be a contiguous float32 [V] tensor")
+    p = L.FlceProblem()
+    p.rows, p.hidden, p.vocab, p.chunk_rows = hidden.shape[0], hidden.shape[1], V, int(chunk_rows)
+    p.target = t.data_ptr() or None
+    p.class_weight = None if class_weight is None else class_weight.data_ptr()
+    p.ignore_index, p.label_smoothing = int(ignore_index), float(label_smoothing)
+    p.softcap, p.z_loss, p.reduction = float(softcap), float(z_loss), L.REDUCTIONS[reduction]
+    return p
+
+
+def flce_forward_backward(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
+                          class_weight: Optional[torch.Tensor] = None, ignore_index: int = -100,
+                          label_smoothing: float = 0.0, reduction: str = "mean",
+                          softcap: float = 0.0, z_loss: float = 0.0, chunk_rows: int = 0,
+                          grad_output: Optional[torch.Tensor] = None, row_loss: bool = False,
+                          accuracy: bool = False, return_z_loss: bool = False,
+                          workspace: Optional[torch.Tensor] = None) -> dict:
+    """flce_forward_backward: the loss outputs of cross_entropy(hidden @
+    weight.T) and both gradients (grad_hidden bf16, grad_weight fp32)."""
+    p = flce_problem(hidden, weight, target, class_weight, ignore_index, label_smoothing,
+                     reduction, softcap, z_loss, chunk_rows)
+    dev = hidden.device
+    ws_bytes = L.vsce_flce_workspace_bytes(p)
+    if ws_bytes == 0:
+        raise ValueError("unsupported FLCE problem")
+    ws = workspace if workspace is not None else torch.empty(ws_bytes, dtype=torch.uint8,
+                                                              device=dev)
+    if ws.numel() < ws_bytes:
+        raise ValueError(f"workspace too small: {ws.numel()} < {ws_bytes} bytes")
+    o, res = _outputs(p.rows, reduction, dev, row_loss, accuracy, return_z_loss)
+    gh = torch.empty_like(hidden)
+    gw = torch.empty(weight.shape, dtype=torch.float32, device=dev)
+    go, go_stride = (None, 0) if grad_output is None else \
+        _grad_output(grad_output, p.rows, reduction, dev)
+    L.flce_forward_backward(p, hidden.data_ptr(), weight.data_ptr(), o,
+                            None if go is None else go.data_ptr(), go_stride, gh.data_ptr(),
+                            gw.data_ptr(), ws.data_ptr(), _stream(hidden))
+    res["grad_hidden"], res["grad_weight"] = gh, gw
+    res["workspace"] = ws
+    return res
