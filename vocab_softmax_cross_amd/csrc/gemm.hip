@@ -3,12 +3,13 @@
 // (Liger-Kernel PR #1622, FLCE: logits = h W^T, dL/dh = G W, dL/dW = G^T h,
 // each arranged so that both operands are contiguous along k).
 //
-// One workgroup of 256 threads computes a 128 x 128 tile of C.  Its four
-// wavefronts each own a 64 x 64 quarter, as 2 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  k advances 64 at a time
-// through two LDS stages of A and B (16 KB each): the next stage is loaded
-// straight into LDS (buffer_load_dwordx4 ... lds) while the current one is
-// multiplied.  In LDS each tile row is 8 chunks of 16 bytes, the chunk
+// One workgroup of 256 threads computes a 256 x 256 block of C (128 x 128
+// for small products).  Its four wavefronts each own a quarter, as 4 x 4 (or
+// 2 x 2) blocks of v_mfma_f32_32x32x16_bf16 with fp32 accumulators: a larger
+// quarter reads fewer operand bytes from LDS per MFMA.  k advances 64 at a
+// time through two LDS stages of A and B (32 KB each for 256 rows): the next
+// stage is loaded straight into LDS (buffer_load_dwordx4 ... lds) while the
+// current one is multiplied.  In LDS each tile row is 8 chunks of 16 bytes, the chunk
 // index XOR-ed with the row (mod 8), so that the 32 rows one MFMA operand
 // reads sit in different banks; the swizzle is applied by choosing which
 // global chunk each lane loads, since a direct-to-LDS load writes lane i at
@@ -32,12 +33,18 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 64, NT = 256;
-constexpr int kChunks = BM * BK * 2 / 16;  // 16-byte chunks per operand stage (1024)
-static_assert(BM == BN, "A and B stages share one layout");
+constexpr int kKMult = 64, NT = 256;  // K must be a multiple of kKMult
 
-// LDS chunk of (row, 16-byte k-chunk kc) in a stage.
-__device__ __forceinline__ int swz(int row, int kc) { return row * 8 + (kc ^ (row & 7)); }
+// LDS chunk of (row, 16-byte k-chunk kc) in a stage whose rows hold BK
+// k-values (BK / 8 chunks).  The chunk index is XOR-ed with a function of the
+// row so that 8 consecutive rows read at one kc hit 8 different 16-byte slots
+// of a 128-byte bank line: rows of 128 bytes (BK 64) use row mod 8; rows of
+// 64 bytes (BK 32, two per line) use (row / 2) mod 4.
+template <int BK>
+__device__ __forceinline__ int swz(int row, int kc) {
+  if constexpr (BK == 64) return row * 8 + (kc ^ (row & 7));
+  else return row * 4 + (kc ^ ((row >> 1) & 3));
+}
 
 // A stage is read with ordinary LDS loads (the compiler places their waits
 // and the MFMA register hazards); the direct-to-LDS loads that fill it are
@@ -47,8 +54,10 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Workgroup barrier after this wavefront's LDS reads have completed (so a
+// stage is refilled only once every wavefront is done reading it).
 __device__ __forceinline__ void barrier() {
-  asm volatile("" ::: "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -70,9 +79,18 @@ __device__ __forceinline__ void tile_of(int64_t t, int tiles_m, int tiles_n, int
   tn = in / gm;
 }
 
-template <int OUT>
-__global__ __launch_bounds__(NT, 2) void gemm_nt_kernel(const GemmArgs g) {
-  __shared__ uint4 lds[2][2][kChunks];  // [stage][A, B][chunk]: 64 KB
+// BM x BN block, four wavefronts as 2 x 2, each a (BM / 2) x (BN / 2) quarter
+// of R x S 32 x 32 MFMA blocks; NS LDS stages of BK k-values (NS - 1 of them
+// in flight while one is multiplied); WPE wavefronts per SIMD to compile for.
+template <int OUT, int BM, int BN, int BK, int NS, int WPE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
+void gemm_nt_kernel(const GemmArgs g) {
+  constexpr int R = BM / 64, S = BN / 64;
+  constexpr int CPR = BK / 8;                      // 16-byte chunks per tile row
+  constexpr int LA = BM * CPR / (4 * kWave), LB = BN * CPR / (4 * kWave);
+  constexpr int L = LA + LB;                       // loads per wavefront per stage
+  static_assert(NS >= 2 && NS <= 4 && (NS - 2) * L <= 63, "stages");
+  __shared__ uint4 lds[NS][(BM + BN) * CPR];       // [stage][A rows, then B rows][chunk]
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = uniform(tid / kWave);
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
@@ -82,7 +100,8 @@ __global__ __launch_bounds__(NT, 2) void gemm_nt_kernel(const GemmArgs g) {
   const int m_eff = g.m_count ? min(max(*g.m_count, 0), g.M) : g.M;
   const int m0 = tm * BM, n0 = tn * BN;
   if (m0 >= m_eff) return;  // rows past the device-side count: nothing to do
-  const int k_eff = g.k_count ? min(g.K, (max(*g.k_count, 0) + BK - 1) / BK * BK) : g.K;
+  const int k_eff =
+      g.k_count ? min(g.K, (max(*g.k_count, 0) + kKMult - 1) / kKMult * kKMult) : g.K;
   const int nk = k_eff / BK;
 
   // One resource per operand tile: rows past those in memory read as zeros.
@@ -91,77 +110,85 @@ __global__ __launch_bounds__(NT, 2) void gemm_nt_kernel(const GemmArgs g) {
                             static_cast<uint32_t>(rows_a * g.lda * 2));
   const auto rb = make_rsrc(static_cast<const uint16_t*>(g.B) + static_cast<int64_t>(n0) * g.ldb,
                             static_cast<uint32_t>(rows_b * g.ldb * 2));
-  // This lane's chunk of each of the wavefront's 4 loads per operand: chunk
-  // j = q 64 + lane of the stage holds (row j / 8, k-chunk (j mod 8) xor row).
-  uint32_t offa[4], offb[4];
+  // This lane's chunk of each of the wavefront's loads: chunk j = q 64 + lane
+  // of an operand's stage is LDS position j, which swz() assigns to (row
+  // j / CPR, k-chunk (j mod CPR) xor f(row)); the XOR is its own inverse.
+  uint32_t offa[LA], offb[LB];
+  auto chunk_offset = [&](int j, int64_t ld) {
+    const int row = j / CPR;
+    const int kc = swz<BK>(row, j % CPR) - row * CPR;
+    return static_cast<uint32_t>((row * ld + kc * 8) * 2);  // < 2^31: ld <= 2^23
+  };
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = (wave * 4 + i) * kWave + lane;
-    const int row = j >> 3, kc = (j & 7) ^ (row & 7);
-    offa[i] = static_cast<uint32_t>((row * g.lda + kc * 8) * 2);  // < 2^31: lda <= 2^23
-    offb[i] = static_cast<uint32_t>((row * g.ldb + kc * 8) * 2);
-  }
+  for (int i = 0; i < LA; ++i) offa[i] = chunk_offset((wave * LA + i) * kWave + lane, g.lda);
+#pragma unroll
+  for (int i = 0; i < LB; ++i) offb[i] = chunk_offset((wave * LB + i) * kWave + lane, g.ldb);
   auto load_stage = [&](int s, int k0) {
     const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = wave * 4 + i;
-      buf_load16_lds(ra, &lds[s][0][q * kWave], offa[i] + kb, 0);
-      buf_load16_lds(rb, &lds[s][1][q * kWave], offb[i] + kb, 0);
-    }
+    for (int i = 0; i < LA; ++i)
+      buf_load16_lds(ra, &lds[s][(wave * LA + i) * kWave], offa[i] + kb, 0);
+#pragma unroll
+    for (int i = 0; i < LB; ++i)
+      buf_load16_lds(rb, &lds[s][BM * CPR + (wave * LB + i) * kWave], offb[i] + kb, 0);
   };
 
-  const int wm = wave >> 1, wn = wave & 1;  // this wavefront's 64 x 64 quarter
+  const int wm = wave >> 1, wn = wave & 1;  // this wavefront's quarter
   const int r32 = lane & 31, khalf = lane >> 5;
-  f32x16 acc[2][2];
+  f32x16 acc[R][S];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < R; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < S; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-  if (nk > 0) load_stage(0, 0);
+  // NS - 1 stages in flight ahead of the one being multiplied.
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) load_stage(st, st * BK);
   for (int kt = 0; kt < nk; ++kt) {
-    const int s = kt & 1;
-    if (kt + 1 < nk) {
-      load_stage(s ^ 1, (kt + 1) * BK);
-      wait_vm<8>();  // this stage's 8 loads have landed; the next stage's may not
-    } else {
-      wait_vm<0>();
-    }
-    barrier();  // every wavefront's part of stage s is in LDS
-    const uint4* As = lds[s][0];
-    const uint4* Bs = lds[s][1];
+    const int s = kt % NS;
+    // Loads issued after stage kt's: the stages kt + 1 .. kt + NS - 2 that exist.
+    const int later = min(NS - 2, nk - 1 - kt);
+    if (later >= 2) wait_vm<(NS >= 4 ? 2 : 0) * L>();
+    else if (later == 1) wait_vm<L>();
+    else wait_vm<0>();
+    barrier();  // stage kt is in LDS; every wavefront is done with stage kt - 1
+    if (kt + NS - 1 < nk) load_stage((kt + NS - 1) % NS, (kt + NS - 1) * BK);
+    const uint4* As = lds[s];
+    const uint4* Bs = lds[s] + BM * CPR;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int kc = ks * 2 + khalf;  // this lane's 8 k-values of the step
-      u32x4_t fa[2], fb[2];
+      u32x4_t fa[R], fb[S];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        fa[b] = *reinterpret_cast<const u32x4_t*>(As + swz(wm * 64 + b * 32 + r32, kc));
-        fb[b] = *reinterpret_cast<const u32x4_t*>(Bs + swz(wn * 64 + b * 32 + r32, kc));
-      }
+      for (int a = 0; a < R; ++a)
+        fa[a] = *reinterpret_cast<const u32x4_t*>(
+            As + swz<BK>(wm * (BM / 2) + a * 32 + r32, kc));
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int b = 0; b < S; ++b)
+        fb[b] = *reinterpret_cast<const u32x4_t*>(
+            Bs + swz<BK>(wn * (BN / 2) + b * 32 + r32, kc));
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+      for (int a = 0; a < R; ++a)
+#pragma unroll
+        for (int b = 0; b < S; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(fb[b]), as_bf16(fa[a]),
                                                               acc[a][b], 0, 0, 0);
     }
-    barrier();  // every wavefront is done with stage s before it is refilled
   }
 
   // Epilogue: lane holds, per block, m = r32 and n = 8 j + 4 khalf + (0..3).
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int m = m0 + wm * 64 + a * 32 + r32;
+  for (int a = 0; a < R; ++a) {
+    const int m = m0 + wm * (BM / 2) + a * 32 + r32;
     if (m >= m_eff) continue;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < S; ++b) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * 64 + b * 32 + j * 8 + khalf * 4;
+        const int n = n0 + wn * (BN / 2) + b * 32 + j * 8 + khalf * 4;
         if (n >= g.N) continue;
         const float v0 = acc[a][b][4 * j], v1 = acc[a][b][4 * j + 1];
         const float v2 = acc[a][b][4 * j + 2], v3 = acc[a][b][4 * j + 3];
@@ -188,25 +215,42 @@ __global__ __launch_bounds__(NT, 2) void gemm_nt_kernel(const GemmArgs g) {
 
 }  // namespace
 
+namespace {
+
+template <int BM, int BN, int BK, int NS, int WPE>
+int launch_blocks(int out, const GemmArgs& g, hipStream_t s) {
+  const int64_t tiles = static_cast<int64_t>((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  if (tiles > 0x7fffffffLL) return VSCE_ERR_UNSUPPORTED;
+  const dim3 grid(static_cast<unsigned>(tiles)), block(NT);
+  switch (out) {
+    case kGemmOutBf16:
+      hipLaunchKernelGGL((gemm_nt_kernel<kGemmOutBf16, BM, BN, BK, NS, WPE>), grid, block, 0, s, g);
+      break;
+    case kGemmOutF32:
+      hipLaunchKernelGGL((gemm_nt_kernel<kGemmOutF32, BM, BN, BK, NS, WPE>), grid, block, 0, s, g);
+      break;
+    case kGemmOutF32Add:
+      hipLaunchKernelGGL((gemm_nt_kernel<kGemmOutF32Add, BM, BN, BK, NS, WPE>), grid, block, 0, s, g);
+      break;
+    default: return VSCE_ERR_INVALID;
+  }
+  return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
+}
+
+}  // namespace
+
 int launch_gemm_nt(int out, const GemmArgs& g, hipStream_t s) {
-  if (g.M < 0 || g.N < 0 || g.K < 0 || g.K % BK != 0 || g.N % 4 != 0 || g.ldc % 4 != 0 ||
+  if (g.M < 0 || g.N < 0 || g.K < 0 || g.K % kKMult != 0 || g.N % 4 != 0 || g.ldc % 4 != 0 ||
       g.lda % 8 != 0 || g.ldb % 8 != 0 || g.lda < g.K || g.ldb < g.K || g.ldc < g.N ||
       g.lda > (int64_t(1) << 23) || g.ldb > (int64_t(1) << 23) || g.group_m < 1 ||
       g.a_rows < 0 || g.b_rows < 0)
     return VSCE_ERR_INVALID;
   if (g.M == 0 || g.N == 0) return VSCE_OK;
-  const int64_t tiles = static_cast<int64_t>((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  if (tiles > 0x7fffffffLL) return VSCE_ERR_UNSUPPORTED;
-  const dim3 grid(static_cast<unsigned>(tiles)), block(NT);
-  switch (out) {
-    case kGemmOutBf16: hipLaunchKernelGGL(gemm_nt_kernel<kGemmOutBf16>, grid, block, 0, s, g); break;
-    case kGemmOutF32: hipLaunchKernelGGL(gemm_nt_kernel<kGemmOutF32>, grid, block, 0, s, g); break;
-    case kGemmOutF32Add:
-      hipLaunchKernelGGL(gemm_nt_kernel<kGemmOutF32Add>, grid, block, 0, s, g);
-      break;
-    default: return VSCE_ERR_INVALID;
-  }
-  return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
+  // Large products: 256 x 256 blocks, one per CU, 2 stages of 64 k-values
+  // (128 KB of LDS, 128 x 128 per wavefront); small ones: 128 x 128 blocks,
+  // two per CU, 2 stages of 64.
+  if (g.M >= 256 && g.N >= 256) return launch_blocks<256, 256, 64, 2, 1>(out, g, s);
+  return launch_blocks<128, 128, 64, 2, 2>(out, g, s);
 }
 
 }  // namespace vsce
