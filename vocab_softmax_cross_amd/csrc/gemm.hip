@@ -49,6 +49,16 @@ __device__ __forceinline__ int swz(int row, int kc) {
 // A stage is read with ordinary LDS loads (the compiler places their waits
 // and the MFMA register hazards); the direct-to-LDS loads that fill it are
 // waited for by hand (wait_vm) and published to the workgroup by barrier().
+// 16 bytes per lane straight into LDS (lane i at lds_wave + 16 i) with the
+// default cache policy: unlike the cross-entropy's single pass over the
+// logits, every operand panel is read again by the other tiles of its row or
+// column, so it should stay in L2 and the infinity cache.
+__device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_wave,
+                                           uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave,
+                                           16, voff, 0, 0, 0);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -127,10 +137,10 @@ void gemm_nt_kernel(const GemmArgs g) {
     const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
 #pragma unroll
     for (int i = 0; i < LA; ++i)
-      buf_load16_lds(ra, &lds[s][(wave * LA + i) * kWave], offa[i] + kb, 0);
+      load16_lds(ra, &lds[s][(wave * LA + i) * kWave], offa[i] + kb);
 #pragma unroll
     for (int i = 0; i < LB; ++i)
-      buf_load16_lds(rb, &lds[s][BM * CPR + (wave * LB + i) * kWave], offb[i] + kb, 0);
+      load16_lds(rb, &lds[s][BM * CPR + (wave * LB + i) * kWave], offb[i] + kb);
   };
 
   const int wm = wave >> 1, wn = wave & 1;  // this wavefront's quarter
