@@ -59,6 +59,17 @@ __device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_w
                                            16, voff, 0, 0, 0);
 }
 
+// A buffer resource from values every lane holds, passed through
+// readfirstlane so that the compiler keeps it in scalar registers (otherwise
+// it may treat it as per-lane and wrap every load in a loop over lanes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bytes));
+  return make_rsrc(reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo), n);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -116,10 +127,10 @@ void gemm_nt_kernel(const GemmArgs g) {
 
   // One resource per operand tile: rows past those in memory read as zeros.
   const int rows_a = max(0, min(BM, g.a_rows - m0)), rows_b = max(0, min(BN, g.b_rows - n0));
-  const auto ra = make_rsrc(static_cast<const uint16_t*>(g.A) + static_cast<int64_t>(m0) * g.lda,
-                            static_cast<uint32_t>(rows_a * g.lda * 2));
-  const auto rb = make_rsrc(static_cast<const uint16_t*>(g.B) + static_cast<int64_t>(n0) * g.ldb,
-                            static_cast<uint32_t>(rows_b * g.ldb * 2));
+  const auto ra = uniform_rsrc(
+      static_cast<const uint16_t*>(g.A) + static_cast<int64_t>(m0) * g.lda, rows_a * g.lda * 2);
+  const auto rb = uniform_rsrc(
+      static_cast<const uint16_t*>(g.B) + static_cast<int64_t>(n0) * g.ldb, rows_b * g.ldb * 2);
   // This lane's chunk of each of the wavefront's loads: chunk j = q 64 + lane
   // of an operand's stage is LDS position j, which swz() assigns to (row
   // j / CPR, k-chunk (j mod CPR) xor f(row)); the XOR is its own inverse.
