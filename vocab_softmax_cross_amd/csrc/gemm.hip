@@ -33,17 +33,20 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kKMult = 64, NT = 256;  // K must be a multiple of kKMult
+constexpr int kKMult = 64;  // K must be a multiple of kKMult
 
 // LDS chunk of (row, 16-byte k-chunk kc) in a stage whose rows hold BK
-// k-values (BK / 8 chunks).  The chunk index is XOR-ed with a function of the
-// row so that 8 consecutive rows read at one kc hit 8 different 16-byte slots
-// of a 128-byte bank line: rows of 128 bytes (BK 64) use row mod 8; rows of
-// 64 bytes (BK 32, two per line) use (row / 2) mod 4.
+// k-values (BK / 8 chunks).  A 16-byte-per-lane LDS read is served 16 lanes
+// at a time across 64 four-byte banks (a 256-byte window; the bank-conflict
+// counter confirms it), and an MFMA operand read has 16 consecutive rows at
+// one kc in each such group.  The chunk index is XOR-ed with a function of
+// the row so that those 16 rows fill the 16 slots of the window: rows of 128
+// bytes (BK 64, two per window) use (row / 2) mod 8; rows of 64 bytes (BK 32,
+// four per window) use (row / 4) mod 4.
 template <int BK>
 __device__ __forceinline__ int swz(int row, int kc) {
-  if constexpr (BK == 64) return row * 8 + (kc ^ (row & 7));
-  else return row * 4 + (kc ^ ((row >> 1) & 3));
+  if constexpr (BK == 64) return row * 8 + (kc ^ ((row >> 1) & 7));
+  else return row * 4 + (kc ^ ((row >> 2) & 3));
 }
 
 // A stage is read with ordinary LDS loads (the compiler places their waits
@@ -100,15 +103,17 @@ __device__ __forceinline__ void tile_of(int64_t t, int tiles_m, int tiles_n, int
   tn = in / gm;
 }
 
-// BM x BN block, four wavefronts as 2 x 2, each a (BM / 2) x (BN / 2) quarter
-// of R x S 32 x 32 MFMA blocks; NS LDS stages of BK k-values (NS - 1 of them
-// in flight while one is multiplied); WPE wavefronts per SIMD to compile for.
-template <int OUT, int BM, int BN, int BK, int NS, int WPE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
+// BM x BN block, WGM x WGN wavefronts, each a (BM / WGM) x (BN / WGN) part of
+// R x S 32 x 32 MFMA blocks; NS LDS stages of BK k-values (NS - 1 of them in
+// flight while one is multiplied); WPE wavefronts per SIMD to compile for.
+template <int OUT, int BM, int BN, int BK, int NS, int WGM, int WGN, int WPE>
+__global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void gemm_nt_kernel(const GemmArgs g) {
-  constexpr int R = BM / 64, S = BN / 64;
+  constexpr int NW = WGM * WGN, NT = NW * 64;
+  constexpr int R = BM / (32 * WGM), S = BN / (32 * WGN);
   constexpr int CPR = BK / 8;                      // 16-byte chunks per tile row
-  constexpr int LA = BM * CPR / (4 * kWave), LB = BN * CPR / (4 * kWave);
+  constexpr int LA = BM * CPR / NT, LB = BN * CPR / NT;
+  static_assert(LA * NT == BM * CPR && LB * NT == BN * CPR, "loads per wavefront");
   constexpr int L = LA + LB;                       // loads per wavefront per stage
   static_assert(NS >= 2 && NS <= 4 && (NS - 2) * L <= 63, "stages");
   __shared__ uint4 lds[NS][(BM + BN) * CPR];       // [stage][A rows, then B rows][chunk]
@@ -154,7 +159,7 @@ void gemm_nt_kernel(const GemmArgs g) {
       load16_lds(rb, &lds[s][BM * CPR + (wave * LB + i) * kWave], offb[i] + kb);
   };
 
-  const int wm = wave >> 1, wn = wave & 1;  // this wavefront's quarter
+  const int wm = wave / WGN, wn = wave % WGN;  // this wavefront's part
   const int r32 = lane & 31, khalf = lane >> 5;
   f32x16 acc[R][S];
 #pragma unroll
@@ -186,11 +191,11 @@ void gemm_nt_kernel(const GemmArgs g) {
 #pragma unroll
       for (int a = 0; a < R; ++a)
         fa[a] = *reinterpret_cast<const u32x4_t*>(
-            As + swz<BK>(wm * (BM / 2) + a * 32 + r32, kc));
+            As + swz<BK>(wm * (BM / WGM) + a * 32 + r32, kc));
 #pragma unroll
       for (int b = 0; b < S; ++b)
         fb[b] = *reinterpret_cast<const u32x4_t*>(
-            Bs + swz<BK>(wn * (BN / 2) + b * 32 + r32, kc));
+            Bs + swz<BK>(wn * (BN / WGN) + b * 32 + r32, kc));
 #pragma unroll
       for (int a = 0; a < R; ++a)
 #pragma unroll
@@ -203,13 +208,13 @@ void gemm_nt_kernel(const GemmArgs g) {
   // Epilogue: lane holds, per block, m = r32 and n = 8 j + 4 khalf + (0..3).
 #pragma unroll
   for (int a = 0; a < R; ++a) {
-    const int m = m0 + wm * (BM / 2) + a * 32 + r32;
+    const int m = m0 + wm * (BM / WGM) + a * 32 + r32;
     if (m >= m_eff) continue;
 #pragma unroll
     for (int b = 0; b < S; ++b) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * (BN / 2) + b * 32 + j * 8 + khalf * 4;
+        const int n = n0 + wn * (BN / WGN) + b * 32 + j * 8 + khalf * 4;
         if (n >= g.N) continue;
         const float v0 = acc[a][b][4 * j], v1 = acc[a][b][4 * j + 1];
         const float v2 = acc[a][b][4 * j + 2], v3 = acc[a][b][4 * j + 3];
@@ -238,20 +243,20 @@ void gemm_nt_kernel(const GemmArgs g) {
 
 namespace {
 
-template <int BM, int BN, int BK, int NS, int WPE>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, int WPE>
 int launch_blocks(int out, const GemmArgs& g, hipStream_t s) {
   const int64_t tiles = static_cast<int64_t>((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   if (tiles > 0x7fffffffLL) return VSCE_ERR_UNSUPPORTED;
-  const dim3 grid(static_cast<unsigned>(tiles)), block(NT);
+  const dim3 grid(static_cast<unsigned>(tiles)), block(WGM * WGN * 64);
   switch (out) {
     case kGemmOutBf16:
-      hipLaunchKernelGGL((gemm_nt_kernel<kGemmOutBf16, BM, BN, BK, NS, WPE>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((gemm_nt_kernel<kGemmOutBf16, BM, BN, BK, NS, WGM, WGN, WPE>), grid, block, 0, s, g);
       break;
     case kGemmOutF32:
-      hipLaunchKernelGGL((gemm_nt_kernel<kGemmOutF32, BM, BN, BK, NS, WPE>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((gemm_nt_kernel<kGemmOutF32, BM, BN, BK, NS, WGM, WGN, WPE>), grid, block, 0, s, g);
       break;
     case kGemmOutF32Add:
-      hipLaunchKernelGGL((gemm_nt_kernel<kGemmOutF32Add, BM, BN, BK, NS, WPE>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((gemm_nt_kernel<kGemmOutF32Add, BM, BN, BK, NS, WGM, WGN, WPE>), grid, block, 0, s, g);
       break;
     default: return VSCE_ERR_INVALID;
   }
@@ -270,8 +275,8 @@ int launch_gemm_nt(int out, const GemmArgs& g, hipStream_t s) {
   // Large products: 256 x 256 blocks, one per CU, 2 stages of 64 k-values
   // (128 KB of LDS, 128 x 128 per wavefront); small ones: 128 x 128 blocks,
   // two per CU, 2 stages of 64.
-  if (g.M >= 256 && g.N >= 256) return launch_blocks<256, 256, 64, 2, 1>(out, g, s);
-  return launch_blocks<128, 128, 64, 2, 2>(out, g, s);
+  if (g.M >= 256 && g.N >= 256) return launch_blocks<256, 256, 64, 2, 2, 4, 2>(out, g, s);
+  return launch_blocks<128, 128, 64, 2, 2, 2, 2>(out, g, s);
 }
 
 }  // namespace vsce
