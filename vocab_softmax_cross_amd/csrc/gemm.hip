@@ -275,7 +275,7 @@ int launch_gemm_nt(int out, const GemmArgs& g, hipStream_t s) {
   // Large products: 256 x 256 blocks, one per CU, 2 stages of 64 k-values
   // (128 KB of LDS, 128 x 128 per wavefront); small ones: 128 x 128 blocks,
   // two per CU, 2 stages of 64.
-  if (g.M >= 256 && g.N >= 256) return launch_blocks<256, 256, 64, 2, 2, 4, 2>(out, g, s);
+  if (g.M >= 256 && g.N >= 256) return launch_blocks<256, 256, 64, 2, 4, 4, 4>(out, g, s);
   return launch_blocks<128, 128, 64, 2, 2, 2, 2>(out, g, s);
 }
 
