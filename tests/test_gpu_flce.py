@@ -257,3 +257,39 @@ def test_flce_all_rows_ignored():
     torch.cuda.synchronize()
     assert float(out["loss"]) == 0.0
     assert torch.all(out["grad_hidden"] == 0) and torch.all(out["grad_weight"] == 0)
+
+
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_flce_rows_off_vectors_weighted_capped_per_row_grad_output(chunk):
+    """V = 999 is not a multiple of 8, so the chunk's cross-entropy takes the
+    statistics + gradient pair instead of the on-chip kernel; with class
+    weights, soft-cap, z-loss and a grad_output per row (reduction none)."""
+    h, W, t, cw = _problem(15, 150, 128, 999, weighted=True, ignore_frac=0.25)
+    _note(f"flce V=999 chunk={chunk}")
+    dev = h.device
+    go = torch.linspace(0.25, 2.0, 150, device=dev)
+    kw = dict(softcap=25.0, z_loss=1e-3)
+    out = vf.flce_forward_backward(h, W, torch.from_numpy(t).to(dev),
+                                   torch.from_numpy(cw).to(dev), -100, 0.1, "none",
+                                   chunk_rows=chunk, grad_output=go, row_loss=True,
+                                   return_z_loss=True, **kw)
+    torch.cuda.synchronize()
+    h64, W64 = _f64(h), _f64(W)
+    ref = oracle.flce(h64, W64, t, cw.astype(np.float64), -100, 0.1, "none",
+                      go.cpu().numpy().astype(np.float64), 25.0, 1e-3)
+    valid = t != -100
+    z = ref.logits
+    dz = 0.5 * _ulp_bf16(np.abs(z)) + 128 * U32 * (np.abs(h64) @ np.abs(W64).T)
+    tol = (3.0 + 2e-3 * (np.abs(z).max(axis=1) + np.log(999.0))) * dz.max(axis=1) \
+        + 1e-5 * np.abs(ref.ce.row_loss)
+    got = out["loss"].cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref.ce.row_loss)[valid] <= tol[valid])
+    assert np.all(got[~valid] == 0.0)
+    zl = out["z_loss"].cpu().numpy().astype(np.float64)
+    z_tol = 2 * 2e-3 * (np.abs(z).max(axis=1) + 7) * dz.max(axis=1) + 1e-5 * np.abs(ref.ce.z_loss)
+    assert np.all((np.abs(zl - ref.ce.z_loss) <= z_tol)[valid])
+    gh = _f64(out["grad_hidden"])
+    assert np.all(gh[~valid] == 0.0)
+    assert np.max(np.abs(gh - ref.grad_hidden)) <= 0.05 * np.abs(ref.grad_hidden).max()
+    gw = out["grad_weight"].cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(gw - ref.grad_weight)) <= 0.05 * np.abs(ref.grad_weight).max()
