@@ -211,7 +211,27 @@ def long_rows_mode(L, W, hip, dev, stream, K):
     return res
 
 
-def flce_mode(L, W, hip, dev, stream, K):
+def cpu_baseline_flce(sample):
+    """The FLCE oracle (fp64: z = h W^T, the cross-entropy, G W and G^T h)
+    on the first rows of the FLCE mode's own inputs; rows per second."""
+    import numpy as np
+    import oracle
+    h, w, t = sample
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except ImportError:
+        cores = os.cpu_count()
+    t0 = time.perf_counter()
+    oracle.flce(h, w, t, None, -100, 0.1, "mean")
+    spent = time.perf_counter() - t0
+    return {"value": len(t) / spent, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {len(t)} rows of the FLCE mode's inputs (H={h.shape[1]}, "
+                      f"V={w.shape[0]}), fp64 logits, cross-entropy and both gradients, "
+                      f"{spent:.1f} s"}
+
+
+def flce_mode(L, W, hip, dev, stream, K, sample_rows=0):
     """The linear head fused with the cross-entropy at the pages' FLCE size
     (BT=8192, H=4096, V=128256 bf16; the headline workload's targets, 410
     ignored rows, smoothing 0.1, mean): flce_forward_backward per call, and
@@ -268,9 +288,13 @@ def flce_mode(L, W, hip, dev, stream, K):
         torch.cuda.synchronize()
         t_ms = hip.launch_ms(fn, reps, stream)
         res[name] = {"ms": round(t_ms, 3), "TFLOPs": round(one / t_ms / 1e9, 1)}
+    sample = None
+    if sample_rows:  # the oracle's sample: the same rows and weights, upcast exactly
+        sample = (hidden[:sample_rows].double().cpu().numpy(), weight.double().cpu().numpy(),
+                  tgt[:sample_rows].copy())
     del a, wt, at, ht, zl, dh, ws, gw, gh, weight, hidden
     torch.cuda.empty_cache()
-    return res
+    return res, sample
 
 
 def main():
@@ -396,6 +420,7 @@ def main():
     achieved = kernel_bytes / mean_kernel_s / 1e9
 
     extra = {}
+    flce_sample = None
     if not args.no_extra_modes:
         go37 = torch.full((1,), 0.37, dtype=torch.float32, device=dev)
         w37 = timed(fused_step, go37)
@@ -460,7 +485,8 @@ def main():
             "backward_GBps": round((n_valid + wl.BT) * shard_row / t_bwd / 1e6, 1),
             "rank_kernels_ms": round(t_stats + t_merge + t_bwd, 4)}
         extra["fused_long_rows"] = long_rows_mode(L, W, hip, dev, stream, K)
-        extra["flce"] = flce_mode(L, W, hip, dev, stream, K)
+        extra["flce"], flce_sample = flce_mode(L, W, hip, dev, stream, K,
+                                               0 if args.no_cpu_baseline else 16)
         extra[f"fused_softcap{CAP:g}_zloss{ZL:g}"] = {
             "ms_per_step": round(wcap / K * 1e3, 4),
             "rows_per_s": round(wl.BT * K / wcap, 1),
@@ -486,10 +512,12 @@ def main():
         hip.destroy(a)
         hip.destroy(b)
 
-    cpu = cpu1 = None
+    cpu = cpu1 = cpu_flce = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, tgt, args.cpu_seconds)
         cpu1 = cpu_baseline(wl, tgt, args.cpu_seconds / 3, threads=1)
+        if flce_sample is not None:
+            cpu_flce = cpu_baseline_flce(flce_sample)
 
     line = {
         "metric": "fwd+bwd rows/s and HBM GB/s (% of peak) at BT=8192, V=128256 bf16",
@@ -518,6 +546,7 @@ def main():
         "copy_ceiling": copy_ceiling,
         "cpu_baseline": cpu,
         "cpu_baseline_1thread": cpu1,
+        "cpu_baseline_flce": cpu_flce,
         "input_gen_s": round(gen_s, 1),
         "ring_buffers": ring_n,
     }

@@ -293,3 +293,61 @@ def test_flce_rows_off_vectors_weighted_capped_per_row_grad_output(chunk):
     assert np.max(np.abs(gh - ref.grad_hidden)) <= 0.05 * np.abs(ref.grad_hidden).max()
     gw = out["grad_weight"].cpu().numpy().astype(np.float64)
     assert np.max(np.abs(gw - ref.grad_weight)) <= 0.05 * np.abs(ref.grad_weight).max()
+
+
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_flce_no_host_sync(reduction):
+    """flce_forward_backward under torch's sync debug mode "error": the
+    compaction's count and every normalizer stay on the device."""
+    h, W, t, cw = _problem(16, 200, 128, 640, weighted=True)
+    dev = h.device
+    tt = torch.from_numpy(t).to(dev)
+    cwt = torch.from_numpy(cw).to(dev)
+    go = torch.full((200,), 0.5, device=dev) if reduction == "none" else \
+        torch.tensor(0.5, device=dev)
+    torch.cuda.synchronize()
+    torch.cuda.set_sync_debug_mode("error")
+    try:
+        out = vf.flce_forward_backward(h, W, tt, cwt, -100, 0.1, reduction, chunk_rows=64,
+                                       grad_output=go)
+    finally:
+        torch.cuda.set_sync_debug_mode("default")
+    torch.cuda.synchronize()
+    ref = oracle.flce(_f64(h), _f64(W), t, cw.astype(np.float64), -100, 0.1, reduction,
+                      0.5 if reduction != "none" else np.full(200, 0.5))
+    gw = out["grad_weight"].cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(gw - ref.grad_weight)) <= 0.05 * np.abs(ref.grad_weight).max()
+
+
+def test_flce_graph_capture_replays_match_eager():
+    """The whole FLCE captured in a HIP graph: every replay (with eager work
+    and synchronizations in between) equals the eager result bit for bit."""
+    h, W, t, _ = _problem(17, 300, 128, 1000)
+    dev = h.device
+    tt = torch.from_numpy(t).to(dev)
+    eager = vf.flce_forward_backward(h, W, tt, None, -100, 0.1, "mean", chunk_rows=128)
+    torch.cuda.synchronize()
+    e_loss, e_gh, e_gw = (eager["loss"].clone(), eager["grad_hidden"].clone(),
+                          eager["grad_weight"].clone())
+    ws = eager["workspace"]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        vf.flce_forward_backward(h, W, tt, None, -100, 0.1, "mean", chunk_rows=128,
+                                 workspace=ws)  # warm-up
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        res = vf.flce_forward_backward(h, W, tt, None, -100, 0.1, "mean", chunk_rows=128,
+                                       workspace=ws)
+    for _ in range(3):
+        res["grad_weight"].fill_(7.0)
+        res["grad_hidden"].fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(res["loss"], e_loss)
+        assert torch.equal(res["grad_hidden"], e_gh)
+        assert torch.equal(res["grad_weight"], e_gw)
+        _ = (h.float() * 2).sum()  # unrelated eager work between replays
