@@ -486,7 +486,7 @@ def main():
             "rank_kernels_ms": round(t_stats + t_merge + t_bwd, 4)}
         extra["fused_long_rows"] = long_rows_mode(L, W, hip, dev, stream, K)
         extra["flce"], flce_sample = flce_mode(L, W, hip, dev, stream, K,
-                                               0 if args.no_cpu_baseline else 16)
+                                               0 if args.no_cpu_baseline else 64)
         extra[f"fused_softcap{CAP:g}_zloss{ZL:g}"] = {
             "ms_per_step": round(wcap / K * 1e3, 4),
             "rows_per_s": round(wl.BT * K / wcap, 1),
