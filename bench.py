@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-modes", action="store_true",
                     help="skip the split-mode and grad_output != 1 context timings")
+    ap.add_argument("--flce-only", action="store_true",
+                    help="run only the FLCE measurement (a short run for profiling) and print "
+                         "its JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle time budget for the cpu_baseline sample")
     return ap.parse_args()
@@ -320,6 +323,11 @@ def main():
     torch.empty(1, device=dev)
     torch.cuda.synchronize()
     L.load()
+    if args.flce_only:
+        res, _ = flce_mode(L, W, Hip(), dev, torch.cuda.current_stream(dev).cuda_stream,
+                           args.steps)
+        print(json.dumps({"flce": res}), flush=True)
+        return
     wl = W.WORKLOADS[args.workload]
     K, Wu = args.steps, args.warmup
     tgt = W.targets(wl)
