@@ -240,7 +240,8 @@ def _sample_rows(BT, k=24, seed=0):
     return np.sort(np.concatenate([r, [0, BT - 1]]))
 
 
-@pytest.mark.parametrize("mode,go", [("fused", 1.0), ("split", 0.37)])
+@pytest.mark.parametrize("mode,go", [("fused", 1.0), ("split", 0.37), ("fused", 0.37),
+                                     ("split", 1.0)])
 def test_llm_head_full_size(mode, go):
     """BT = 8192, V = 128256 bf16 in the launch configuration the benchmark
     times: every row loss, the reduced loss and the statistics checked, the
