@@ -3,17 +3,18 @@
 // (Liger-Kernel PR #1622, FLCE: logits = h W^T, dL/dh = G W, dL/dW = G^T h,
 // each arranged so that both operands are contiguous along k).
 //
-// One workgroup of 256 threads computes a 256 x 256 block of C (128 x 128
-// for small products).  Its four wavefronts each own a quarter, as 4 x 4 (or
-// 2 x 2) blocks of v_mfma_f32_32x32x16_bf16 with fp32 accumulators: a larger
-// quarter reads fewer operand bytes from LDS per MFMA.  k advances 64 at a
-// time through two LDS stages of A and B (32 KB each for 256 rows): the next
-// stage is loaded straight into LDS (buffer_load_dwordx4 ... lds) while the
-// current one is multiplied.  In LDS each tile row is 8 chunks of 16 bytes, the chunk
-// index XOR-ed with the row (mod 8), so that the 32 rows one MFMA operand
-// reads sit in different banks; the swizzle is applied by choosing which
-// global chunk each lane loads, since a direct-to-LDS load writes lane i at
-// base + 16 i.
+// Large products: one workgroup of 16 wavefronts (1024 threads, one per CU,
+// four per SIMD) computes a 256 x 256 block of C, each wavefront a 64 x 64
+// part as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
+// Small products (M or N below 256): 128 x 128 blocks of 4 wavefronts, two
+// workgroups per CU.  k advances 64 at a time through two LDS stages of A and
+// B (64 KB per stage for 256 x 256): the next stage is loaded straight into
+// LDS (buffer_load_dwordx4 ... lds) while the current one is multiplied, with
+// one workgroup barrier per stage.  In LDS each tile row is 8 chunks of 16
+// bytes, the chunk index XOR-ed with a function of the row (swz below) so the
+// rows one MFMA operand read touches sit in different banks; the swizzle is
+// applied by choosing which global chunk each lane loads, since a
+// direct-to-LDS load writes lane i at base + 16 i.
 //
 // Operand lane layout of the 32x32x16 bf16 MFMA (checked on the hardware):
 // lane l supplies row l mod 32 and the 8 k-values 8 (l / 32) .. + 7 of each
