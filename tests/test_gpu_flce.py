@@ -351,3 +351,57 @@ def test_flce_graph_capture_replays_match_eager():
         assert torch.equal(res["grad_hidden"], e_gh)
         assert torch.equal(res["grad_weight"], e_gw)
         _ = (h.float() * 2).sum()  # unrelated eager work between replays
+
+
+def test_flce_empty_batch():
+    """No rows: the mean is NaN (0/0), dL/dW is zero, nothing else is written."""
+    dev = _dev()
+    rng = np.random.default_rng(18)
+    h = torch.empty((0, 128), dtype=torch.bfloat16, device=dev)
+    W = _bf16(rng, (300, 128), 0.2, dev)
+    t = torch.empty(0, dtype=torch.int64, device=dev)
+    out = vf.flce_forward_backward(h, W, t, None, -100, 0.0, "mean")
+    torch.cuda.synchronize()
+    assert np.isnan(float(out["loss"]))
+    assert torch.all(out["grad_weight"] == 0)
+
+
+def test_flce_one_class():
+    """V = 1: the loss and both gradients are 0 (the softmax of one logit is
+    1); the row takes the per-element path of the cross-entropy."""
+    dev = _dev()
+    rng = np.random.default_rng(19)
+    h = _bf16(rng, (40, 64), 1.0, dev)
+    W = _bf16(rng, (1, 64), 1.0, dev)
+    t = torch.zeros(40, dtype=torch.int64, device=dev)
+    out = vf.flce_forward_backward(h, W, t, None, -100, 0.1, "sum", row_loss=True)
+    torch.cuda.synchronize()
+    assert float(out["loss"]) == 0.0
+    assert torch.all(out["row_loss"] == 0)
+    assert torch.all(out["grad_hidden"] == 0) and torch.all(out["grad_weight"] == 0)
+
+
+def test_flce_bad_target_is_flagged():
+    """A target outside [0, V) that is not ignore_index: kept by the
+    compaction so the cross-entropy flags it (status bit, NaN row loss, zero
+    gradient row), and the mean is NaN."""
+    h, W, t, _ = _problem(20, 64, 128, 256, ignore_frac=0.1)
+    t = t.copy()
+    t[5] = 256 + 7
+    dev = h.device
+    out = vf.flce_forward_backward(h, W, torch.from_numpy(t).to(dev), None, -100, 0.0, "mean",
+                                   row_loss=True)
+    torch.cuda.synchronize()
+    st = vf.status(out["workspace"])
+    assert st["status"] & 1 and st["n_invalid"] == 1
+    assert np.isnan(float(out["loss"]))
+    rl = out["row_loss"].cpu().numpy()
+    assert np.isnan(rl[5]) and np.all(np.isfinite(np.delete(rl, 5)))
+    assert torch.all(out["grad_hidden"][5] == 0)
+    # the other rows' gradients are those of the batch without row 5 and
+    # with W = the valid count (the bad row is out of the mean)
+    keep = np.ones(64, bool)
+    keep[5] = False
+    ref = oracle.flce(_f64(h)[keep], _f64(W), t[keep], None, -100, 0.0, "mean")
+    gh = _f64(out["grad_hidden"])[keep]
+    assert np.max(np.abs(gh - ref.grad_hidden)) <= 0.05 * np.abs(ref.grad_hidden).max()
