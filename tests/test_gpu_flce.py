@@ -405,3 +405,48 @@ def test_flce_bad_target_is_flagged():
     ref = oracle.flce(_f64(h)[keep], _f64(W), t[keep], None, -100, 0.0, "mean")
     gh = _f64(out["grad_hidden"])[keep]
     assert np.max(np.abs(gh - ref.grad_hidden)) <= 0.05 * np.abs(ref.grad_hidden).max()
+
+
+# ---------------------------------------------------------------- the autograd wrapper
+
+def test_linear_cross_entropy_autograd_mean():
+    """loss.backward(0.5): the gradients equal the FLCE's with grad_output 0.5
+    bit for bit (a power-of-two scale commutes with every rounding), dL/dW
+    cast by autograd to the weight's bf16."""
+    from vocab_softmax_cross_amd import linear_cross_entropy
+    h, W, t, cw = _problem(21, 200, 128, 640, weighted=True)
+    dev = h.device
+    tt = torch.from_numpy(t).to(dev)
+    cwt = torch.from_numpy(cw).to(dev)
+    hg = h.clone().requires_grad_(True)
+    Wg = W.clone().requires_grad_(True)
+    loss = linear_cross_entropy(hg, Wg, tt, cwt, -100, 0.1, "mean")
+    loss.backward(torch.tensor(0.5, device=dev))
+    ref = vf.flce_forward_backward(h, W, tt, cwt, -100, 0.1, "mean",
+                                   grad_output=torch.tensor(0.5, device=dev))
+    torch.cuda.synchronize()
+    assert float(loss) == float(ref["loss"])
+    assert torch.equal(hg.grad, ref["grad_hidden"])
+    assert torch.equal(Wg.grad, ref["grad_weight"].to(torch.bfloat16))
+    with pytest.raises(RuntimeError):
+        loss2 = linear_cross_entropy(h.clone().requires_grad_(True), W, tt, None)
+        loss2.backward(retain_graph=True)
+        loss2.backward()
+
+
+def test_linear_cross_entropy_autograd_none_per_row():
+    from vocab_softmax_cross_amd import linear_cross_entropy
+    h, W, t, _ = _problem(22, 150, 64, 512)
+    dev = h.device
+    tt = torch.from_numpy(t).to(dev)
+    go = torch.linspace(0.1, 2.0, 150, device=dev)
+    hg = h.clone().requires_grad_(True)
+    Wg = W.clone().requires_grad_(True)
+    loss = linear_cross_entropy(hg, Wg, tt, None, -100, 0.0, "none", chunk_rows=64)
+    loss.backward(go)
+    ref = vf.flce_forward_backward(h, W, tt, None, -100, 0.0, "none", chunk_rows=64,
+                                   grad_output=go)
+    torch.cuda.synchronize()
+    assert torch.equal(loss.detach(), ref["loss"])
+    assert torch.equal(hg.grad, ref["grad_hidden"])
+    assert torch.equal(Wg.grad, ref["grad_weight"].to(torch.bfloat16))

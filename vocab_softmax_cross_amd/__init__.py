@@ -6,9 +6,13 @@ ABI), exposes it to PyTorch (``functional``) and builds it (``build``).
 """
 from .functional import (
     FusedCrossEntropy,
+    LinearCrossEntropy,
     SplitCrossEntropy,
     backward_from_stats,
     cross_entropy,
+    flce_forward_backward,
+    gemm_bf16_nt,
+    linear_cross_entropy,
     forward_fused_inplace,
     forward_stats,
     scale_grad,
@@ -17,6 +21,9 @@ from .functional import (
 
 __all__ = [
     "cross_entropy",
+    "linear_cross_entropy",
+    "flce_forward_backward",
+    "gemm_bf16_nt",
     "forward_fused_inplace",
     "forward_stats",
     "backward_from_stats",
@@ -24,4 +31,5 @@ __all__ = [
     "status",
     "FusedCrossEntropy",
     "SplitCrossEntropy",
+    "LinearCrossEntropy",
 ]

@@ -443,3 +443,58 @@ def flce_forward_backward(hidden: torch.Tensor, weight: torch.Tensor, target: to
     res["grad_hidden"], res["grad_weight"] = gh, gw
     res["workspace"] = ws
     return res
+
+
+class LinearCrossEntropy(torch.autograd.Function):
+    """The FLCE: loss of cross_entropy(hidden @ weight.T), both gradients
+    computed in the forward (for grad_output 1) and scaled in place by the
+    backward's scalar grad_output.  With reduction "none" and a grad_output
+    per row, the backward runs the FLCE again with that grad_output (dL/dW
+    mixes rows, so a per-row scale cannot be applied afterwards)."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, target, class_weight, ignore_index, label_smoothing,
+                reduction, softcap, z_loss, chunk_rows):
+        res = flce_forward_backward(hidden, weight, target, class_weight, ignore_index,
+                                    label_smoothing, reduction, softcap, z_loss, chunk_rows)
+        ctx.save_for_backward(hidden, weight, target,
+                              *([] if class_weight is None else [class_weight]))
+        ctx.args = (ignore_index, label_smoothing, reduction, softcap, z_loss, chunk_rows,
+                    class_weight is not None)
+        ctx.grads = (res["grad_hidden"], res["grad_weight"])
+        ctx.used = False
+        return res["loss"]
+
+    @staticmethod
+    def backward(ctx, grad_loss):
+        if ctx.used:
+            raise RuntimeError("the FLCE gradients were already scaled in place; a second "
+                               "backward (retain_graph=True) is not supported")
+        ctx.used = True
+        ignore_index, ls, reduction, softcap, z_loss, chunk_rows, weighted = ctx.args
+        gh, gw = ctx.grads
+        ctx.grads = None
+        if reduction == "none" and grad_loss.numel() > 1:
+            hidden, weight, target, *cw = ctx.saved_tensors
+            res = flce_forward_backward(hidden, weight, target, cw[0] if weighted else None,
+                                        ignore_index, ls, reduction, softcap, z_loss,
+                                        chunk_rows, grad_output=grad_loss)
+            gh, gw = res["grad_hidden"], res["grad_weight"]
+        else:
+            scale_grad(gh, grad_loss.reshape(1), "mean", skip_if_one=True)
+            scale_grad(gw, grad_loss.reshape(1), "mean", skip_if_one=True)
+        return (gh, gw) + (None,) * 8
+
+
+def linear_cross_entropy(hidden: torch.Tensor, weight: torch.Tensor, target: torch.Tensor,
+                         class_weight: Optional[torch.Tensor] = None, ignore_index: int = -100,
+                         label_smoothing: float = 0.0, reduction: str = "mean", *,
+                         softcap: float = 0.0, z_loss: float = 0.0, chunk_rows: int = 0):
+    """cross_entropy(hidden @ weight.T, target) without materialising more
+    than one chunk of logits (bf16 hidden [BT, H] and weight [V, H]); autograd
+    gives dL/dhidden (bf16) and dL/dweight (computed in fp32, cast by autograd
+    to the weight's type)."""
+    if reduction not in L.REDUCTIONS:
+        raise ValueError(f"reduction must be one of {tuple(L.REDUCTIONS)}")
+    return LinearCrossEntropy.apply(hidden, weight, target, class_weight, ignore_index,
+                                    label_smoothing, reduction, softcap, z_loss, chunk_rows)
