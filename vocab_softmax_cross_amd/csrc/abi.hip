@@ -95,6 +95,8 @@ void problem_args(const Prob& p, RowArgs& a) {
   a.rows = p.rows;
 }
 
+int64_t stats_scratch_offset(int64_t rows) { return VSCE_WS_HEADER_BYTES + 3 * align_up(4 * rows); }
+
 namespace {
 
 // The entry points that see whole rows (loss, fused gradient) take no shard.
@@ -114,7 +116,6 @@ int check_outputs(const vsce_outputs* out) {
 // accuracies and the z-losses (each used when the caller's outputs do not take
 // its place), then [rows] float4 statistics (the fused mode's rows that are
 // read twice).
-int64_t stats_scratch_offset(int64_t rows) { return VSCE_WS_HEADER_BYTES + 3 * align_up(4 * rows); }
 
 // Per-row destinations of the forward kernels.
 RowArgs row_args(const Prob& p, void* x, const vsce_outputs* out, void* workspace) {

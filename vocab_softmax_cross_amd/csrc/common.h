@@ -285,10 +285,22 @@ __device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint
 }
 // 16 bytes per lane straight into LDS; lane i of the wavefront lands at
 // lds_wave + 16 i, so `lds_wave` must be the same for the whole wavefront.
+// POLICY: kNT for a stream read once; 0 (default) for data other workgroups
+// read again.
+template <int POLICY = kNT>
 __device__ inline void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_wave, uint32_t voff,
                                       uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave,
-                                           16, voff, soff, 0, kNT);
+                                           16, voff, soff, 0, POLICY);
+}
+
+// Waits until at most N vector-memory operations of this wavefront are still
+// outstanding.  The counter covers loads (those into LDS too) and stores, and
+// they leave it in the order they were issued.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "the counter holds 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Plain-pointer 16-byte loads and stores with the same non-temporal policy.

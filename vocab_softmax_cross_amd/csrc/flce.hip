@@ -354,8 +354,7 @@ int flce_forward_backward(const vsce_flce_problem* fp, const void* hidden, const
     a.ws = hdr;
     rc = launch_fused_resident(p, a, stream);
     if (rc == VSCE_ERR_UNSUPPORTED) {  // rows too long for the chip: read twice
-      a.stats = reinterpret_cast<float*>(ws + Lw.ce + VSCE_WS_HEADER_BYTES +
-                                         3 * al(4 * Lw.R));
+      a.stats = reinterpret_cast<float*>(ws + Lw.ce + stats_scratch_offset(Lw.R));
       rc = launch_stats(p, a, stream);
       if (rc == VSCE_OK) {
         RowArgs b = a;

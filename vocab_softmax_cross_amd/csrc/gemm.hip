@@ -53,14 +53,13 @@ __device__ __forceinline__ int swz(int row, int kc) {
 // A stage is read with ordinary LDS loads (the compiler places their waits
 // and the MFMA register hazards); the direct-to-LDS loads that fill it are
 // waited for by hand (wait_vm) and published to the workgroup by barrier().
-// 16 bytes per lane straight into LDS (lane i at lds_wave + 16 i) with the
-// default cache policy: unlike the cross-entropy's single pass over the
-// logits, every operand panel is read again by the other tiles of its row or
-// column, so it should stay in L2 and the infinity cache.
+// Operand stages are loaded with the default cache policy: unlike the
+// cross-entropy's single pass over the logits, every operand panel is read
+// again by the other tiles of its row or column, so it should stay in L2 and
+// the infinity cache.
 __device__ __forceinline__ void load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_wave,
                                            uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave,
-                                           16, voff, 0, 0, 0);
+  buf_load16_lds<0>(r, lds_wave, voff, 0);
 }
 
 // A buffer resource from values every lane holds, passed through
@@ -72,11 +71,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
   const uint32_t n = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bytes));
   return make_rsrc(reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo), n);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Workgroup barrier after this wavefront's LDS reads have completed (so a

@@ -70,6 +70,9 @@ struct RowArgs {
 int check_problem(const vsce_problem* pb, const void* logits, Prob& p);
 // The problem's fields every per-row kernel reads.
 void problem_args(const Prob& p, RowArgs& a);
+// Byte offset, in a workspace of vsce_workspace_bytes(rows), of its [rows]
+// float4 statistics area (the fused mode's rows that are read twice).
+int64_t stats_scratch_offset(int64_t rows);
 
 int launch_prologue(const Prob& p, WsHeader* ws, hipStream_t s);
 int launch_finalize(const Prob& p, const float* loss_rows, const float* acc_rows,

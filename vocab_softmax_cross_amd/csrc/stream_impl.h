@@ -255,7 +255,7 @@ __device__ inline void stream_grad(const RowArgs& a, const char* src, char* dst,
 }
 
 template <int DT, bool VECP>
-__device__ inline void stream_zero(char* dst, int64_t g_begin, int64_t g_end, int nt, int u_) {
+__device__ inline void stream_zero(char* dst, int64_t g_begin, int64_t g_end, int nt) {
   using G = Grp<DT, VECP>;
   float z[G::E];
 #pragma unroll
@@ -335,15 +335,6 @@ __global__ __launch_bounds__(NT) void stats_kernel(const RowArgs a) {
 }
 
 // ---------------------------------------------------------------- LDS ring
-// Waits until at most N vector-memory operations of this wavefront are still
-// outstanding.  The counter covers loads (those into LDS too) and stores, and
-// they leave it in the order they were issued.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N <= 63, "the counter holds 6 bits");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // 16 bytes from LDS, complete on return.  The read is opaque to the compiler
 // (no wait for the direct-to-LDS loads it cannot tell apart), and it has
 // finished before the caller refills the slot.
@@ -393,7 +384,7 @@ __global__ __launch_bounds__(NT) void fused_ring_kernel(const RowArgs a) {
   const int64_t y = a.target[n];
   const int cls = row_class(y, a.Vt, a.ignore_index);
   if (cls != kValid) {
-    stream_zero<DT, true>(row, 0, a.nvec, NT, 1);
+    stream_zero<DT, true>(row, 0, a.nvec, NT);
     const float l = (cls == kIgnored) ? 0.0f : __builtin_nanf("");
     if (tid == 0) store_row(a, n, l, 0.0f, l);
     return;
@@ -508,7 +499,7 @@ __global__ __launch_bounds__(NT) void backward_kernel(const RowArgs a) {
   const int64_t y = a.target[n];
   const int cls = row_class(y, a.Vt, a.ignore_index);
   if (cls != kValid) {
-    stream_zero<DT, VECP>(dst, g_begin, g_end, NT, U);
+    stream_zero<DT, VECP>(dst, g_begin, g_end, NT);
     return;
   }
   const float4 st = reinterpret_cast<const float4*>(a.stats)[n];
