@@ -321,7 +321,11 @@ int flce_forward_backward(const vsce_flce_problem* fp, const void* hidden, const
   rc = launch_prologue(pall, hdr, stream);
   if (rc != VSCE_OK) return rc;
 
-  const int tiles_c = static_cast<int>((Lw.C + 127) / 128);
+  // Tile order of the products: groups of 8 m-tiles by all n-tiles, so the
+  // 32 tiles one XCD runs at a time form an 8 x 4 block and share each
+  // operand stage through that XCD's L2 (12 panels of A and B per stage
+  // instead of 33 when the 32 tiles span one whole column of m-tiles).
+  constexpr int kGroupM = 8;
   for (int64_t ch = 0; ch < Lw.nch; ++ch) {
     const int64_t c0 = ch * Lw.C;
     // 4. z = h W^T for the chunk's kept rows (bf16).
@@ -337,7 +341,7 @@ int flce_forward_backward(const vsce_flce_problem* fp, const void* hidden, const
     g.M = static_cast<int>(Lw.C);
     g.N = static_cast<int>(Lw.Vp);
     g.K = static_cast<int>(H);
-    g.group_m = tiles_c;  // all m-tiles of one n-tile together: each W panel read once
+    g.group_m = kGroupM;
     g.m_count = counts + ch;
     rc = launch_gemm_nt(kGemmOutBf16, g, stream);
     if (rc != VSCE_OK) return rc;
@@ -392,7 +396,7 @@ int flce_forward_backward(const vsce_flce_problem* fp, const void* hidden, const
     d.M = static_cast<int>(Lw.C);
     d.N = static_cast<int>(H);
     d.K = static_cast<int>(Lw.Vp);
-    d.group_m = 8;
+    d.group_m = kGroupM;
     d.m_count = counts + ch;
     rc = launch_gemm_nt(kGemmOutBf16, d, stream);
     if (rc != VSCE_OK) return rc;
@@ -409,7 +413,7 @@ int flce_forward_backward(const vsce_flce_problem* fp, const void* hidden, const
     w.M = static_cast<int>(V);
     w.N = static_cast<int>(H);
     w.K = static_cast<int>(Lw.C);
-    w.group_m = 1;  // the n-tiles of one m-tile together: each G^T panel read once
+    w.group_m = kGroupM;
     w.k_count = counts + ch;
     rc = launch_gemm_nt(ch == 0 ? kGemmOutF32 : kGemmOutF32Add, w, stream);
     if (rc != VSCE_OK) return rc;
