@@ -323,8 +323,9 @@ int ce_scale_grad(void *grad, int64_t rows, int64_t vocab, int64_t row_stride,
 /* bf16 GEMM on the matrix cores, used by the FLCE and callable on its own:
  * C[m][n] = sum_k A[m][k] B[n][k] with fp32 accumulation.  A is [M][lda] and B
  * [N][ldb] bf16, both contiguous along k, 16-byte aligned, lda and ldb
- * multiples of 8 with K <= lda, ldb <= 2^23; K a multiple of 64.  C is
- * [M][ldc], 16-byte aligned, N and ldc multiples of 4, ldc >= N.  out_mode:
+ * multiples of 8 with K <= lda, ldb < 2^23; K a multiple of 64.  C is
+ * [M][ldc], 16-byte aligned, N and ldc multiples of 4, ldc >= N, a row of C
+ * at most 2^23 bytes (ldc <= 2^22 for bf16, 2^21 for fp32).  out_mode:
  * VSCE_GEMM_OUT_BF16 (C bf16, each value rounded once to nearest even),
  * VSCE_GEMM_OUT_F32 (C fp32), VSCE_GEMM_OUT_F32_ADD (C fp32, the product added
  * to it).  Returns VSCE_ERR_INVALID for shapes outside these rules. */

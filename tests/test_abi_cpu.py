@@ -290,7 +290,9 @@ def _gemm(M=128, N=128, K=64, lda=64, ldb=64, ldc=128, mode=0, A=FAKE, B=FAKE, C
 @pytest.mark.parametrize("kw", [dict(K=96, lda=96, ldb=96), dict(lda=32), dict(ldb=40),
                                 dict(lda=68), dict(N=126, ldc=128), dict(ldc=126),
                                 dict(ldc=64), dict(mode=3), dict(M=-1), dict(A=FAKE + 8),
-                                dict(C=None), dict(lda=(1 << 23) + 8, ldb=64)])
+                                dict(C=None), dict(lda=(1 << 23) + 8, ldb=64),
+                                dict(lda=1 << 23), dict(ldb=1 << 23),
+                                dict(ldc=(1 << 22) + 4), dict(ldc=(1 << 21) + 4, mode=1)])
 def test_gemm_argument_checks(kw):
     assert _gemm(**kw) == L.ERR_INVALID
 

@@ -86,19 +86,47 @@ def test_gemm_matches_fp64(M, N, K, mode):
     _check_product(_f64(c), _f64(a), _f64(b), mode == "bf16", "gemm", add)
 
 
-def test_gemm_leaves_padding_alone():
-    """Strided operands and output: columns past N of C are not written."""
+@pytest.mark.parametrize("M,N,K", [(1100, 16388, 128), (1100, 16392, 64), (200, 40000, 64)])
+@pytest.mark.parametrize("mode", ["bf16", "f32_add"])
+def test_gemm_workgroups_walk_several_tiles(M, N, K, mode):
+    """More tiles than the chip holds workgroups (325 blocks of 256 x 256, 626
+    of 128 x 128): each workgroup runs a sequence of tiles, loading the next
+    tile's first stage while storing the last; K = 64 makes every step a
+    tile's first and last.  N = 16388 takes the bf16 stores that stop at N
+    (N not a multiple of 8), the others whole 16-byte chunks."""
+    dev = _dev()
+    _note(f"gemm M={M} N={N} K={K} {mode}")
+    rng = np.random.default_rng(M + N + K)
+    a = _bf16(rng, (M, K), 1.0, dev)
+    b = _bf16(rng, (N, K), 1.0, dev)
+    if mode == "bf16":
+        c = vf.gemm_bf16_nt(a, b)
+        add = None
+    else:
+        c0 = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32)).to(dev)
+        c = c0.clone()
+        vf.gemm_bf16_nt(a, b, out=c, accumulate=True)
+        add = _f64(c0)
+    torch.cuda.synchronize()
+    _check_product(_f64(c), _f64(a), _f64(b), mode == "bf16", "gemm", add)
+
+
+@pytest.mark.parametrize("dtype,N,ldc", [(torch.float32, 40, 48), (torch.bfloat16, 36, 44),
+                                         (torch.bfloat16, 40, 48)])
+def test_gemm_leaves_padding_alone(dtype, N, ldc):
+    """Strided operands and output: columns past N of C are not written (bf16
+    with N or ldc not a multiple of 8 stores 8 bytes at a time)."""
     dev = _dev()
     rng = np.random.default_rng(5)
     abuf = _bf16(rng, (96, 200), 1.0, dev)
-    bbuf = _bf16(rng, (40, 200), 1.0, dev)
+    bbuf = _bf16(rng, (N, 200), 1.0, dev)
     a, b = abuf[:, :128], bbuf[:, :128]
-    cbuf = torch.full((96, 48), 7.0, dtype=torch.float32, device=dev)
-    c = cbuf[:, :40]
+    cbuf = torch.full((96, ldc), 7.0, dtype=dtype, device=dev)
+    c = cbuf[:, :N]
     vf.gemm_bf16_nt(a, b, out=c)
     torch.cuda.synchronize()
-    assert torch.all(cbuf[:, 40:] == 7.0)
-    _check_product(_f64(c), _f64(a), _f64(b), False, "strided gemm")
+    assert torch.all(cbuf[:, N:] == 7.0)
+    _check_product(_f64(c), _f64(a), _f64(b), dtype == torch.bfloat16, "strided gemm")
 
 
 # ---------------------------------------------------------------- FLCE

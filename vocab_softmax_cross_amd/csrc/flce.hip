@@ -263,8 +263,8 @@ int flce_forward_backward(const vsce_flce_problem* fp, const void* hidden, const
   if (grad_output_stride != 0 && grad_output_stride != 1) return VSCE_ERR_INVALID;
   const int64_t rows = fp->rows, H = fp->hidden, V = fp->vocab;
   const FlceLayout Lw = layout(rows, H, V, fp->chunk_rows);
-  // The chunk's rows are the k extent of dL/dW's product (at most 2^23).
-  if (Lw.C > (int64_t(1) << 23)) return VSCE_ERR_UNSUPPORTED;
+  // The chunk's rows are the k extent of dL/dW's product (below 2^23).
+  if (Lw.C >= (int64_t(1) << 23)) return VSCE_ERR_UNSUPPORTED;
   char* ws = static_cast<char*>(workspace);
 
   // The cross-entropy of one chunk of compacted rows: a [C, Vp] bf16 logits

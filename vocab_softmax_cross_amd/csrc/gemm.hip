@@ -3,8 +3,8 @@
 // (Liger-Kernel PR #1622, FLCE: logits = h W^T, dL/dh = G W, dL/dW = G^T h,
 // each arranged so that both operands are contiguous along k).
 //
-// Large products: one workgroup of 16 wavefronts (1024 threads, one per CU,
-// four per SIMD) computes a 256 x 256 block of C, each wavefront a 64 x 64
+// Large products: workgroups of 16 wavefronts (1024 threads, one per CU,
+// four per SIMD) compute 256 x 256 blocks of C, each wavefront a 64 x 64
 // part as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
 // Small products (M or N below 256): 128 x 128 blocks of 4 wavefronts, two
 // workgroups per CU.  k advances 64 at a time through two LDS stages of A and
@@ -25,6 +25,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 
@@ -33,6 +36,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kKMult = 64;  // K must be a multiple of kKMult
 
@@ -98,9 +102,18 @@ __device__ __forceinline__ void tile_of(int64_t t, int tiles_m, int tiles_n, int
   tn = in / gm;
 }
 
-// BM x BN block, WGM x WGN wavefronts, each a (BM / WGM) x (BN / WGN) part of
-// R x S 32 x 32 MFMA blocks; NS LDS stages of BK k-values (NS - 1 of them in
-// flight while one is multiplied); WPE wavefronts per SIMD to compile for.
+// BM x BN blocks, WGM x WGN wavefronts, each a (BM / WGM) x (BN / WGN) part of
+// R x S 32 x 32 MFMA blocks; two LDS stages of BK k-values (one in flight
+// while the other is multiplied); WPE wavefronts per SIMD to compile for.
+//
+// Persistent: the grid holds as many workgroups as the chip runs at once, and
+// each walks its own sequence of tiles as one flat loop over (tile, k-step),
+// so the first stage of its next tile is loaded while the last stage of the
+// current one is multiplied and while that tile's C is stored.  Workgroup b
+// runs on XCD b mod 8; XCD x takes a contiguous range of the tile order and
+// its gridDim / 8 workgroups every (gridDim / 8)-th tile of it, so the tiles
+// one XCD has in flight are neighbours in the order (tile_of) and share
+// operand panels in that XCD's L2.
 template <int OUT, int BM, int BN, int BK, int NS, int WGM, int WGN, int WPE>
 __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void gemm_nt_kernel(const GemmArgs g) {
@@ -109,28 +122,131 @@ void gemm_nt_kernel(const GemmArgs g) {
   constexpr int CPR = BK / 8;                      // 16-byte chunks per tile row
   constexpr int LA = BM * CPR / NT, LB = BN * CPR / NT;
   static_assert(LA * NT == BM * CPR && LB * NT == BN * CPR, "loads per wavefront");
-  constexpr int L = LA + LB;                       // loads per wavefront per stage
-  static_assert(NS >= 2 && NS <= 4 && (NS - 2) * L <= 63, "stages");
+  static_assert(NS == 2, "the waits below assume one stage in flight");
+  // Vector-memory stores of one tile's epilogue per wavefront, at least: every
+  // one is issued (lanes outside C are dropped by the buffer's range check,
+  // not skipped), so the count of operations issued after a stage's loads is
+  // known.  4 per round of the epilogue below.
+  static_assert(R == 2 && S == 2, "the epilogue stages 64 x 64 per wavefront");
+  static_assert((BM + BN) * CPR >= NW * 256, "4 KB of a stage per wavefront");
+  constexpr int kEpilogueStores = (OUT == kGemmOutBf16 ? R : R * S) * 4;
+  constexpr int ES = OUT == kGemmOutBf16 ? 2 : 4;  // bytes per element of C
   __shared__ uint4 lds[NS][(BM + BN) * CPR];       // [stage][A rows, then B rows][chunk]
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = uniform(tid / kWave);
-  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-  int tm, tn;
-  tile_of(xcd_contiguous(blockIdx.x, static_cast<int64_t>(tiles_m) * tiles_n), tiles_m, tiles_n,
-          g.group_m, tm, tn);
   const int m_eff = g.m_count ? min(max(*g.m_count, 0), g.M) : g.M;
-  const int m0 = tm * BM, n0 = tn * BN;
-  if (m0 >= m_eff) return;  // rows past the device-side count: nothing to do
   const int k_eff =
       g.k_count ? min(g.K, (max(*g.k_count, 0) + kKMult - 1) / kKMult * kKMult) : g.K;
   const int nk = k_eff / BK;
+  // Tiles with rows past the device-side count are left out of the order.
+  const int tiles_m = (m_eff + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
+  const int64_t xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds, slot = blockIdx.x / kXcds;
+  const int64_t q = tiles / kXcds, rem = tiles % kXcds;
+  const int64_t first = xcd * q + min(xcd, rem) + slot;  // this workgroup's first tile
+  const int64_t range = q + (xcd < rem ? 1 : 0);         // tiles of this XCD
+  const int64_t mine = range > slot ? (range - 1 - slot) / per_xcd + 1 : 0;
+  if (mine == 0) return;
+  auto origin = [&](int64_t ord, int& m0, int& n0) {  // of this workgroup's tile ord
+    int tm, tn;
+    tile_of(first + ord * per_xcd, tiles_m, tiles_n, g.group_m, tm, tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+  };
 
-  // One resource per operand tile: rows past those in memory read as zeros.
-  const int rows_a = max(0, min(BM, g.a_rows - m0)), rows_b = max(0, min(BN, g.b_rows - n0));
-  const auto ra = uniform_rsrc(
-      static_cast<const uint16_t*>(g.A) + static_cast<int64_t>(m0) * g.lda, rows_a * g.lda * 2);
-  const auto rb = uniform_rsrc(
-      static_cast<const uint16_t*>(g.B) + static_cast<int64_t>(n0) * g.ldb, rows_b * g.ldb * 2);
+  const int wm = wave / WGN, wn = wave % WGN;  // this wavefront's part
+  const int r32 = lane & 31, khalf = lane >> 5;
+  f32x16 acc[R][S];
+  auto clear = [&]() {
+#pragma unroll
+    for (int a = 0; a < R; ++a)
+#pragma unroll
+      for (int b = 0; b < S; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+  };
+  // C of the tile at (m0, n0) from acc, staged through this wavefront's 4 KB
+  // of LDS stage s (free once every wavefront is done multiplying it) so that
+  // each store writes whole 128-byte row segments, 8 rows per instruction,
+  // instead of 16 bytes in each of 32 rows.  acc holds, per 32 x 32 block,
+  // m = r32 and n = 8 j + 4 khalf + (0..3).  A round stages 32 rows: bf16, one
+  // block row (S blocks, 64 n); fp32, one block (32 n); each row is 128 bytes,
+  // its 16-byte chunk c kept at c xor (row mod 8) so that the writes of a
+  // column of rows and the reads of 2 rows at a time spread over the banks.
+  // One resource spans the tile's rows of C (< 2^31 bytes: ldc bytes <= 2^23);
+  // chunks past N get an offset outside it.
+  auto epilogue = [&](int m0, int n0, int s) {
+    const int rows_c = min(BM, m_eff - m0);
+    const auto rc = uniform_rsrc(static_cast<char*>(g.C) + static_cast<int64_t>(m0) * g.ldc * ES,
+                                 static_cast<int64_t>(rows_c) * g.ldc * ES);
+    // bf16 chunks are 8 n: one 16-byte store each when N and ldc allow it,
+    // else two 8-byte stores that stop at N.
+    const bool whole = OUT != kGemmOutBf16 || (g.N % 8 == 0 && g.ldc % 8 == 0);
+    barrier();  // every wavefront is done reading stage s
+    uint4* const buf = lds[s] + wave * 256;
+    const int rrow = lane >> 3, rc8 = lane & 7;  // read-back: row in 8, chunk
+    constexpr int kRounds = OUT == kGemmOutBf16 ? R : R * S;
+#pragma unroll
+    for (int round = 0; round < kRounds; ++round) {
+      const int a = OUT == kGemmOutBf16 ? round : round / S;
+      const int b0 = OUT == kGemmOutBf16 ? 0 : round % S;
+      if constexpr (OUT == kGemmOutBf16) {
+#pragma unroll
+        for (int b = 0; b < S; ++b)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float lo[2] = {acc[a][b][4 * j], acc[a][b][4 * j + 1]};
+            const float hi[2] = {acc[a][b][4 * j + 2], acc[a][b][4 * j + 3]};
+            const uint2 w = make_uint2(Dt<VSCE_BF16>::pack_word(lo), Dt<VSCE_BF16>::pack_word(hi));
+            uint2* p = reinterpret_cast<uint2*>(buf + r32 * 8 + ((b * 4 + j) ^ (r32 & 7)));
+            p[khalf] = w;
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          buf[r32 * 8 + ((2 * j + khalf) ^ (r32 & 7))] =
+              make_uint4(__float_as_uint(acc[a][b0][4 * j]), __float_as_uint(acc[a][b0][4 * j + 1]),
+                         __float_as_uint(acc[a][b0][4 * j + 2]),
+                         __float_as_uint(acc[a][b0][4 * j + 3]));
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = rr * 8 + rrow;
+        const uint4 v = buf[row * 8 + (rc8 ^ (row & 7))];
+        const int64_t mrow = static_cast<int64_t>(wm * (BM / WGM) + a * 32 + row) * g.ldc;
+        const int n = n0 + wn * (BN / WGN) + (OUT == kGemmOutBf16 ? rc8 * 8 : b0 * 32 + rc8 * 4);
+        const uint32_t off = n < g.N ? static_cast<uint32_t>((mrow + n) * ES) : kOutOfRange;
+        if constexpr (OUT == kGemmOutBf16) {
+          if (whole) {
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, rc, off, 0, 0);
+          } else {
+            const uint32_t off2 =
+                n + 4 < g.N ? static_cast<uint32_t>((mrow + n + 4) * ES) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{v.x, v.y}, rc, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{v.z, v.w}, rc, off2, 0, 0);
+          }
+        } else {
+          float4 o = __builtin_bit_cast(float4, v);
+          if constexpr (OUT == kGemmOutF32Add) {
+            const float4 c =
+                __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0));
+            o = make_float4(c.x + o.x, c.y + o.y, c.z + o.z, c.w + o.w);
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), rc, off, 0, 0);
+        }
+      }
+    }
+  };
+  if (nk == 0) {  // empty k: C = 0 (or C unchanged when adding)
+    clear();
+    for (int64_t ord = 0; ord < mine; ++ord) {
+      int m0, n0;
+      origin(ord, m0, n0);
+      epilogue(m0, n0, 0);
+    }
+    return;
+  }
+
   // This lane's chunk of each of the wavefront's loads: chunk j = q 64 + lane
   // of an operand's stage is LDS position j, which swz() assigns to (row
   // j / CPR, k-chunk (j mod CPR) xor f(row)); the XOR is its own inverse.
@@ -138,45 +254,56 @@ void gemm_nt_kernel(const GemmArgs g) {
   auto chunk_offset = [&](int j, int64_t ld) {
     const int row = j / CPR;
     const int kc = swz<BK>(row, j % CPR) - row * CPR;
-    return static_cast<uint32_t>((row * ld + kc * 8) * 2);  // < 2^31: ld <= 2^23
+    return static_cast<uint32_t>((row * ld + kc * 8) * 2);  // < 2^32: ld < 2^23
   };
 #pragma unroll
   for (int i = 0; i < LA; ++i) offa[i] = chunk_offset((wave * LA + i) * kWave + lane, g.lda);
 #pragma unroll
   for (int i = 0; i < LB; ++i) offb[i] = chunk_offset((wave * LB + i) * kWave + lane, g.ldb);
-  auto load_stage = [&](int s, int k0) {
-    const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
+  // The load cursor: tile ordinal and k-step of the next stage to load, and
+  // one resource per operand tile (rows past those in memory read as zeros).
+  int64_t l_ord = 0;
+  int l_k = 0;
+  __amdgpu_buffer_rsrc_t ra, rb;
+  auto aim = [&](int64_t ord) {
+    int m0, n0;
+    origin(ord, m0, n0);
+    const int rows_a = max(0, min(BM, g.a_rows - m0)), rows_b = max(0, min(BN, g.b_rows - n0));
+    ra = uniform_rsrc(static_cast<const uint16_t*>(g.A) + static_cast<int64_t>(m0) * g.lda,
+                      static_cast<int64_t>(rows_a) * g.lda * 2);
+    rb = uniform_rsrc(static_cast<const uint16_t*>(g.B) + static_cast<int64_t>(n0) * g.ldb,
+                      static_cast<int64_t>(rows_b) * g.ldb * 2);
+  };
+  auto load_next = [&](int s) {
+    if (l_ord == mine) return;
+    const uint32_t kb = static_cast<uint32_t>(l_k * BK) * 2u;
 #pragma unroll
     for (int i = 0; i < LA; ++i)
       load16_lds(ra, &lds[s][(wave * LA + i) * kWave], offa[i] + kb);
 #pragma unroll
     for (int i = 0; i < LB; ++i)
       load16_lds(rb, &lds[s][BM * CPR + (wave * LB + i) * kWave], offb[i] + kb);
+    if (++l_k == nk) {
+      l_k = 0;
+      if (++l_ord < mine) aim(l_ord);
+    }
   };
 
-  const int wm = wave / WGN, wn = wave % WGN;  // this wavefront's part
-  const int r32 = lane & 31, khalf = lane >> 5;
-  f32x16 acc[R][S];
-#pragma unroll
-  for (int a = 0; a < R; ++a)
-#pragma unroll
-    for (int b = 0; b < S; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-
-  // NS - 1 stages in flight ahead of the one being multiplied.
-#pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
-    if (st < nk) load_stage(st, st * BK);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int s = kt % NS;
-    // Loads issued after stage kt's: the stages kt + 1 .. kt + NS - 2 that exist.
-    const int later = min(NS - 2, nk - 1 - kt);
-    if (later >= 2) wait_vm<(NS >= 4 ? 2 : 0) * L>();
-    else if (later == 1) wait_vm<L>();
+  aim(0);
+  load_next(0);
+  int64_t c_ord = 0;  // tile being multiplied, and its k-step
+  int c_k = 0, cm0, cn0;
+  origin(0, cm0, cn0);
+  clear();
+  const int64_t steps = mine * nk;
+  for (int64_t it = 0; it < steps; ++it) {
+    const int s = static_cast<int>(it & 1);
+    // Stage it was loaded during step it - 1; when that step ended a tile,
+    // the tile's epilogue stores were issued after it and may stay in flight.
+    if (c_k == 0 && it > 0) wait_vm<kEpilogueStores>();
     else wait_vm<0>();
-    barrier();  // stage kt is in LDS; every wavefront is done with stage kt - 1
-    if (kt + NS - 1 < nk) load_stage((kt + NS - 1) % NS, (kt + NS - 1) * BK);
+    barrier();  // stage it is in LDS; every wavefront is done with stage it - 1
+    load_next(s ^ 1);
     const uint4* As = lds[s];
     const uint4* Bs = lds[s] + BM * CPR;
 #pragma unroll
@@ -198,38 +325,11 @@ void gemm_nt_kernel(const GemmArgs g) {
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(fb[b]), as_bf16(fa[a]),
                                                               acc[a][b], 0, 0, 0);
     }
-  }
-
-  // Epilogue: lane holds, per block, m = r32 and n = 8 j + 4 khalf + (0..3).
-#pragma unroll
-  for (int a = 0; a < R; ++a) {
-    const int m = m0 + wm * (BM / WGM) + a * 32 + r32;
-    if (m >= m_eff) continue;
-#pragma unroll
-    for (int b = 0; b < S; ++b) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * (BN / WGN) + b * 32 + j * 8 + khalf * 4;
-        if (n >= g.N) continue;
-        const float v0 = acc[a][b][4 * j], v1 = acc[a][b][4 * j + 1];
-        const float v2 = acc[a][b][4 * j + 2], v3 = acc[a][b][4 * j + 3];
-        const int64_t off = static_cast<int64_t>(m) * g.ldc + n;
-        if constexpr (OUT == kGemmOutBf16) {
-          const float lo[2] = {v0, v1}, hi[2] = {v2, v3};
-          uint2 w;
-          w.x = Dt<VSCE_BF16>::pack_word(lo);
-          w.y = Dt<VSCE_BF16>::pack_word(hi);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.C) + off) = w;
-        } else {
-          float4* p = reinterpret_cast<float4*>(static_cast<float*>(g.C) + off);
-          if constexpr (OUT == kGemmOutF32Add) {
-            const float4 o = *p;
-            *p = make_float4(o.x + v0, o.y + v1, o.z + v2, o.w + v3);
-          } else {
-            *p = make_float4(v0, v1, v2, v3);
-          }
-        }
-      }
+    if (++c_k == nk) {
+      epilogue(cm0, cn0, s);
+      clear();
+      c_k = 0;
+      if (++c_ord < mine) origin(c_ord, cm0, cn0);
     }
   }
 }
@@ -238,24 +338,52 @@ void gemm_nt_kernel(const GemmArgs g) {
 
 namespace {
 
+constexpr int kMaxDevices = 64;
+
+// Workgroups of `kernel` the current device runs at once (CUs x workgroups
+// per CU), cached per device.
+template <typename Kernel>
+int resident_workgroups(Kernel kernel, int threads) {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+    return 0;
+  const int n = cus * per_cu;
+  if (n > 0 && dev >= 0 && dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+template <int OUT, int BM, int BN, int BK, int NS, int WGM, int WGN, int WPE>
+int launch_persistent(const GemmArgs& g, hipStream_t s) {
+  auto kernel = gemm_nt_kernel<OUT, BM, BN, BK, NS, WGM, WGN, WPE>;
+  const int threads = WGM * WGN * 64;
+  const int64_t tiles = static_cast<int64_t>((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  const int resident = resident_workgroups(kernel, threads);
+  if (resident <= 0) return VSCE_ERR_LAUNCH;
+  // A multiple of 8 (the tile ranges are split by XCD), no more than the
+  // chip holds at once nor than the tiles need.
+  const int64_t cap = std::max<int64_t>(kXcds, resident / kXcds * kXcds);
+  const int64_t grid = std::min<int64_t>(cap, (tiles + kXcds - 1) / kXcds * kXcds);
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(threads), 0, s, g);
+  return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
+}
+
 template <int BM, int BN, int BK, int NS, int WGM, int WGN, int WPE>
 int launch_blocks(int out, const GemmArgs& g, hipStream_t s) {
-  const int64_t tiles = static_cast<int64_t>((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  if (tiles > 0x7fffffffLL) return VSCE_ERR_UNSUPPORTED;
-  const dim3 grid(static_cast<unsigned>(tiles)), block(WGM * WGN * 64);
   switch (out) {
-    case kGemmOutBf16:
-      hipLaunchKernelGGL((gemm_nt_kernel<kGemmOutBf16, BM, BN, BK, NS, WGM, WGN, WPE>), grid, block, 0, s, g);
-      break;
-    case kGemmOutF32:
-      hipLaunchKernelGGL((gemm_nt_kernel<kGemmOutF32, BM, BN, BK, NS, WGM, WGN, WPE>), grid, block, 0, s, g);
-      break;
+    case kGemmOutBf16: return launch_persistent<kGemmOutBf16, BM, BN, BK, NS, WGM, WGN, WPE>(g, s);
+    case kGemmOutF32: return launch_persistent<kGemmOutF32, BM, BN, BK, NS, WGM, WGN, WPE>(g, s);
     case kGemmOutF32Add:
-      hipLaunchKernelGGL((gemm_nt_kernel<kGemmOutF32Add, BM, BN, BK, NS, WGM, WGN, WPE>), grid, block, 0, s, g);
-      break;
+      return launch_persistent<kGemmOutF32Add, BM, BN, BK, NS, WGM, WGN, WPE>(g, s);
     default: return VSCE_ERR_INVALID;
   }
-  return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -263,12 +391,13 @@ int launch_blocks(int out, const GemmArgs& g, hipStream_t s) {
 int launch_gemm_nt(int out, const GemmArgs& g, hipStream_t s) {
   if (g.M < 0 || g.N < 0 || g.K < 0 || g.K % kKMult != 0 || g.N % 4 != 0 || g.ldc % 4 != 0 ||
       g.lda % 8 != 0 || g.ldb % 8 != 0 || g.lda < g.K || g.ldb < g.K || g.ldc < g.N ||
-      g.lda > (int64_t(1) << 23) || g.ldb > (int64_t(1) << 23) || g.group_m < 1 ||
-      g.a_rows < 0 || g.b_rows < 0)
+      g.lda >= (int64_t(1) << 23) || g.ldb >= (int64_t(1) << 23) || g.group_m < 1 ||
+      g.a_rows < 0 || g.b_rows < 0 ||
+      g.ldc * (out == kGemmOutBf16 ? 2 : 4) > (int64_t(1) << 23))
     return VSCE_ERR_INVALID;
   if (g.M == 0 || g.N == 0) return VSCE_OK;
   // Large products: 256 x 256 blocks, one per CU, 2 stages of 64 k-values
-  // (128 KB of LDS, 128 x 128 per wavefront); small ones: 128 x 128 blocks,
+  // (128 KB of LDS, 64 x 64 per wavefront); small ones: 128 x 128 blocks,
   // two per CU, 2 stages of 64.
   if (g.M >= 256 && g.N >= 256) return launch_blocks<256, 256, 64, 2, 4, 4, 4>(out, g, s);
   return launch_blocks<128, 128, 64, 2, 2, 2, 2>(out, g, s);
