@@ -272,18 +272,16 @@ def flce_mode(L, W, hip, dev, stream, K, sample_rows=0):
     res = {"shape": {"BT": BT, "H": H, "V": V, "kept_rows": n}, "ms": round(ms, 3),
            "TFLOPs": round(flops / ms / 1e9, 1),
            "frac_of_bf16_mfma_peak": round(flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
-    # The three products alone, at the same shapes (bf16 operands of the right
-    # sizes; their values do not change the work).
+    # The three products alone, at the same shapes and operand layouts as in
+    # the FLCE (W, G and h read k-major, in place, by the backward products;
+    # a bf16 G of the right size: its values do not change the work).
     a = torch.empty((BT, V), dtype=torch.bfloat16, device=dev).normal_(generator=g)
-    wt = torch.empty((H, V), dtype=torch.bfloat16, device=dev).normal_(generator=g)
-    at = torch.empty((V, BT), dtype=torch.bfloat16, device=dev).normal_(generator=g)
-    ht = torch.empty((H, BT), dtype=torch.bfloat16, device=dev).normal_(generator=g)
     zl = torch.empty((BT, V), dtype=torch.bfloat16, device=dev)
     dh = torch.empty((BT, H), dtype=torch.bfloat16, device=dev)
     products = {
         "z=hW^T": lambda: vf.gemm_bf16_nt(hidden, weight, out=zl),
-        "dh=GW": lambda: vf.gemm_bf16_nt(a, wt, out=dh),
-        "dW=G^Th": lambda: vf.gemm_bf16_nt(at, ht, out=gw),
+        "dh=GW": lambda: vf.gemm_bf16_nt(a, weight.t(), out=dh),
+        "dW=G^Th": lambda: vf.gemm_bf16_nt(a.t(), hidden.t(), out=gw),
     }
     one = 2.0 * BT * H * V
     for name, fn in products.items():
@@ -295,7 +293,7 @@ def flce_mode(L, W, hip, dev, stream, K, sample_rows=0):
     if sample_rows:  # the oracle's sample: the same rows and weights, upcast exactly
         sample = (hidden[:sample_rows].double().cpu().numpy(), weight.double().cpu().numpy(),
                   tgt[:sample_rows].copy())
-    del a, wt, at, ht, zl, dh, ws, gw, gh, weight, hidden
+    del a, zl, dh, ws, gw, gh, weight, hidden
     torch.cuda.empty_cache()
     return res, sample
 

@@ -336,6 +336,20 @@ int vsce_gemm_bf16_nt(const void *A, int64_t lda, const void *B, int64_t ldb, vo
                       int64_t ldc, int64_t M, int64_t N, int64_t K, int32_t out_mode,
                       hipStream_t stream);
 
+/* The same product with either operand stored k-major, as the FLCE's
+ * backward products need them (dL/dh = G W reads W [V][H] with k = the
+ * vocabulary entry; dL/dW = G^T h reads G and h with k = the row): layout
+ * VSCE_GEMM_A_K_MAJOR means A is [K][lda] with lda >= M (element (m, k) at
+ * A[k * lda + m]), VSCE_GEMM_B_K_MAJOR that B is [K][ldb] with ldb >= N; an
+ * operand without its bit is stored as in vsce_gemm_bf16_nt.  Leading
+ * dimensions are multiples of 8 below 2^23.  Every layout gives bit-identical
+ * C for the same operand values.  layout 0 is vsce_gemm_bf16_nt. */
+#define VSCE_GEMM_A_K_MAJOR 1u
+#define VSCE_GEMM_B_K_MAJOR 2u
+int vsce_gemm_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
+                   int64_t ldc, int64_t M, int64_t N, int64_t K, uint32_t layout,
+                   int32_t out_mode, hipStream_t stream);
+
 /*
  * An FLCE problem: hidden states h [rows][hidden] and the head's weight W
  * [vocab][hidden], both bf16 row-major (nn.Linear's layout), the logits

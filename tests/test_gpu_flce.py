@@ -111,6 +111,50 @@ def test_gemm_workgroups_walk_several_tiles(M, N, K, mode):
     _check_product(_f64(c), _f64(a), _f64(b), mode == "bf16", "gemm", add)
 
 
+def _k_major(x, dev):
+    """x [rows, K] as a transposed view of a [K, ld] buffer (ld a multiple of
+    8 above rows), its padding columns NaN: only rows of C that are not
+    stored may read them."""
+    rows, K = x.shape
+    ld = (rows + 8) // 8 * 8 + 8
+    buf = torch.full((K, ld), float("nan"), dtype=torch.bfloat16, device=dev)
+    buf[:, :rows] = x.t()
+    return buf[:, :rows].t()
+
+
+@pytest.mark.parametrize("layout", ["a", "b", "ab"])
+@pytest.mark.parametrize("M,N,K", [(300, 260, 192), (1100, 16392, 64), (200, 4100, 128),
+                                   (1100, 1004, 4096)])
+@pytest.mark.parametrize("mode", ["bf16", "f32_add"])
+def test_gemm_k_major_operands(layout, M, N, K, mode):
+    """A and/or B read k-major in place ([K, rows] storage): within the fp64
+    bound, and bit-identical to the row layout on the same values (the
+    transposing LDS reads hand the MFMA the same operands, k in the same
+    order)."""
+    dev = _dev()
+    _note(f"gemm k-major {layout} M={M} N={N} K={K} {mode}")
+    rng = np.random.default_rng(M * 3 + N + K)
+    a = _bf16(rng, (M, K), 1.0, dev)
+    b = _bf16(rng, (N, K), 1.0, dev)
+    ak = _k_major(a, dev) if "a" in layout else a
+    bk = _k_major(b, dev) if "b" in layout else b
+    assert (ak.stride(0) == 1) == ("a" in layout) and (bk.stride(0) == 1) == ("b" in layout)
+    if mode == "bf16":
+        c = vf.gemm_bf16_nt(ak, bk)
+        ref = vf.gemm_bf16_nt(a, b)
+        add = None
+    else:
+        c0 = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32)).to(dev)
+        c, ref = c0.clone(), c0.clone()
+        vf.gemm_bf16_nt(ak, bk, out=c, accumulate=True)
+        vf.gemm_bf16_nt(a, b, out=ref, accumulate=True)
+        add = _f64(c0)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16) if mode == "bf16" else c.view(torch.int32),
+                       ref.view(torch.int16) if mode == "bf16" else ref.view(torch.int32))
+    _check_product(_f64(c), _f64(a), _f64(b), mode == "bf16", "k-major gemm", add)
+
+
 @pytest.mark.parametrize("dtype,N,ldc", [(torch.float32, 40, 48), (torch.bfloat16, 36, 44),
                                          (torch.bfloat16, 40, 48)])
 def test_gemm_leaves_padding_alone(dtype, N, ldc):

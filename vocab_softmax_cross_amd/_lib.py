@@ -28,9 +28,10 @@ WS_INV_W, WS_INV_N_VALID = 40, 44
 
 EXPORTS = ("vsce_workspace_bytes", "ce_forward_fused_inplace", "ce_forward_fused_inplace_timed",
            "ce_forward_stats", "ce_forward_stats_partial", "ce_merge_stats",
-           "ce_backward_from_stats", "ce_scale_grad", "vsce_gemm_bf16_nt",
+           "ce_backward_from_stats", "ce_scale_grad", "vsce_gemm_bf16_nt", "vsce_gemm_bf16",
            "vsce_flce_workspace_bytes", "flce_forward_backward", "vsce_strerror", "vsce_version")
 GEMM_OUT_BF16, GEMM_OUT_F32, GEMM_OUT_F32_ADD = 0, 1, 2
+GEMM_A_K_MAJOR, GEMM_B_K_MAJOR = 1, 2
 
 
 class Problem(ctypes.Structure):
@@ -123,6 +124,9 @@ def load() -> ctypes.CDLL:
     lib.vsce_gemm_bf16_nt.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                                       c_int64, c_int64, c_int64, c_int32, c_void_p]
     lib.vsce_gemm_bf16_nt.restype = ctypes.c_int
+    lib.vsce_gemm_bf16.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
+                                   c_int64, c_int64, c_int64, c_uint32, c_int32, c_void_p]
+    lib.vsce_gemm_bf16.restype = ctypes.c_int
     lib.vsce_flce_workspace_bytes.argtypes = [P(FlceProblem)]
     lib.vsce_flce_workspace_bytes.restype = c_size_t
     lib.flce_forward_backward.argtypes = [P(FlceProblem), c_void_p, c_void_p, P(Outputs),
@@ -206,6 +210,12 @@ def vsce_gemm_bf16_nt(A: int, lda: int, B: int, ldb: int, C: int, ldc: int, M: i
                       out_mode: int, stream: int) -> int:
     return _check("vsce_gemm_bf16_nt", load().vsce_gemm_bf16_nt(A, lda, B, ldb, C, ldc, M, N, K,
                                                                  out_mode, stream))
+
+
+def vsce_gemm_bf16(A: int, lda: int, B: int, ldb: int, C: int, ldc: int, M: int, N: int, K: int,
+                   layout: int, out_mode: int, stream: int) -> int:
+    return _check("vsce_gemm_bf16", load().vsce_gemm_bf16(A, lda, B, ldb, C, ldc, M, N, K, layout,
+                                                          out_mode, stream))
 
 
 def vsce_flce_workspace_bytes(problem: FlceProblem) -> int:

@@ -5,8 +5,9 @@
 // products).  For a chunk of rows with hidden states h and the weight W:
 //   logits z = h W^T            (bf16 GEMM on the matrix cores, bf16 logits)
 //   the fused cross-entropy     (loss rows; G = dL/dz written over z)
-//   dL/dh = G W,  dL/dW += G^T h   (two more GEMMs, W and G transposed first
-//                                  so every product reads k-contiguous rows)
+//   dL/dh = G W,  dL/dW += G^T h   (two more GEMMs that read W, G and h
+//                                  k-major where they need it: no transposed
+//                                  copies)
 // Ignored rows are compacted out on the device first (a prefix count over the
 // targets): the products skip them through device-side row counts, so no
 // count is read on the host, and their dL/dh rows are written as zeros at the
@@ -32,7 +33,7 @@ struct FlceLayout {
   int64_t nch;    // chunks
   int64_t R;      // compacted rows held: nch * C
   int64_t Vp;     // vocabulary padded to a multiple of 64
-  int64_t ce, ints, tc, goc, lossc, zc, accc, xc, dxc, wt, logits, gt, xt, end;
+  int64_t ce, ints, tc, goc, lossc, zc, accc, xc, dxc, logits, end;
 };
 
 FlceLayout layout(int64_t rows, int64_t H, int64_t V, int64_t chunk_rows) {
@@ -53,10 +54,7 @@ FlceLayout layout(int64_t rows, int64_t H, int64_t V, int64_t chunk_rows) {
   L.accc = o;   o += al(4 * L.R);
   L.xc = o;     o += al(2 * L.R * H);
   L.dxc = o;    o += al(2 * L.R * H);
-  L.wt = o;     o += al(2 * H * L.Vp);
   L.logits = o; o += al(2 * L.C * L.Vp);
-  L.gt = o;     o += al(2 * L.Vp * L.C);
-  L.xt = o;     o += al(2 * H * L.C);
   L.end = o;
   return L;
 }
@@ -150,54 +148,6 @@ __global__ __launch_bounds__(256) void scatter_floats_kernel(const float* in, co
   out[r] = i >= 0 ? in[i] : 0.0f;
 }
 
-// ---------------------------------------------------------------- transpose
-// out[c][r] = in[r][c] for r < rows_valid, 0 for rows_valid <= r < out_cols;
-// c < in_cols (a multiple of 8).  64 x 64 tiles through LDS, 16-byte loads
-// and stores; out_cols and ld_out multiples of 8.
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* in, int64_t ld_in,
-                                                        int64_t rows_valid, int64_t in_cols,
-                                                        uint16_t* out, int64_t ld_out,
-                                                        int64_t out_cols, int64_t tiles_c) {
-  __shared__ uint16_t tile[64][64 + 8];
-  const int64_t tr = blockIdx.x / tiles_c, tcb = blockIdx.x % tiles_c;
-  const int64_t r0 = tr * 64, c0 = tcb * 64;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {  // 64 rows x 8 vectors of 8 = 512 loads
-    const int idx = q * 256 + t;
-    const int rr = idx >> 3, cv = idx & 7;
-    const int64_t r = r0 + rr, c = c0 + cv * 8;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (r < rows_valid && c < in_cols) v = *reinterpret_cast<const uint4*>(in + r * ld_in + c);
-    const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tile[rr][cv * 8 + j] = e[j];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {  // 64 output rows (c) x 8 vectors of 8 r
-    const int idx = q * 256 + t;
-    const int cc = idx >> 3, rv = idx & 7;
-    const int64_t c = c0 + cc, r = r0 + rv * 8;
-    if (c >= in_cols || r >= out_cols) continue;
-    uint4 v;
-    uint16_t* e = reinterpret_cast<uint16_t*>(&v);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = tile[rv * 8 + j][cc];
-    *reinterpret_cast<uint4*>(out + c * ld_out + r) = v;
-  }
-}
-
-int transpose(const void* in, int64_t ld_in, int64_t rows_valid, int64_t in_cols, void* out,
-              int64_t ld_out, int64_t out_cols, hipStream_t s) {
-  const int64_t tiles_r = (out_cols + 63) / 64, tiles_c = (in_cols + 63) / 64;
-  if (tiles_r * tiles_c == 0) return VSCE_OK;
-  hipLaunchKernelGGL(transpose_kernel, dim3(static_cast<unsigned>(tiles_r * tiles_c)), dim3(256),
-                     0, s, static_cast<const uint16_t*>(in), ld_in, rows_valid, in_cols,
-                     static_cast<uint16_t*>(out), ld_out, out_cols, tiles_c);
-  return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
-}
-
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 int check_flce(const vsce_flce_problem* fp) {
@@ -218,14 +168,15 @@ using namespace vsce;
 
 extern "C" {
 
-int vsce_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
-                      int64_t ldc, int64_t M, int64_t N, int64_t K, int32_t out_mode,
-                      hipStream_t stream) {
+int vsce_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                   int64_t ldc, int64_t M, int64_t N, int64_t K, uint32_t layout,
+                   int32_t out_mode, hipStream_t stream) {
   if (M < 0 || N < 0 || K < 0 || M > 0x7fffffffLL || N > 0x7fffffffLL || K > 0x7fffffffLL)
     return VSCE_ERR_INVALID;
   if (M > 0 && N > 0 && (!A || !B || !C || !al16(A) || !al16(B) || !al16(C)))
     return VSCE_ERR_INVALID;
   if (out_mode < VSCE_GEMM_OUT_BF16 || out_mode > VSCE_GEMM_OUT_F32_ADD) return VSCE_ERR_INVALID;
+  if (layout & ~(VSCE_GEMM_A_K_MAJOR | VSCE_GEMM_B_K_MAJOR)) return VSCE_ERR_INVALID;
   GemmArgs g = {};
   g.A = A;
   g.lda = lda;
@@ -236,10 +187,17 @@ int vsce_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_t ldb, vo
   g.M = static_cast<int>(M);
   g.N = static_cast<int>(N);
   g.K = static_cast<int>(K);
-  g.a_rows = g.M;
-  g.b_rows = g.N;
+  g.layout = static_cast<int>(layout);
+  g.a_rows = (layout & VSCE_GEMM_A_K_MAJOR) ? g.K : g.M;
+  g.b_rows = (layout & VSCE_GEMM_B_K_MAJOR) ? g.K : g.N;
   g.group_m = 8;
   return launch_gemm_nt(out_mode, g, stream);
+}
+
+int vsce_gemm_bf16_nt(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                      int64_t ldc, int64_t M, int64_t N, int64_t K, int32_t out_mode,
+                      hipStream_t stream) {
+  return vsce_gemm_bf16(A, lda, B, ldb, C, ldc, M, N, K, 0u, out_mode, stream);
 }
 
 size_t vsce_flce_workspace_bytes(const vsce_flce_problem* problem) {
@@ -298,10 +256,7 @@ int flce_forward_backward(const vsce_flce_problem* fp, const void* hidden, const
   float* accc = reinterpret_cast<float*>(ws + Lw.accc);
   uint16_t* xc = reinterpret_cast<uint16_t*>(ws + Lw.xc);
   uint16_t* dxc = reinterpret_cast<uint16_t*>(ws + Lw.dxc);
-  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + Lw.wt);
   uint16_t* logits = reinterpret_cast<uint16_t*>(ws + Lw.logits);
-  uint16_t* gt = reinterpret_cast<uint16_t*>(ws + Lw.gt);
-  uint16_t* xt = reinterpret_cast<uint16_t*>(ws + Lw.xt);
   WsHeader* hdr = reinterpret_cast<WsHeader*>(ws + Lw.ce);
   const int64_t hvec = H / 8;
   const bool none = fp->reduction == VSCE_REDUCTION_NONE;
@@ -314,10 +269,7 @@ int flce_forward_backward(const vsce_flce_problem* fp, const void* hidden, const
                      grad_output_stride, fp->ignore_index, n_valid, src_of,
                      reinterpret_cast<uint4*>(xc), tc, goc);
   if (hipGetLastError() != hipSuccess) return VSCE_ERR_LAUNCH;
-  // 2. W^T, [H, Vp], zero past V.
-  rc = transpose(weight, H, V, H, wt, Lw.Vp, Lw.Vp, stream);
-  if (rc != VSCE_OK) return rc;
-  // 3. Normalizers over all kept rows.
+  // 2. Normalizers over all kept rows.
   rc = launch_prologue(pall, hdr, stream);
   if (rc != VSCE_OK) return rc;
 
@@ -328,7 +280,7 @@ int flce_forward_backward(const vsce_flce_problem* fp, const void* hidden, const
   constexpr int kGroupM = 8;
   for (int64_t ch = 0; ch < Lw.nch; ++ch) {
     const int64_t c0 = ch * Lw.C;
-    // 4. z = h W^T for the chunk's kept rows (bf16).
+    // 3. z = h W^T for the chunk's kept rows (bf16).
     GemmArgs g = {};
     g.A = xc + c0 * H;
     g.lda = H;
@@ -345,7 +297,7 @@ int flce_forward_backward(const vsce_flce_problem* fp, const void* hidden, const
     g.m_count = counts + ch;
     rc = launch_gemm_nt(kGemmOutBf16, g, stream);
     if (rc != VSCE_OK) return rc;
-    // 5. The cross-entropy; G = dL/dz over the logits.
+    // 4. The cross-entropy; G = dL/dz over the logits.
     Prob p = pc;
     p.target = tc + c0;
     RowArgs a = {};
@@ -379,18 +331,16 @@ int flce_forward_backward(const vsce_flce_problem* fp, const void* hidden, const
       rc = launch_scale(p, sa, stream);
       if (rc != VSCE_OK) return rc;
     }
-    // 6. G^T [Vp, C] and h^T [H, C] of the chunk.
-    rc = transpose(logits, Lw.Vp, Lw.C, Lw.Vp, gt, Lw.C, Lw.C, stream);
-    if (rc == VSCE_OK) rc = transpose(xc + c0 * H, H, Lw.C, H, xt, Lw.C, Lw.C, stream);
-    if (rc != VSCE_OK) return rc;
-    // 7. dL/dh = G W for the kept rows.
+    // 5. dL/dh = G W for the kept rows: W read k-major (k = vocabulary
+    // entry), its k-rows past V as zeros.
     GemmArgs d = {};
     d.A = logits;
     d.lda = Lw.Vp;
     d.a_rows = static_cast<int>(Lw.C);
-    d.B = wt;
-    d.ldb = Lw.Vp;
-    d.b_rows = static_cast<int>(H);
+    d.B = weight;
+    d.ldb = H;
+    d.b_rows = static_cast<int>(V);
+    d.layout = kGemmBKMajor;
     d.C = dxc + c0 * H;
     d.ldc = H;
     d.M = static_cast<int>(Lw.C);
@@ -400,14 +350,16 @@ int flce_forward_backward(const vsce_flce_problem* fp, const void* hidden, const
     d.m_count = counts + ch;
     rc = launch_gemm_nt(kGemmOutBf16, d, stream);
     if (rc != VSCE_OK) return rc;
-    // 8. dL/dW (+)= G^T h over the chunk's kept rows.
+    // 6. dL/dW (+)= G^T h over the chunk's kept rows: G and h read k-major
+    // (k = kept row).
     GemmArgs w = {};
-    w.A = gt;
-    w.lda = Lw.C;
-    w.a_rows = static_cast<int>(Lw.Vp);
-    w.B = xt;
-    w.ldb = Lw.C;
-    w.b_rows = static_cast<int>(H);
+    w.A = logits;
+    w.lda = Lw.Vp;
+    w.a_rows = static_cast<int>(Lw.C);
+    w.B = xc + c0 * H;
+    w.ldb = H;
+    w.b_rows = static_cast<int>(Lw.C);
+    w.layout = kGemmAKMajor | kGemmBKMajor;
     w.C = grad_weight;
     w.ldc = H;
     w.M = static_cast<int>(V);
@@ -419,7 +371,7 @@ int flce_forward_backward(const vsce_flce_problem* fp, const void* hidden, const
     if (rc != VSCE_OK) return rc;
   }
 
-  // 9. The reduction over all kept rows, then everything per row back in the
+  // 7. The reduction over all kept rows, then everything per row back in the
   // caller's order.
   rc = launch_finalize(pall, lossc, accc, zc, none ? nullptr : out->loss, out->acc_mean,
                        none ? nullptr : out->z_loss, hdr, stream);

@@ -16,6 +16,13 @@
 // applied by choosing which global chunk each lane loads, since a
 // direct-to-LDS load writes lane i at base + 16 i.
 //
+// An operand is stored either with k contiguous ([rows][ld], the row layout)
+// or k-major ([k][ld], its rows contiguous: G and h for dL/dW = G^T h, W for
+// dL/dh = G W), so that no product needs a transposed copy.  A k-major stage
+// holds BK k-rows of the tile's rows and is read with the transposing LDS
+// load (fragment() below), which gives the MFMA the same operand, k in the
+// same order, as the row layout: the results do not depend on the layout.
+//
 // Operand lane layout of the 32x32x16 bf16 MFMA (checked on the hardware):
 // lane l supplies row l mod 32 and the 8 k-values 8 (l / 32) .. + 7 of each
 // operand; result element i of lane l is (row 8 (i / 4) + 4 (l / 32) + i mod 4,
@@ -37,6 +44,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKMult = 64;  // K must be a multiple of kKMult
 
@@ -87,6 +95,50 @@ __device__ __forceinline__ void barrier() {
 
 __device__ __forceinline__ bf16x8 as_bf16(const u32x4_t v) { return __builtin_bit_cast(bf16x8, v); }
 
+// This lane's MFMA operand for the 32 rows rb.. of a stage X at k-step ks
+// (k-values 16 ks ..): 8 k-values of row rb + (lane mod 32), from k-value
+// 16 ks + 8 (lane / 32).
+// Row layout (tile rows of BK / 8 chunks, swz): one 16-byte LDS read.
+// k-major layout (BK k-rows of CPM chunks; chunk c of k-row k kept at
+// c xor 4 (k mod 4), so the 4 k-rows one read touches fill all 64 banks): two
+// ds_read_b64_tr_b16.  That load treats the 8 bytes each lane of a group of
+// 16 addresses as a 16 x 4 matrix D of 16-bit values (row i from lane i) and
+// gives lane t the 4 values D[4 j + t / 4][t mod 4], j = 0..3 (measured on
+// gfx950).  Lane i of a group addresses k-row k0 + i / 4 at rows
+// r0 + 4 (i mod 4) .. + 3, so lane t receives row r0 + t at k-rows k0 .. k0 + 3.
+// One ds_read_b64_tr_b16.  The restrict pointer of this inlined function
+// gives the load alias-scope metadata, from which the compiler can tell it
+// apart from the direct-to-LDS loads in flight into the other stage; without
+// any, it would wait for all of those before every transposing read.
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ s16x4 read_tr(lds_s16x4* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+}
+
+// LDS accesses of the epilogue, through restrict pointers for the same
+// reason: the stage they use is not the one the loads in flight fill.
+template <typename T>
+__device__ __forceinline__ void lds_put(T* __restrict__ p, const T v) { *p = v; }
+template <typename T>
+__device__ __forceinline__ T lds_get(const T* __restrict__ p) { return *p; }
+
+template <bool KM, int BK, int CPM>
+__device__ __forceinline__ u32x4_t fragment(const uint4* X, int rb, int ks, int lane) {
+  if constexpr (!KM) {
+    return *reinterpret_cast<const u32x4_t*>(X + swz<BK>(rb + (lane & 31), ks * 2 + (lane >> 5)));
+  } else {
+    const int grp = lane >> 4, t = lane & 15;
+    const int r = rb + 16 * (grp & 1) + 4 * (t & 3);   // rows this lane addresses
+    const int k = ks * 16 + 8 * (grp >> 1) + (t >> 2);  // its k-row; k mod 4 = t / 4
+    const int c = (r >> 3) ^ (4 * (t >> 2));
+    const char* p = reinterpret_cast<const char*>(X + k * CPM + c) + (r & 7) * 2;
+    const s16x4 lo = read_tr((lds_s16x4*)(p));
+    const s16x4 hi = read_tr((lds_s16x4*)(p + 4 * CPM * 16));  // k-rows + 4
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    return u32x4_t{a.x, a.y, b.x, b.y};
+  }
+}
+
 // Tile (tm, tn) of linear tile index t: groups of group_m m-tiles by all
 // n-tiles, m fastest inside a group (tile indices are first made contiguous
 // per XCD, so one XCD works on neighbouring tiles and shares their panels in
@@ -105,6 +157,7 @@ __device__ __forceinline__ void tile_of(int64_t t, int tiles_m, int tiles_n, int
 // BM x BN blocks, WGM x WGN wavefronts, each a (BM / WGM) x (BN / WGN) part of
 // R x S 32 x 32 MFMA blocks; two LDS stages of BK k-values (one in flight
 // while the other is multiplied); WPE wavefronts per SIMD to compile for.
+// LAYOUT: bit 0, A k-major; bit 1, B k-major.
 //
 // Persistent: the grid holds as many workgroups as the chip runs at once, and
 // each walks its own sequence of tiles as one flat loop over (tile, k-step),
@@ -114,9 +167,12 @@ __device__ __forceinline__ void tile_of(int64_t t, int tiles_m, int tiles_n, int
 // its gridDim / 8 workgroups every (gridDim / 8)-th tile of it, so the tiles
 // one XCD has in flight are neighbours in the order (tile_of) and share
 // operand panels in that XCD's L2.
-template <int OUT, int BM, int BN, int BK, int NS, int WGM, int WGN, int WPE>
+template <int OUT, int LAYOUT, int BM, int BN, int BK, int NS, int WGM, int WGN, int WPE>
 __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void gemm_nt_kernel(const GemmArgs g) {
+  constexpr bool AKM = LAYOUT & 1, BKM = LAYOUT & 2;
+  constexpr int CPA = BM / 8, CPB = BN / 8;        // 16-byte chunks per k-major k-row
+  static_assert(CPA >= 16 && CPB >= 16, "the k-major swizzle spans 16 chunks");
   constexpr int NW = WGM * WGN, NT = NW * 64;
   constexpr int R = BM / (32 * WGM), S = BN / (32 * WGN);
   constexpr int CPR = BK / 8;                      // 16-byte chunks per tile row
@@ -143,7 +199,7 @@ void gemm_nt_kernel(const GemmArgs g) {
   const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
   const int64_t xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds, slot = blockIdx.x / kXcds;
   const int64_t q = tiles / kXcds, rem = tiles % kXcds;
-  const int64_t first = xcd * q + min(xcd, rem) + slot;  // this workgroup's first tile
+  const int64_t first = xcd * q + (xcd < rem ? xcd : rem) + slot;  // this workgroup's first tile
   const int64_t range = q + (xcd < rem ? 1 : 0);         // tiles of this XCD
   const int64_t mine = range > slot ? (range - 1 - slot) / per_xcd + 1 : 0;
   if (mine == 0) return;
@@ -198,21 +254,20 @@ void gemm_nt_kernel(const GemmArgs g) {
             const float lo[2] = {acc[a][b][4 * j], acc[a][b][4 * j + 1]};
             const float hi[2] = {acc[a][b][4 * j + 2], acc[a][b][4 * j + 3]};
             const uint2 w = make_uint2(Dt<VSCE_BF16>::pack_word(lo), Dt<VSCE_BF16>::pack_word(hi));
-            uint2* p = reinterpret_cast<uint2*>(buf + r32 * 8 + ((b * 4 + j) ^ (r32 & 7)));
-            p[khalf] = w;
+            lds_put(reinterpret_cast<uint2*>(buf + r32 * 8 + ((b * 4 + j) ^ (r32 & 7))) + khalf, w);
           }
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          buf[r32 * 8 + ((2 * j + khalf) ^ (r32 & 7))] =
+          lds_put(buf + r32 * 8 + ((2 * j + khalf) ^ (r32 & 7)),
               make_uint4(__float_as_uint(acc[a][b0][4 * j]), __float_as_uint(acc[a][b0][4 * j + 1]),
                          __float_as_uint(acc[a][b0][4 * j + 2]),
-                         __float_as_uint(acc[a][b0][4 * j + 3]));
+                         __float_as_uint(acc[a][b0][4 * j + 3])));
       }
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int row = rr * 8 + rrow;
-        const uint4 v = buf[row * 8 + (rc8 ^ (row & 7))];
+        const uint4 v = lds_get(buf + row * 8 + (rc8 ^ (row & 7)));
         const int64_t mrow = static_cast<int64_t>(wm * (BM / WGM) + a * 32 + row) * g.ldc;
         const int n = n0 + wn * (BN / WGN) + (OUT == kGemmOutBf16 ? rc8 * 8 : b0 * 32 + rc8 * 4);
         const uint32_t off = n < g.N ? static_cast<uint32_t>((mrow + n) * ES) : kOutOfRange;
@@ -248,38 +303,60 @@ void gemm_nt_kernel(const GemmArgs g) {
   }
 
   // This lane's chunk of each of the wavefront's loads: chunk j = q 64 + lane
-  // of an operand's stage is LDS position j, which swz() assigns to (row
-  // j / CPR, k-chunk (j mod CPR) xor f(row)); the XOR is its own inverse.
+  // of an operand's stage is LDS position j.  Row layout: swz() assigns it to
+  // (row j / CPR, k-chunk (j mod CPR) xor f(row)); k-major: to (k-row j / CP,
+  // chunk (j mod CP) xor 4 (k-row mod 4)).  Each XOR is its own inverse.
   uint32_t offa[LA], offb[LB];
-  auto chunk_offset = [&](int j, int64_t ld) {
+  auto chunk_offset = [&](int j, int64_t ld, bool km, int cp) {
+    if (km) {
+      const int k = j / cp;
+      const int c = (j % cp) ^ (4 * (k & 3));
+      return static_cast<uint32_t>((k * ld + c * 8) * 2);  // < 2^30: k < 64, ld < 2^23
+    }
     const int row = j / CPR;
     const int kc = swz<BK>(row, j % CPR) - row * CPR;
     return static_cast<uint32_t>((row * ld + kc * 8) * 2);  // < 2^32: ld < 2^23
   };
 #pragma unroll
-  for (int i = 0; i < LA; ++i) offa[i] = chunk_offset((wave * LA + i) * kWave + lane, g.lda);
+  for (int i = 0; i < LA; ++i)
+    offa[i] = chunk_offset((wave * LA + i) * kWave + lane, g.lda, AKM, CPA);
 #pragma unroll
-  for (int i = 0; i < LB; ++i) offb[i] = chunk_offset((wave * LB + i) * kWave + lane, g.ldb);
+  for (int i = 0; i < LB; ++i)
+    offb[i] = chunk_offset((wave * LB + i) * kWave + lane, g.ldb, BKM, CPB);
   // The load cursor: tile ordinal and k-step of the next stage to load, and
-  // one resource per operand tile (rows past those in memory read as zeros).
+  // one resource per operand: per tile for the row layout (rows past a_rows /
+  // b_rows read as zeros), per stage for k-major (k-rows past a_rows / b_rows,
+  // and columns past M / N of the last k-row, read as zeros; other columns
+  // past M / N only reach rows of C that are not stored).
   int64_t l_ord = 0;
-  int l_k = 0;
+  int l_k = 0, l_m0 = 0, l_n0 = 0;
   __amdgpu_buffer_rsrc_t ra, rb;
+  auto row_rsrc = [&](const void* X, int64_t ld, int rows_mem, int r0, int rows) {
+    const int n = max(0, min(rows, rows_mem - r0));
+    return uniform_rsrc(static_cast<const uint16_t*>(X) + static_cast<int64_t>(r0) * ld,
+                        static_cast<int64_t>(n) * ld * 2);
+  };
+  auto km_rsrc = [&](const void* X, int64_t ld, int krows_mem, int cols, int k0, int c0) {
+    const int64_t left = (static_cast<int64_t>(krows_mem - 1 - k0) * ld + (cols - c0)) * 2;
+    const int64_t cap = int64_t(1) << 31;  // past every offset of a stage (< 2^30)
+    return uniform_rsrc(static_cast<const uint16_t*>(X) + static_cast<int64_t>(k0) * ld + c0,
+                        left <= 0 ? 0 : (left < cap ? left : cap));
+  };
   auto aim = [&](int64_t ord) {
-    int m0, n0;
-    origin(ord, m0, n0);
-    const int rows_a = max(0, min(BM, g.a_rows - m0)), rows_b = max(0, min(BN, g.b_rows - n0));
-    ra = uniform_rsrc(static_cast<const uint16_t*>(g.A) + static_cast<int64_t>(m0) * g.lda,
-                      static_cast<int64_t>(rows_a) * g.lda * 2);
-    rb = uniform_rsrc(static_cast<const uint16_t*>(g.B) + static_cast<int64_t>(n0) * g.ldb,
-                      static_cast<int64_t>(rows_b) * g.ldb * 2);
+    origin(ord, l_m0, l_n0);
+    if constexpr (!AKM) ra = row_rsrc(g.A, g.lda, g.a_rows, l_m0, BM);
+    if constexpr (!BKM) rb = row_rsrc(g.B, g.ldb, g.b_rows, l_n0, BN);
   };
   auto load_next = [&](int s) {
     if (l_ord == mine) return;
-    const uint32_t kb = static_cast<uint32_t>(l_k * BK) * 2u;
+    const int k0 = l_k * BK;
+    if constexpr (AKM) ra = km_rsrc(g.A, g.lda, g.a_rows, g.M, k0, l_m0);
+    if constexpr (BKM) rb = km_rsrc(g.B, g.ldb, g.b_rows, g.N, k0, l_n0);
+    const uint32_t ka = AKM ? 0u : static_cast<uint32_t>(k0) * 2u;
+    const uint32_t kb = BKM ? 0u : static_cast<uint32_t>(k0) * 2u;
 #pragma unroll
     for (int i = 0; i < LA; ++i)
-      load16_lds(ra, &lds[s][(wave * LA + i) * kWave], offa[i] + kb);
+      load16_lds(ra, &lds[s][(wave * LA + i) * kWave], offa[i] + ka);
 #pragma unroll
     for (int i = 0; i < LB; ++i)
       load16_lds(rb, &lds[s][BM * CPR + (wave * LB + i) * kWave], offb[i] + kb);
@@ -308,16 +385,13 @@ void gemm_nt_kernel(const GemmArgs g) {
     const uint4* Bs = lds[s] + BM * CPR;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const int kc = ks * 2 + khalf;  // this lane's 8 k-values of the step
       u32x4_t fa[R], fb[S];
 #pragma unroll
       for (int a = 0; a < R; ++a)
-        fa[a] = *reinterpret_cast<const u32x4_t*>(
-            As + swz<BK>(wm * (BM / WGM) + a * 32 + r32, kc));
+        fa[a] = fragment<AKM, BK, CPA>(As, wm * (BM / WGM) + a * 32, ks, lane);
 #pragma unroll
       for (int b = 0; b < S; ++b)
-        fb[b] = *reinterpret_cast<const u32x4_t*>(
-            Bs + swz<BK>(wn * (BN / WGN) + b * 32 + r32, kc));
+        fb[b] = fragment<BKM, BK, CPB>(Bs, wn * (BN / WGN) + b * 32, ks, lane);
 #pragma unroll
       for (int a = 0; a < R; ++a)
 #pragma unroll
@@ -360,9 +434,9 @@ int resident_workgroups(Kernel kernel, int threads) {
   return n;
 }
 
-template <int OUT, int BM, int BN, int BK, int NS, int WGM, int WGN, int WPE>
+template <int OUT, int LAYOUT, int BM, int BN, int BK, int NS, int WGM, int WGN, int WPE>
 int launch_persistent(const GemmArgs& g, hipStream_t s) {
-  auto kernel = gemm_nt_kernel<OUT, BM, BN, BK, NS, WGM, WGN, WPE>;
+  auto kernel = gemm_nt_kernel<OUT, LAYOUT, BM, BN, BK, NS, WGM, WGN, WPE>;
   const int threads = WGM * WGN * 64;
   const int64_t tiles = static_cast<int64_t>((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   const int resident = resident_workgroups(kernel, threads);
@@ -375,23 +449,39 @@ int launch_persistent(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
 }
 
+template <int OUT, int BM, int BN, int BK, int NS, int WGM, int WGN, int WPE>
+int launch_layout(const GemmArgs& g, hipStream_t s) {
+  switch (g.layout) {
+    case 0: return launch_persistent<OUT, 0, BM, BN, BK, NS, WGM, WGN, WPE>(g, s);
+    case 1: return launch_persistent<OUT, 1, BM, BN, BK, NS, WGM, WGN, WPE>(g, s);
+    case 2: return launch_persistent<OUT, 2, BM, BN, BK, NS, WGM, WGN, WPE>(g, s);
+    case 3: return launch_persistent<OUT, 3, BM, BN, BK, NS, WGM, WGN, WPE>(g, s);
+    default: return VSCE_ERR_INVALID;
+  }
+}
+
 template <int BM, int BN, int BK, int NS, int WGM, int WGN, int WPE>
 int launch_blocks(int out, const GemmArgs& g, hipStream_t s) {
   switch (out) {
-    case kGemmOutBf16: return launch_persistent<kGemmOutBf16, BM, BN, BK, NS, WGM, WGN, WPE>(g, s);
-    case kGemmOutF32: return launch_persistent<kGemmOutF32, BM, BN, BK, NS, WGM, WGN, WPE>(g, s);
-    case kGemmOutF32Add:
-      return launch_persistent<kGemmOutF32Add, BM, BN, BK, NS, WGM, WGN, WPE>(g, s);
+    case kGemmOutBf16: return launch_layout<kGemmOutBf16, BM, BN, BK, NS, WGM, WGN, WPE>(g, s);
+    case kGemmOutF32: return launch_layout<kGemmOutF32, BM, BN, BK, NS, WGM, WGN, WPE>(g, s);
+    case kGemmOutF32Add: return launch_layout<kGemmOutF32Add, BM, BN, BK, NS, WGM, WGN, WPE>(g, s);
     default: return VSCE_ERR_INVALID;
   }
+}
+
+// An operand's leading dimension: a multiple of 8, below 2^23, and at least
+// its contiguous extent (K in the row layout, its rows when k-major).
+bool ld_ok(int64_t ld, int64_t contiguous) {
+  return ld % 8 == 0 && ld >= contiguous && ld < (int64_t(1) << 23);
 }
 
 }  // namespace
 
 int launch_gemm_nt(int out, const GemmArgs& g, hipStream_t s) {
   if (g.M < 0 || g.N < 0 || g.K < 0 || g.K % kKMult != 0 || g.N % 4 != 0 || g.ldc % 4 != 0 ||
-      g.lda % 8 != 0 || g.ldb % 8 != 0 || g.lda < g.K || g.ldb < g.K || g.ldc < g.N ||
-      g.lda >= (int64_t(1) << 23) || g.ldb >= (int64_t(1) << 23) || g.group_m < 1 ||
+      g.layout < 0 || g.layout > 3 || !ld_ok(g.lda, (g.layout & 1) ? g.M : g.K) ||
+      !ld_ok(g.ldb, (g.layout & 2) ? g.N : g.K) || g.ldc < g.N || g.group_m < 1 ||
       g.a_rows < 0 || g.b_rows < 0 ||
       g.ldc * (out == kGemmOutBf16 ? 2 : 4) > (int64_t(1) << 23))
     return VSCE_ERR_INVALID;

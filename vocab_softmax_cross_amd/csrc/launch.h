@@ -103,9 +103,11 @@ int launch_merge(const Prob& p, const float* partials, int shards, float* stats,
 int launch_scale(const Prob& p, RowArgs a, hipStream_t s);
 
 // bf16 GEMM on the matrix cores: C[m, n] = sum_k A[m, k] B[n, k] with fp32
-// accumulation.  A is [M, K] and B [N, K], both contiguous along k (leading
-// dimensions lda, ldb in elements, multiples of 8, at most 2^23), 16-byte
-// aligned; K a multiple of 64; N and ldc multiples of 4.  Device-side counts
+// accumulation.  A is [M, K] and B [N, K], each either contiguous along k
+// (the row layout) or stored k-major as [K][M] / [K][N] (layout); leading
+// dimensions lda, ldb in elements, multiples of 8, below 2^23, at least K in
+// the row layout and M / N when k-major; 16-byte aligned; K a multiple of 64;
+// N and ldc multiples of 4, a row of C at most 2^23 bytes.  Device-side counts
 // (optional) narrow the work without a host read: rows m >= *m_count are
 // neither computed nor stored, and k runs to *k_count rounded up to 64 (the
 // caller keeps A and B zero between the count and that bound).
@@ -117,12 +119,16 @@ struct GemmArgs {
   void* C;
   int64_t ldc;
   int M, N, K;
-  int a_rows, b_rows;     // rows of A and B in memory (rows past them read as zeros)
+  // Rows of A and B in memory, rows past them read as zeros: m- / n-rows in
+  // the row layout ([M][lda], [N][ldb]), k-rows when k-major ([K][lda], [K][ldb]).
+  int a_rows, b_rows;
+  int layout;             // bit 0: A k-major; bit 1: B k-major
   int group_m;            // m-tiles per group of the tile order (>= 1)
   const int* m_count;     // device, or null (all M rows)
   const int* k_count;     // device, or null (all K)
 };
 enum { kGemmOutBf16 = 0, kGemmOutF32 = 1, kGemmOutF32Add = 2 };
+enum { kGemmAKMajor = 1, kGemmBKMajor = 2 };
 int launch_gemm_nt(int out, const GemmArgs& g, hipStream_t s);
 
 }  // namespace vsce

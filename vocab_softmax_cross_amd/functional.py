@@ -362,15 +362,29 @@ def status(workspace: torch.Tensor) -> dict:
 
 # ---------------------------------------------------------------- FLCE
 
+def _operand(x: torch.Tensor, name: str):
+    """(leading dimension, k-major) of a [rows, K] operand: contiguous along K
+    (the row layout), else contiguous along its rows (a transposed view of a
+    [K, rows] tensor, read k-major)."""
+    if x.stride(1) == 1 or x.shape[1] == 1:
+        return x.stride(0), False
+    if x.stride(0) == 1 or x.shape[0] == 1:
+        return x.stride(1), True
+    raise ValueError(f"{name} must be contiguous along one of its dimensions")
+
+
 def gemm_bf16_nt(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None,
                  accumulate: bool = False, out_dtype=torch.bfloat16) -> torch.Tensor:
-    """vsce_gemm_bf16_nt: a @ b.T for bf16 a [M, K] and b [N, K] (contiguous
-    rows, K a multiple of 64) on the matrix cores; bf16 or fp32 out, or added
-    to an fp32 `out` when accumulate."""
+    """vsce_gemm_bf16: a @ b.T for bf16 a [M, K] and b [N, K] on the matrix
+    cores (K a multiple of 64); each operand contiguous along K or along its
+    rows (e.g. g.t() for a [K, M] tensor g, read in place); bf16 or fp32 out,
+    or added to an fp32 `out` when accumulate."""
     if a.dtype != torch.bfloat16 or b.dtype != torch.bfloat16 or a.dim() != 2 or b.dim() != 2:
         raise ValueError("a and b must be 2-D bfloat16 tensors")
-    if a.shape[1] != b.shape[1] or a.stride(1) != 1 or b.stride(1) != 1:
-        raise ValueError("a and b must share K and be contiguous along it")
+    if a.shape[1] != b.shape[1]:
+        raise ValueError("a and b must share K")
+    lda, a_km = _operand(a, "a")
+    ldb, b_km = _operand(b, "b")
     M, K = a.shape
     N = b.shape[0]
     if out is None:
@@ -381,8 +395,9 @@ def gemm_bf16_nt(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] =
         if out.dtype == torch.float32 else L.GEMM_OUT_BF16
     if out.dtype not in (torch.float32, torch.bfloat16) or out.shape != (M, N) or out.stride(1) != 1:
         raise ValueError("out must be a [M, N] float32 or bfloat16 tensor with contiguous rows")
-    L.vsce_gemm_bf16_nt(a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0), out.data_ptr(),
-                        out.stride(0), M, N, K, mode, _stream(a))
+    layout = (L.GEMM_A_K_MAJOR if a_km else 0) | (L.GEMM_B_K_MAJOR if b_km else 0)
+    L.vsce_gemm_bf16(a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), out.stride(0), M, N, K,
+                     layout, mode, _stream(a))
     return out
 
 
