@@ -514,6 +514,30 @@ def main():
                     "ms": round(copy_s * 1e3, 4),
                     "GBps": round(2 * wl.BT * row_bytes / copy_s / 1e9, 1)}
 
+    # Peak memory of one fused forward + backward through the autograd entry
+    # point, beside the logits it overwrites (the pages' measure: the
+    # gradient takes the logits' place, so the peak is one logits tensor).
+    from vocab_softmax_cross_amd import cross_entropy
+    xm = ring[0]
+    xm.copy_(pristine)
+    xm.requires_grad_(True)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base_alloc = torch.cuda.memory_allocated()
+    loss_m = cross_entropy(xm, t, label_smoothing=wl.label_smoothing, reduction=red)
+    loss_m.backward()
+    torch.cuda.synchronize()
+    extra_alloc = torch.cuda.max_memory_allocated() - base_alloc
+    logits_bytes = wl.BT * row_bytes
+    peak_memory = {"kind": "torch max_memory_allocated over one fused forward + backward "
+                           "(the cross_entropy autograd function), beyond what was allocated before",
+                   "logits_MB": round(logits_bytes / 1e6, 1),
+                   "extra_bytes": int(extra_alloc),
+                   "peak_MB_with_logits": round((logits_bytes + extra_alloc) / 1e6, 1)}
+    del loss_m
+    xm.grad = None
+    xm.requires_grad_(False)
+
     for a, b in ev:
         hip.destroy(a)
         hip.destroy(b)
@@ -550,6 +574,7 @@ def main():
                      "mean_launch_ms": round(mean_kernel_s * 1e3, 4)},
         "modes": extra,
         "copy_ceiling": copy_ceiling,
+        "peak_memory": peak_memory,
         "cpu_baseline": cpu,
         "cpu_baseline_1thread": cpu1,
         "cpu_baseline_flce": cpu_flce,
