@@ -214,27 +214,35 @@ __device__ __forceinline__ T fresh_args() {
 }
 
 // ---------------------------------------------------------------- soft-capping
-// Logit soft-capping x -> s tanh(x / s) and its slope 1 - tanh^2(x / s), both
-// from q = exp(-2 |x| / s) in [0, 1] through the identities
+// Logit soft-capping x -> s tanh(x / s) and its slope 1 - tanh^2(x / s), each
+// with one hardware exp and one reciprocal.
+//
+// value(x) (the sums of the statistics pass, the maximum, the target logit):
+//   s tanh(x / s) = s - 2 s / (1 + e),   e = exp(2 x / s),
+// one fma after the reciprocal and no sign handling: e = +inf gives s, e = 0
+// gives -s.  The result is accurate to a few units of 2^-24 s.
+//
+// value(x, slope) (the gradient pass, which also needs the slope) works from
+// q = exp(-2 |x| / s) in [0, 1], taken as q4 = 4 q = 2^(-2 |x| log2(e) / s + 2):
 //   tanh(|x| / s) = (1 - q) / (1 + q),   1 - tanh^2(x / s) = 4 q / (1 + q)^2,
-// with one hardware exp and one reciprocal.  q keeps its relative accuracy
-// for every x, so the slope does too (no 1 - t^2 cancellation where the cap
-// saturates); the capped value is accurate to a few units of 2^-24 s.
+// so s tanh(|x| / s) = (s - (s / 4) q4) r and the slope is q4 r^2 with
+// r = 1 / (1 + q4 / 4).  q keeps its relative accuracy for every x, so the
+// slope does too (no 1 - t^2 cancellation where the cap saturates).  The two
+// forms of the capped value differ by a few units of 2^-24 s.
 // A NaN logit stays NaN; +-inf caps to +-s with slope 0.
 struct SoftCap {
   float s;  // the cap, > 0
   float k;  // -2 log2(e) / s
 
   __device__ __forceinline__ float value(float x) const {
-    const float q = __builtin_amdgcn_exp2f(__builtin_fabsf(x) * k);
-    const float t = (1.0f - q) * __builtin_amdgcn_rcpf(1.0f + q);
-    return __builtin_copysignf(s * t, x);
+    const float e = __builtin_amdgcn_exp2f(-k * x);
+    return __builtin_fmaf(-2.0f * s, __builtin_amdgcn_rcpf(1.0f + e), s);
   }
   __device__ __forceinline__ float value(float x, float& slope) const {
-    const float q = __builtin_amdgcn_exp2f(__builtin_fabsf(x) * k);
-    const float r = __builtin_amdgcn_rcpf(1.0f + q);
-    slope = 4.0f * q * r * r;
-    return __builtin_copysignf(s * ((1.0f - q) * r), x);
+    const float q4 = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fabsf(x), k, 2.0f));
+    const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(q4, 0.25f, 1.0f));
+    slope = q4 * r * r;
+    return __builtin_copysignf(__builtin_fmaf(-0.25f * s, q4, s) * r, x);
   }
 };
 
