@@ -778,3 +778,76 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(static_x, eager_g)
         assert torch.equal(res["loss"], eager_l)
         _ = (pristine.float() * 2).sum()  # unrelated eager work between replays
+
+
+# ---------------------------------------------------------------- rows with an overflow
+# Uncapped, unweighted rows a little past the largest two-rows-per-CU shape
+# (16320 vectors on chip) keep that shape and read the rest, the overflow,
+# twice: 3 or 6 more vectors per thread (bf16 / f16 V <= 155136 / 179712,
+# fp32 V <= 77568 / 89856).
+
+ONCHIP_VECTORS = 16320
+
+
+def _overflow_case(V, dtype, label_smoothing=0.1):
+    """Rows engineered around the overflow: the target in it, a dominant
+    target in it (confident row), maxima tied between the chip and the
+    overflow and within the overflow, and an ignored row."""
+    wl = _small("llm_head", 12, V, dtype=dtype, ignore_frac=0.0, label_smoothing=label_smoothing)
+    tgt = W.targets(wl)
+    xh = W.logits(wl, tgt)
+    vec = 4 if dtype == "f32" else 8
+    ov0 = ONCHIP_VECTORS * vec  # first overflow column
+    assert ov0 < V
+    c1, c2, c3, c4 = 100, ov0 + 7, ov0 + 5, V - 3
+    tgt[0] = V - 1
+    tgt[1] = ov0
+    tgt[2] = ov0 + 1234 % (V - ov0)
+    xh[2, int(tgt[2])] = 24.0
+    for r, y in ((3, c1), (4, c2)):
+        xh[r, c1] = xh[r, c2] = 16.0
+        tgt[r] = y
+    xh[5, c3] = xh[5, c4] = 16.0
+    tgt[5] = c4
+    xh[6, c3] = 16.0
+    tgt[6] = c3
+    tgt[7] = -100
+    return wl, xh, tgt
+
+
+@pytest.mark.parametrize("V,dtype", [(131072, "bf16"), (155136, "bf16"), (155144, "bf16"),
+                                     (179712, "bf16"), (151936, "f16"), (70000, "f32"),
+                                     (89856, "f32")])
+@pytest.mark.parametrize("reduction,go", [("mean", 1.0), ("none", 0.37)])
+def test_overflow_rows(V, dtype, reduction, go):
+    """Every overflow shape, at its capacity and just past the one before;
+    targets, maxima and ties inside the overflow."""
+    wl, xh, tgt = _overflow_case(V, dtype)
+    out, xh, tgt, w = run(wl, "fused", reduction, go, accuracy=True, x_host=xh, tgt=tgt)
+    check(wl, out, reference(wl, xh, tgt, w, reduction, go), xh, tgt, w)
+    assert out["acc"][3] == 1.0 and out["acc"][4] == 0.0 and out["acc"][5] == 0.0
+    assert out["acc"][6] == 1.0
+
+
+def test_overflow_rows_confident_without_smoothing():
+    """A dominant target in the overflow without smoothing: the strict 1-ulp
+    bar for every gradient element, and the loss of the confident row."""
+    wl, xh, tgt = _overflow_case(151936, "bf16", label_smoothing=0.0)
+    out, xh, tgt, w = run(wl, "fused", "none", 1.0, accuracy=True, x_host=xh, tgt=tgt)
+    check(wl, out, reference(wl, xh, tgt, w, "none", 1.0), xh, tgt, w, strict_bf16=True)
+
+
+def test_overflow_nan_propagates():
+    """A NaN logit in the overflow reaches its row's loss and gradient only."""
+    dev = _dev()
+    wl = _small("llm_head", 4, 131072)
+    tgt = W.targets(wl)
+    xh = W.logits(wl, tgt)
+    xh[2, ONCHIP_VECTORS * 8 + 9] = float("nan")
+    x = xh.to(dev)
+    t = torch.from_numpy(tgt).to(dev)
+    res = vf.forward_fused_inplace(x, t, reduction="none")
+    torch.cuda.synchronize()
+    loss = res["loss"].cpu()
+    assert math.isnan(loss[2]) and torch.isfinite(loss[[0, 1, 3]]).all()
+    assert torch.isnan(x[2]).all() and torch.isfinite(x[[0, 1, 3]]).all()

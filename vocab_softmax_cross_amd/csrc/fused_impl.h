@@ -14,6 +14,15 @@
 //   3. the gradient, written over the logits with one store per vector; the
 //      lane that owns the target column substitutes the fp32 true-class value
 //      before its store.
+// Rows a little longer than the chip holds (NOV > 0, uncapped logits): the
+// first NT * NREG + LDS_CAP vectors are held as above and the rest, the
+// overflow (thread t: vectors ONCHIP + k NT + t, k < NOV), is read twice
+// instead: once before the row's first register slots are loaded, folded
+// into an online (maximum, sum below it, count of it, first index of it,
+// logit sum), merged over the wavefront and parked in LDS, which joins the
+// row maximum in pass 1 and the pass-2 sums once that maximum is known; and
+// once more in pass 3, for its gradient.  Two rows per CU stay resident, at
+// the cost of reading the overflow twice.
 // The design follows the fused kernel of Liger-Kernel PR #1268 ("pass 1"
 // online statistics, "pass 2" in-place gradient, one O(1) true-class
 // correction, fp32 per the linkedin#1329 commit message), with the second
@@ -37,7 +46,9 @@ namespace {
 // are taken on the stored logits (capping does not reorder them); every sum,
 // the loss and the gradient read the capped values, and each gradient element
 // is multiplied by the slope of the cap at its own stored logit.
-template <int DT, int NT, int NREG, int NLDS, int LDS_CAP, bool WEIGHTED, bool CAP, int WPE>
+// NOV: overflow vectors per thread (0: the row fits on chip).
+template <int DT, int NT, int NREG, int NLDS, int LDS_CAP, int NOV, bool WEIGHTED, bool CAP,
+          int WPE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
 void fused_resident_kernel(const RowArgs a) {
   using D = Dt<DT>;
@@ -46,10 +57,18 @@ void fused_resident_kernel(const RowArgs a) {
   constexpr uint32_t SLOT_BYTES = NT * 16u;  // bytes between a thread's vectors
   static_assert(LDS_CAP <= NLDS * NT && LDS_CAP > (NLDS - 1) * NT - (NLDS == 0 ? 1 : 0),
                 "the capped LDS must still reach into the last LDS slot");
+  static_assert(NOV == 0 || (!CAP && !WEIGHTED && NOV <= NREG),
+                "overflow: uncapped, unweighted rows, reusing registers");
+  constexpr int ONCHIP = NT * NREG + LDS_CAP;  // vectors held on chip
   __shared__ uint4 xl[NLDS > 0 ? LDS_CAP : 1];
   __shared__ float red_max[NW];
   __shared__ float4 red_sum[NW];
   __shared__ float xy_sh;  // the stored target logit, posted by its owner lane
+  // Each wavefront's overflow state (NOV > 0): maximum, sum below it, logit
+  // sum, count at it, first index of it.
+  constexpr int NWO = NOV > 0 ? NW : 1;
+  __shared__ float ov_m[NWO], ov_s[NWO], ov_S[NWO];
+  __shared__ int ov_c[NWO], ov_f[NWO];
 
   const int tid = threadIdx.x;
   const int64_t n = xcd_contiguous(blockIdx.x, a.rows);
@@ -57,10 +76,20 @@ void fused_resident_kernel(const RowArgs a) {
   char* rowb = static_cast<char*>(a.x) + n * a.stride * D::BYTES;
   const auto rsrc = make_rsrc(rowb, static_cast<uint32_t>(a.V * D::BYTES));
   const uint32_t voff = static_cast<uint32_t>(tid) * 16u;
-  auto in_row = [&](int k) { return k * NT + tid < nvec; };
+  // On-chip slot k of this thread is in the row (with an overflow, only the
+  // first ONCHIP vectors are on chip: no lane past LDS_CAP touches LDS).
+  const int nchip = NOV > 0 ? min(nvec, ONCHIP) : nvec;
+  auto in_row = [&](int k) { return k * NT + tid < nchip; };
   // Lanes past the end of the row get a per-lane offset beyond num_records,
   // so the buffer range check drops them whether or not it counts soffset.
   auto lane_off = [&](int k) { return in_row(k) ? voff : kOutOfRange; };
+  // Overflow vector k of thread t, addressed by its per-lane offset alone.
+  // Callers pass a fresh_tid() of their own, so that the offsets are
+  // computed where they are used instead of held in registers in between.
+  auto ov_col = [&](int k, int t) { return ONCHIP + k * NT + t; };
+  auto ov_off = [&](int k, int t) {
+    return ov_col(k, t) < nvec ? static_cast<uint32_t>(ov_col(k, t)) * 16u : kOutOfRange;
+  };
   const int64_t y = a.target[n];
   const int cls = row_class(y, a.Vt, a.ignore_index);
   const SoftCap cap{a.cap, a.cap_k};
@@ -68,6 +97,7 @@ void fused_resident_kernel(const RowArgs a) {
   if (cls != kValid) {  // uniform over the workgroup: zero gradient, no read
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
     static_for<NREG + NLDS>([&](auto k) { buf_store16(rsrc, lane_off(k), k * SLOT_BYTES, z); });
+    static_for<NOV>([&](auto k) { buf_store16(rsrc, ov_off(k, tid), 0u, z); });
     const float l = (cls == kIgnored) ? 0.0f : __builtin_nanf("");
     if (tid == 0) store_row(a, n, l, 0.0f, l);
     return;
@@ -76,8 +106,12 @@ void fused_resident_kernel(const RowArgs a) {
 
   // ---- one read of the row: registers, then LDS (lanes past the row read 0
   //      and are masked out of every pass below)
+  // (With an overflow, slots 0 .. NOV-1 are loaded after it: their registers
+  // first carry the overflow.)
   uint4 r[NREG];
-  static_for<NREG>([&](auto k) { r[k] = buf_load16(rsrc, lane_off(k), k * SLOT_BYTES); });
+  static_for<NREG>([&](auto k) {
+    if constexpr (k >= NOV) r[k] = buf_load16(rsrc, lane_off(k), k * SLOT_BYTES);
+  });
   if constexpr (NLDS > 0) {
     const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~(kWave - 1));
     // Exec-masked rather than range-checked: lanes past the row write nothing
@@ -89,8 +123,6 @@ void fused_resident_kernel(const RowArgs a) {
   }
 
 
-  // ---- pass 1: row maximum
-  float mx = -__builtin_inff();
   // Every pass works on one 32-bit word (EPW elements) at a time, so only a
   // few fp32 temporaries are live next to the resident row.
   constexpr int EPW = D::EPW;
@@ -98,6 +130,94 @@ void fused_resident_kernel(const RowArgs a) {
     struct W4 { uint32_t w[4]; };
     return W4{{v.x, v.y, v.z, v.w}};
   };
+  // ---- the overflow, read for the first time: an online maximum om, the sum
+  //      osum of exp(x - om) over elements below it, their count oc at it, the
+  //      first index of it and the logit sum.  A vector that raises om rescales
+  //      what came before once (the elements then at the old maximum join the
+  //      sum).  The owner of the target column posts x[y] here.  The lanes'
+  //      states are merged over the wavefront (the same rescaling) and lane 0
+  //      parks the result in LDS, so no register carries it through pass 1.
+  if constexpr (NOV > 0) {
+    float om = -__builtin_inff(), osum = 0.0f, oS = 0.0f;
+    int oc = 0, ofirst = 0x7fffffff;
+    const int jy_ov = static_cast<int>(y / VEC) - ONCHIP;  // < 0: on chip
+    const int iy_ov = static_cast<int>(y % VEC);
+    auto online = [&](const uint4 v, int j) {
+      // Word by word, as the passes below: few fp32 temporaries next to the
+      // register slots already in flight.
+      const auto w = words(v);
+      float bm = -__builtin_inff();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float f[EPW];
+        D::word_fresh(w.w[q], f);
+#pragma unroll
+        for (int e = 0; e < EPW; ++e) bm = fmaxf(bm, f[e]);
+      }
+      if (bm > om) {
+        osum = (osum + static_cast<float>(oc)) * __builtin_amdgcn_exp2f((om - bm) * kLog2e);
+        om = bm;
+        oc = 0;
+        ofirst = 0x7fffffff;
+      }
+      const float mL = om * kLog2e;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float f[EPW];
+        D::word_fresh(w.w[q], f);
+#pragma unroll
+        for (int e = 0; e < EPW; ++e) {
+          const int i = q * EPW + e;
+          const bool eq = f[e] == om;
+          osum += eq ? 0.0f : exp_shifted(f[e], mL);
+          oc += eq ? 1 : 0;
+          if (eq) ofirst = min(ofirst, j * VEC + i);
+          if constexpr (WEIGHTED) oS = __builtin_fmaf(a.weight[j * VEC + i], f[e], oS);
+          else oS += f[e];
+          if (j - ONCHIP == jy_ov && i == iy_ov) xy_sh = f[e];
+        }
+      }
+    };
+    // Exec-masked loads: one per-lane offset for all k, slot k in soffset.
+    const int t1 = fresh_tid();
+    const uint32_t vo1 = static_cast<uint32_t>(ONCHIP + t1) * 16u;
+    uint4 ov[NOV];
+    static_for<NOV>([&](auto k) {
+      if (ov_col(k, t1) < nvec) ov[k] = buf_load16(rsrc, vo1, k * SLOT_BYTES);
+    });
+    static_for<NOV>([&](auto k) {
+      if (ov_col(k, t1) < nvec) online(ov[k], ov_col(k, t1));
+    });
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d /= 2) {  // fixed order
+      const float m2 = __shfl_xor(om, d), s2 = __shfl_xor(osum, d), S2 = __shfl_xor(oS, d);
+      const int c2 = __shfl_xor(oc, d), f2 = __shfl_xor(ofirst, d);
+      const float mm = fmaxf(om, m2);
+      const float s1 = om == mm ? osum
+                                : (osum + static_cast<float>(oc)) *
+                                      __builtin_amdgcn_exp2f((om - mm) * kLog2e);
+      const float s2m = m2 == mm ? s2
+                                 : (s2 + static_cast<float>(c2)) *
+                                       __builtin_amdgcn_exp2f((m2 - mm) * kLog2e);
+      oc = (om == mm ? oc : 0) + (m2 == mm ? c2 : 0);
+      ofirst = min(om == mm ? ofirst : 0x7fffffff, m2 == mm ? f2 : 0x7fffffff);
+      om = mm;
+      osum = s1 + s2m;
+      oS += S2;
+    }
+    if ((tid & (kWave - 1)) == 0) {
+      const int wv = tid / kWave;
+      ov_m[wv] = om;
+      ov_s[wv] = osum;
+      ov_S[wv] = oS;
+      ov_c[wv] = oc;
+      ov_f[wv] = ofirst;
+    }
+    static_for<NOV>([&](auto k) { r[k] = buf_load16(rsrc, lane_off(k), k * SLOT_BYTES); });
+  }
+
+  // ---- pass 1: row maximum
+  float mx = -__builtin_inff();
   auto max_vec = [&](const uint4 v) {
     const auto w = words(v);
 #pragma unroll
@@ -125,7 +245,8 @@ void fused_resident_kernel(const RowArgs a) {
   const int ky = static_cast<int>(jy / NT);  // slot and lane owning the target
   const int ty = static_cast<int>(jy % NT);
   const int iy = static_cast<int>(y % VEC);
-  if (tid == ty) {
+  const bool y_chip = NOV == 0 || jy < ONCHIP;  // else posted by the overflow pass
+  if (tid == ty && y_chip) {
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (ky < NREG) {
       static_for<NREG>([&](auto k) {
@@ -142,6 +263,7 @@ void fused_resident_kernel(const RowArgs a) {
       if (e == iy) xv = f[e];
     xy_sh = xv;
   }
+  if constexpr (NOV > 0) mx = fmaxf(mx, ov_m[tid / kWave]);  // this wavefront's lane 0 wrote it
   const float M = block_max<NT>(mx, red_max);          // of the stored logits
   const float Mc = CAP ? uniform(cap.value(M)) : M;    // of the logits the loss reads
   const float ML = Mc * kLog2e;
@@ -184,6 +306,21 @@ void fused_resident_kernel(const RowArgs a) {
   // compare per element.
   if (__ballot(mx == M) != 0ull) sum_pass(std::true_type{});
   else sum_pass(std::false_type{});
+  if constexpr (NOV > 0) {  // the wavefront's overflow share, at the row maximum, on lane 0
+    if ((tid & (kWave - 1)) == 0) {
+      const int wv = tid / kWave;
+      const float om = ov_m[wv];
+      if (om == M) {
+        rs.s += ov_s[wv];
+        rs.cnt += ov_c[wv];
+        rs.first = min(rs.first, ov_f[wv]);
+      } else {
+        rs.s += (ov_s[wv] + static_cast<float>(ov_c[wv])) *
+                __builtin_amdgcn_exp2f((om - M) * kLog2e);
+      }
+      rs.S += ov_S[wv];
+    }
+  }
   rs = block_sums<NT>(rs, red_sum);
 
   const float dp = rs.s + static_cast<float>(rs.cnt - 1);  // d' = d - 1
@@ -236,7 +373,7 @@ void fused_resident_kernel(const RowArgs a) {
       }
       w.w[q] = D::pack_word(f);  // the result word replaces the input word
     }
-    if (k == ky && tid == ty) {
+    if (k == ky && tid == ty && y_chip) {
       // The owner of the target column writes the fp32 true-class value,
       // rounded once, in place of its softmax term.
       float f[EPW];
@@ -255,12 +392,41 @@ void fused_resident_kernel(const RowArgs a) {
     buf_store16(rsrc, voff, static_cast<uint32_t>(k) * SLOT_BYTES,
                 make_uint4(w.w[0], w.w[1], w.w[2], w.w[3]));
   };
+  // The overflow is read again once the registers of slots 0 .. NOV-1 are
+  // free, ahead of the stores of the later slots (so its wait does not cover
+  // them), and its gradient is written last.
   static_for<NREG>([&](auto k) {
     if (in_row(k)) grad_vec(r[k], k);
   });
   static_for<NLDS>([&](auto k) {
     if (in_row(NREG + k)) grad_vec(xl[k * NT + tid], NREG + k);
   });
+  if constexpr (NOV > 0) {
+    const int t3 = fresh_tid();
+    const uint32_t vo3 = static_cast<uint32_t>(ONCHIP + t3) * 16u;
+    uint4 ov2[NOV];
+    static_for<NOV>([&](auto q) {
+      if (ov_col(q, t3) < nvec) ov2[q] = buf_load16(rsrc, vo3, q * SLOT_BYTES);
+    });
+    static_for<NOV>([&](auto q) {
+      const int j = ov_col(q, t3);
+      if (j >= nvec) return;
+      auto w = words(ov2[q]);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        float f[EPW];
+        D::word_fresh(w.w[qq], f);
+#pragma unroll
+        for (int e = 0; e < EPW; ++e) {
+          const float b = WEIGHTED ? t.B * a.weight[j * VEC + qq * EPW + e] : t.B;
+          f[e] = __builtin_fmaf(exp_shifted(f[e], t.ML), t.K, -b);
+          if (static_cast<int64_t>(j) * VEC + qq * EPW + e == y) f[e] = t.dxy;
+        }
+        w.w[qq] = D::pack_word(f);
+      }
+      buf_store16(rsrc, vo3, q * SLOT_BYTES, make_uint4(w.w[0], w.w[1], w.w[2], w.w[3]));
+    });
+  }
   }
   (void)a0;
 }
@@ -268,10 +434,11 @@ void fused_resident_kernel(const RowArgs a) {
 // Shapes of the resident kernel: threads per workgroup, vectors per thread in
 // registers and in LDS, and the minimum wavefronts per SIMD to compile for
 // (which caps the registers per wavefront at 512 / WPE).
-template <int NT_, int NREG_, int NLDS_, int WPE_, int LDS_CAP_ = NT_ * NLDS_>
+template <int NT_, int NREG_, int NLDS_, int WPE_, int LDS_CAP_ = NT_ * NLDS_, int NOV_ = 0>
 struct Shape {
   static constexpr int NT = NT_, NREG = NREG_, NLDS = NLDS_, WPE = WPE_, LDS_CAP = LDS_CAP_;
-  static constexpr int64_t CAPACITY = static_cast<int64_t>(NT_) * NREG_ + LDS_CAP_;
+  static constexpr int NOV = NOV_;
+  static constexpr int64_t CAPACITY = static_cast<int64_t>(NT_) * (NREG_ + NOV_) + LDS_CAP_;
 };
 
 using Shapes = std::tuple<Shape<64, 4, 0, 4>,       // rows up to 256 vectors
@@ -281,13 +448,20 @@ using Shapes = std::tuple<Shape<64, 4, 0, 4>,       // rows up to 256 vectors
                           // 16320 vectors (bf16 V <= 130560): 2 workgroups per CU,
                           // 64 VGPRs and 79 KB of LDS each
                           Shape<1024, 11, 5, 8, 5056>,
+                          // the same with an overflow read twice (uncapped,
+                          // unweighted rows): 19392 / 22464 vectors (bf16 V
+                          // <= 155136 / 179712).  Past about a third of the
+                          // row in the overflow, one row per CU is faster.
+                          Shape<1024, 11, 5, 8, 5056, 3>,
+                          Shape<1024, 11, 5, 8, 5056, 6>,
                           Shape<1024, 16, 4, 4>,    // 20480 vectors
                           Shape<1024, 24, 8, 4>>;   // 32768 vectors
 
 template <int DT, bool W, bool CAP, class SH>
 int launch_shape(const Prob& p, const RowArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(
-      (fused_resident_kernel<DT, SH::NT, SH::NREG, SH::NLDS, SH::LDS_CAP, W, CAP, SH::WPE>),
+      (fused_resident_kernel<DT, SH::NT, SH::NREG, SH::NLDS, SH::LDS_CAP, SH::NOV, W, CAP,
+                             SH::WPE>),
                      dim3(static_cast<unsigned>(p.rows)), dim3(SH::NT), 0, s, a);
   return hipGetLastError() == hipSuccess ? VSCE_OK : VSCE_ERR_LAUNCH;
 }
@@ -298,8 +472,11 @@ int pick_shape(const Prob& p, const RowArgs& a, hipStream_t s) {
     return VSCE_ERR_UNSUPPORTED;
   } else {
     using SH = std::tuple_element_t<I, Shapes>;
-    if (a.nvec <= SH::CAPACITY)
-      return launch_shape<DT, W, CAP, SH>(p, a, s);
+    if constexpr ((CAP || W) && SH::NOV > 0) {  // overflow: uncapped, unweighted rows
+      return pick_shape<DT, W, CAP, I + 1>(p, a, s);
+    } else {
+      if (a.nvec <= SH::CAPACITY) return launch_shape<DT, W, CAP, SH>(p, a, s);
+    }
     return pick_shape<DT, W, CAP, I + 1>(p, a, s);
   }
 }
