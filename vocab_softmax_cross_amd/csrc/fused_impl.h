@@ -64,6 +64,7 @@ void fused_resident_kernel(const RowArgs a) {
   __shared__ float red_max[NW];
   __shared__ float4 red_sum[NW];
   __shared__ float xy_sh;  // the stored target logit, posted by its owner lane
+  __shared__ float4 red_sum3[WEIGHTED ? NW : 1];  // pass 3's weighted logit sum
   // Each wavefront's overflow state (NOV > 0): maximum, sum below it, logit
   // sum, count at it, first index of it.
   constexpr int NWO = NOV > 0 ? NW : 1;
@@ -289,8 +290,7 @@ void fused_resident_kernel(const RowArgs a) {
         } else {
           rs.s += ex;
         }
-        if constexpr (WEIGHTED) rs.S = __builtin_fmaf(a.weight[j * VEC + i], fc, rs.S);
-        else rs.S += fc;
+        if constexpr (!WEIGHTED) rs.S += fc;  // weighted: summed in pass 3
       }
     }
   };
@@ -335,9 +335,17 @@ void fused_resident_kernel(const RowArgs a) {
   const float sum_w = uniform(static_cast<float>(a.ws->sum_w));
   const float wy = uniform(WEIGHTED ? a.weight[y] : 1.0f);
   const float lg = uniform(log1pf(dp));  // lse - m, once per row
+  // The row's outputs.  With class weights the logit sum S = sum w x is
+  // taken in pass 3, which loads every weight anyway (the weights are read
+  // once per row instead of twice): the loss is first written without its
+  // -eta S term, which pass 3's end subtracts.
+  float l0 = 0.0f;
+  if constexpr (WEIGHTED) {
+    l0 = uniform(row_loss(Mc, lg, xy, 0.0f, wy, sum_w, a.eps, a.eta) + row_z(Mc, lg, a.zl));
+  }
   if (tid == 0) {
     const float zrow = row_z(Mc, lg, a.zl);
-    store_row(a, n, row_loss(Mc, lg, xy, rs.S, wy, sum_w, a.eps, a.eta) + zrow,
+    store_row(a, n, WEIGHTED ? l0 : row_loss(Mc, lg, xy, rs.S, wy, sum_w, a.eps, a.eta) + zrow,
               (static_cast<int64_t>(rs.first) == y) ? 1.0f : 0.0f, zrow);
   }
 
@@ -353,6 +361,7 @@ void fused_resident_kernel(const RowArgs a) {
   t.K = uniform(t.K);
   t.B = uniform(t.B);
   t.dxy = uniform(t.dxy);
+  float Sw = 0.0f;  // this thread's share of sum w x (class weights)
   auto grad_vec = [&](const uint4 v, int k) {
     const int j = k * NT + tid;
     auto w = words(v);
@@ -362,12 +371,15 @@ void fused_resident_kernel(const RowArgs a) {
       D::word_fresh(w.w[q], f);
 #pragma unroll
       for (int e = 0; e < EPW; ++e) {
-        const float b = WEIGHTED ? t.B * a.weight[j * VEC + q * EPW + e] : t.B;
+        const float wc = WEIGHTED ? a.weight[j * VEC + q * EPW + e] : 1.0f;
+        const float b = WEIGHTED ? t.B * wc : t.B;
         if constexpr (CAP) {
           float slope;
           const float fc = cap.value(f[e], slope);
+          if constexpr (WEIGHTED) Sw = __builtin_fmaf(wc, fc, Sw);
           f[e] = __builtin_fmaf(exp_shifted(fc, t.ML), t.K, -b) * slope;
         } else {
+          if constexpr (WEIGHTED) Sw = __builtin_fmaf(wc, f[e], Sw);
           f[e] = __builtin_fmaf(exp_shifted(f[e], t.ML), t.K, -b);
         }
       }
@@ -392,15 +404,22 @@ void fused_resident_kernel(const RowArgs a) {
     buf_store16(rsrc, voff, static_cast<uint32_t>(k) * SLOT_BYTES,
                 make_uint4(w.w[0], w.w[1], w.w[2], w.w[3]));
   };
-  // The overflow is read again once the registers of slots 0 .. NOV-1 are
-  // free, ahead of the stores of the later slots (so its wait does not cover
-  // them), and its gradient is written last.
   static_for<NREG>([&](auto k) {
     if (in_row(k)) grad_vec(r[k], k);
   });
   static_for<NLDS>([&](auto k) {
     if (in_row(NREG + k)) grad_vec(xl[k * NT + tid], NREG + k);
   });
+  if constexpr (WEIGHTED) {  // summed in the order pass 2 sums the unweighted S
+    const RowSums sw = block_sums<NT>(RowSums{0.0f, Sw, 0, 0x7fffffff}, red_sum3);
+    if (tid == 0 && a.eps > 0.0f) {
+      const float l = l0 - a.eta * sw.S;
+      a.loss_rows[n] = l;
+      if (a.loss_rows2) a.loss_rows2[n] = l;
+    }
+  }
+  // The overflow (unweighted rows only) is read again after the on-chip
+  // row's stores, and its gradient is written last.
   if constexpr (NOV > 0) {
     const int t3 = fresh_tid();
     const uint32_t vo3 = static_cast<uint32_t>(ONCHIP + t3) * 16u;
