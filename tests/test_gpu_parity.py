@@ -789,11 +789,11 @@ def test_graph_capture_replays_match_eager():
 ONCHIP_VECTORS = 16320
 
 
-def _overflow_case(V, dtype, label_smoothing=0.1):
+def _overflow_case(V, dtype, label_smoothing=0.1, base="llm_head"):
     """Rows engineered around the overflow: the target in it, a dominant
     target in it (confident row), maxima tied between the chip and the
     overflow and within the overflow, and an ignored row."""
-    wl = _small("llm_head", 12, V, dtype=dtype, ignore_frac=0.0, label_smoothing=label_smoothing)
+    wl = _small(base, 12, V, dtype=dtype, ignore_frac=0.0, label_smoothing=label_smoothing)
     tgt = W.targets(wl)
     xh = W.logits(wl, tgt)
     vec = 4 if dtype == "f32" else 8
@@ -827,6 +827,18 @@ def test_overflow_rows(V, dtype, reduction, go):
     check(wl, out, reference(wl, xh, tgt, w, reduction, go), xh, tgt, w)
     assert out["acc"][3] == 1.0 and out["acc"][4] == 0.0 and out["acc"][5] == 0.0
     assert out["acc"][6] == 1.0
+
+
+@pytest.mark.parametrize("V", [131072, 151936, 179712])
+@pytest.mark.parametrize("reduction,go", [("sum", 0.5), ("none", 0.5)])
+def test_overflow_rows_weighted(V, reduction, go):
+    """Class weights on the rows the overflow shapes serve unweighted (these
+    take one row per CU): the weighted logit sum taken in the gradient pass,
+    with the same engineered targets and maxima."""
+    wl, xh, tgt = _overflow_case(V, "bf16", base="weighted")
+    assert W.class_weights(wl) is not None
+    out, xh, tgt, w = run(wl, "fused", reduction, go, accuracy=True, x_host=xh, tgt=tgt)
+    check(wl, out, reference(wl, xh, tgt, w, reduction, go), xh, tgt, w)
 
 
 def test_overflow_rows_confident_without_smoothing():
