@@ -84,9 +84,11 @@ void fused_resident_kernel(const RowArgs a) {
   // Lanes past the end of the row get a per-lane offset beyond num_records,
   // so the buffer range check drops them whether or not it counts soffset.
   auto lane_off = [&](int k) { return in_row(k) ? voff : kOutOfRange; };
-  // Overflow vector k of thread t, addressed by its per-lane offset alone.
-  // Callers pass a fresh_tid() of their own, so that the offsets are
-  // computed where they are used instead of held in registers in between.
+  // Overflow vector k of thread t.  A valid row's overflow loads and stores
+  // are exec-masked, with one per-lane offset and slot k in soffset; ov_off
+  // (each lane's own offset, past num_records beyond the row) serves the
+  // stores of an ignored row.  Callers pass a fresh_tid() of their own, so
+  // that these are computed where used instead of held in registers.
   auto ov_col = [&](int k, int t) { return ONCHIP + k * NT + t; };
   auto ov_off = [&](int k, int t) {
     return ov_col(k, t) < nvec ? static_cast<uint32_t>(ov_col(k, t)) * 16u : kOutOfRange;
