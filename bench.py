@@ -302,8 +302,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(rows shard across GPUs with no exchange; see DESIGN.md). Use --gpus 1.",
+        print("bench.py measures one GPU: the library has no multi-GPU path (rows shard "
+              "across GPUs with no exchange, one process per GPU). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -45,7 +45,7 @@
  *    `stream` (NULL = the null stream) and the call returns at once.
  *  - Return codes: VSCE_OK (work enqueued), VSCE_ERR_INVALID (an argument is
  *    out of its documented domain; nothing was enqueued),
- *    VSCE_ERR_UNSUPPORTED (a valid combination this build does not handle;
+ *    VSCE_ERR_UNSUPPORTED (a valid combination the library does not handle;
  *    nothing enqueued), VSCE_ERR_LAUNCH (a kernel launch failed).
  *  - Data-dependent errors (a target neither equal to ignore_index nor in
  *    [0, vocab)) are not return codes: the row gets a NaN loss and a zero
