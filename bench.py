@@ -214,6 +214,65 @@ def long_rows_mode(L, W, hip, dev, stream, K):
     return res
 
 
+def workload_modes(L, W, hip, dev, stream, K):
+    """The fused row kernel on the other workloads' full sizes: the
+    confidence workload (4096 x 32000 bf16, targets at p = 0.9 / 0.99 / 0.999)
+    and the weighted one (16384 x 151936 bf16, class weights, smoothing 0.1,
+    5% ignored rows, sum).  Each launch on a fresh copy of the logits, timed
+    by events on the launch stream around the row kernel (as the headline's
+    roofline), its algorithmic bytes: a read of every valid row, a write of
+    every row, 12 bytes per row."""
+    import numpy as np
+    import torch
+    res = {}
+    for name in ("confidence", "weighted"):
+        wl = W.WORKLOADS[name]
+        tgt = W.targets(wl)
+        w = W.class_weights(wl)
+        pristine = W.logits_device(wl, dev, tgt)
+        n_buf = 4
+        bufs = [torch.empty_like(pristine) for _ in range(n_buf)]
+        t = torch.from_numpy(tgt).to(dev)
+        wt = None if w is None else torch.from_numpy(w).to(dev)
+        ws = torch.empty(L.vsce_workspace_bytes(wl.BT), dtype=torch.uint8, device=dev)
+        red = wl.reductions[0]
+        loss = torch.empty(wl.BT if red == "none" else 1, dtype=torch.float32, device=dev)
+        outs = L.Outputs()
+        outs.loss = loss.data_ptr()
+        p = L.Problem()
+        p.rows, p.vocab, p.row_stride = wl.BT, wl.V, wl.V
+        p.dtype, p.reduction = L.BF16, L.REDUCTIONS[red]
+        p.target, p.class_weight = t.data_ptr(), (None if wt is None else wt.data_ptr())
+        p.ignore_index, p.label_smoothing, p.flags = -100, wl.label_smoothing, 0
+        p.softcap, p.z_loss = 0.0, 0.0
+        n_valid = int(np.sum((tgt >= 0) & (tgt < wl.V)))
+        row = wl.V * wl.elem_bytes
+        alg = n_valid * row + wl.BT * row + 12 * wl.BT
+        ms = []
+        for r0 in range(0, K, n_buf):
+            for b in bufs:
+                b.copy_(pristine)
+            torch.cuda.synchronize()
+            evs = [(hip.event(), hip.event()) for _ in range(min(n_buf, K - r0))]
+            for b, (e0, e1) in zip(bufs, evs):
+                L.ce_forward_fused_inplace_timed(p, b.data_ptr(), outs, ws.data_ptr(), stream,
+                                                 e0, e1)
+            torch.cuda.synchronize()
+            ms += [hip.elapsed_ms(a, b) for a, b in evs]
+            for a, b in evs:
+                hip.destroy(a)
+                hip.destroy(b)
+        m = float(np.median(ms))
+        res[name] = {"shape": [wl.BT, wl.V], "logits": wl.dtype, "weighted": w is not None,
+                     "label_smoothing": wl.label_smoothing, "reduction": red,
+                     "kernel_ms": round(m, 4), "rows_per_s": round(wl.BT / m * 1e3, 1),
+                     "alg_bytes_per_launch": alg, "alg_GBps": round(alg / m / 1e6, 1),
+                     "frac_of_hbm_peak": round(alg / m / 1e6 / HBM_PEAK_GBPS, 4)}
+        del bufs, pristine
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline_flce(sample):
     """The FLCE oracle (fp64: z = h W^T, the cross-entropy, G W and G^T h)
     on the first rows of the FLCE mode's own inputs; rows per second."""
@@ -491,6 +550,7 @@ def main():
             "backward_GBps": round((n_valid + wl.BT) * shard_row / t_bwd / 1e6, 1),
             "rank_kernels_ms": round(t_stats + t_merge + t_bwd, 4)}
         extra["fused_long_rows"] = long_rows_mode(L, W, hip, dev, stream, K)
+        extra["fused_other_workloads"] = workload_modes(L, W, hip, dev, stream, K)
         extra["flce"], flce_sample = flce_mode(L, W, hip, dev, stream, K,
                                                0 if args.no_cpu_baseline else 64)
         extra[f"fused_softcap{CAP:g}_zloss{ZL:g}"] = {
