@@ -863,3 +863,13 @@ def test_overflow_nan_propagates():
     loss = res["loss"].cpu()
     assert math.isnan(loss[2]) and torch.isfinite(loss[[0, 1, 3]]).all()
     assert torch.isnan(x[2]).all() and torch.isfinite(x[[0, 1, 3]]).all()
+
+
+@pytest.mark.parametrize("V", [131072, 179712])
+def test_overflow_rows_padded_stride(V):
+    """The overflow of rows that live in wider buffers: the padding columns
+    past V stay untouched (the overflow's accesses stop at the row's end)."""
+    wl, xh, tgt = _overflow_case(V, "bf16")
+    out, xh, tgt, w = run(wl, "fused", "mean", 1.0, accuracy=True, x_host=xh, tgt=tgt,
+                          row_stride=V + 1024)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0), xh, tgt, w)
