@@ -464,7 +464,10 @@ struct Shape {
 
 using Shapes = std::tuple<Shape<64, 4, 0, 4>,       // rows up to 256 vectors
                           Shape<256, 8, 0, 4>,      // 2048 vectors
-                          Shape<256, 16, 0, 4>,     // 4096 vectors
+                          // 4096 vectors (bf16 V <= 32768): 512 threads at 8
+                          // waves per SIMD, 1-3% ahead of 256 threads x 16
+                          // vectors at V = 32000
+                          Shape<512, 8, 0, 8>,
                           Shape<512, 16, 0, 4>,     // 8192 vectors
                           // 16320 vectors (bf16 V <= 130560): 2 workgroups per CU,
                           // 64 VGPRs and 79 KB of LDS each
