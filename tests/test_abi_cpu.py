@@ -316,3 +316,51 @@ def test_gemm_layout_argument_checks(kw):
 def test_gemm_empty_is_a_no_op():
     assert _gemm(M=0) == L.OK
     assert _gemm(N=0) == L.OK
+
+
+# ---------------------------------------------------------------- which HIP runtime the library binds
+# PyTorch ships its own HIP and HSA runtimes with the same sonames as the
+# system ROCm's; the library must bind to the copy torch uses.  Each case runs
+# in a fresh interpreter, because a process keeps whatever it has loaded.
+
+_MAPS = r"""
+import sys
+def runtimes():
+    found = set()
+    for line in open("/proc/self/maps"):
+        p = line.split()[-1]
+        if "libamdhip64" in p or "libhsa-runtime64" in p:
+            found.add(p)
+    return sorted(found)
+"""
+
+
+def _run(code):
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, "-c", _MAPS + code], cwd=ROOT, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    return [l for l in r.stdout.splitlines() if l.startswith("/")]
+
+
+def test_load_binds_the_library_to_torchs_runtime():
+    """_lib.load() alone, in a fresh process: one HIP runtime and one HSA
+    runtime are mapped, both torch's."""
+    maps = _run("import vocab_softmax_cross_amd._lib as L\nL.load()\n"
+                "import torch\nprint('\\n'.join(runtimes()))")
+    hip = [p for p in maps if "libamdhip64" in p]
+    hsa = [p for p in maps if "libhsa-runtime64" in p]
+    assert len(hip) == 1 and len(hsa) == 1, maps
+    assert "torch" in hip[0] and "torch" in hsa[0], maps
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="hosts without a GPU only: the order "
+                    "shown here puts two HIP runtimes over one device")
+def test_loading_the_library_before_torch_maps_two_runtimes():
+    """The order load() rules out: the library opened with a bare dlopen before
+    torch is imported maps the system ROCm runtime, and torch then maps its
+    own as well (no HIP call is made; nothing touches a device)."""
+    maps = _run(f"import ctypes\nctypes.CDLL({L.LIB_PATH!r})\n"
+                "import torch\nprint('\\n'.join(runtimes()))")
+    assert len([p for p in maps if "libamdhip64" in p]) == 2, maps

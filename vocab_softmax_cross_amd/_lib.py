@@ -91,14 +91,34 @@ class VsceError(RuntimeError):
 _lib = None
 
 
+def _bind_torch_runtime() -> None:
+    """Loads PyTorch's HIP runtime before libvsce.so, and initialises it
+    when a GPU is present.
+
+    libvsce.so asks the dynamic loader for ``libamdhip64.so.7``; PyTorch's
+    libraries ask for ``libamdhip64.so`` and ship their own copy, whose soname
+    is also ``libamdhip64.so.7``.  Loaded after torch, the library's request is
+    met by torch's copy (the loader matches it by soname), so one HIP runtime
+    serves both.  Loaded before torch, the request pulls in the system ROCm
+    runtime, torch's request for the unversioned name then loads its own copy
+    as well, and the process holds two HIP runtimes and two HSA runtimes over
+    the same device (tests/test_abi_cpu.py shows both orders on the host).
+    So the binding always brings torch's runtime in first."""
+    import torch
+    if torch.cuda.is_available():
+        torch.cuda.init()
+
+
 def load() -> ctypes.CDLL:
     """Load libvsce.so from the package directory (build it with
-    ``python -m vocab_softmax_cross_amd.build``)."""
+    ``python -m vocab_softmax_cross_amd.build``), after PyTorch's HIP
+    runtime."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m vocab_softmax_cross_amd.build`")
+    _bind_torch_runtime()
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     lib.vsce_workspace_bytes.argtypes = [c_int64]
