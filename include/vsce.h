@@ -52,8 +52,10 @@
  *    gradient, is left out of W and of the valid count, and bit
  *    VSCE_STATUS_BAD_TARGET is set in the workspace status word, which the
  *    caller may read whenever it chooses.
- *  - Calls are reentrant; the library keeps no mutable global state.  Two
- *    calls that share a workspace must be ordered on one stream.
+ *  - Calls are reentrant.  Two calls that share a workspace must be ordered
+ *    on one stream.  The library's only mutable state is the static workspace
+ *    of ce_forward_fused_inplace_noalloc (one per device) and the launch
+ *    shapes of the GEMM, computed once per device and kept.
  */
 #ifndef VSCE_H
 #define VSCE_H
@@ -81,7 +83,9 @@ enum {
   VSCE_OK = 0,
   VSCE_ERR_INVALID = -1,
   VSCE_ERR_UNSUPPORTED = -2,
-  VSCE_ERR_LAUNCH = -3
+  VSCE_ERR_LAUNCH = -3,
+  VSCE_ERR_TOO_LARGE = -4 /* ce_forward_fused_inplace_noalloc: more rows than
+                             its static workspace holds; nothing enqueued */
 };
 
 /* Bits of the workspace status word. */
@@ -232,6 +236,30 @@ int ce_forward_fused_inplace(const vsce_problem *problem, void *logits_inout,
 int ce_forward_fused_inplace_timed(const vsce_problem *problem, void *logits_inout,
                                    const vsce_outputs *out, void *workspace,
                                    hipStream_t stream, hipEvent_t begin, hipEvent_t end);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * work as ce_forward_fused_inplace, with the workspace taken from a static
+ * array inside the library instead of a caller's buffer.  Nothing is
+ * allocated: the array (vsce_workspace_bytes(VSCE_NOALLOC_MAX_ROWS) bytes,
+ * about 1.8 MB) is part of the library's device code and each device the
+ * library runs on holds its own copy until the process ends.  The first call
+ * on a device looks up that device's copy (hipGetSymbolAddress, with the
+ * device current) and keeps its address.
+ *  - rows > VSCE_NOALLOC_MAX_ROWS: returns VSCE_ERR_TOO_LARGE, nothing
+ *    enqueued.  Other arguments as ce_forward_fused_inplace.
+ *  - Every call on one device shares that device's array, and each forward
+ *    rewrites what it reads (the header and the per-row scratch need no
+ *    clearing).  Calls that overlap on one device race: order them on one
+ *    stream.
+ *  - The header (normalizers, status word) stays inside the library: a bad
+ *    target still shows as a NaN row loss and a NaN reduced loss.  The
+ *    gradient needs nothing more: apply grad_output with ce_scale_grad.
+ */
+#define VSCE_NOALLOC_MAX_ROWS 65536
+int ce_forward_fused_inplace_noalloc(const vsce_problem *problem, void *logits_inout,
+                                     const vsce_outputs *out, hipStream_t stream);
 
 /*
  * Split forward (TransformerEngine PR #2325 online_softmax_kernel +

@@ -53,7 +53,7 @@ def test_header_constants_match_the_binding():
                                     flags=re.M)}
     for name in ("WS_W", "WS_SUM_W", "WS_N_VALID", "WS_N_INVALID", "WS_STATUS", "WS_INV_W",
                  "WS_INV_N_VALID", "WS_HEADER_BYTES", "STATS_STRIDE", "PARTIAL_STRIDE",
-                 "FLAG_LONG_ROWS_RING"):
+                 "FLAG_LONG_ROWS_RING", "NOALLOC_MAX_ROWS"):
         assert defines[name] == getattr(L, name), name
 
 
@@ -364,3 +364,23 @@ def test_loading_the_library_before_torch_maps_two_runtimes():
     maps = _run(f"import ctypes\nctypes.CDLL({L.LIB_PATH!r})\n"
                 "import torch\nprint('\\n'.join(runtimes()))")
     assert len([p for p in maps if "libamdhip64" in p]) == 2, maps
+
+
+def test_noalloc_rejects_more_rows_than_its_static_workspace():
+    """The check happens before any HIP call (no GPU needed)."""
+    lib = L.load()
+    p = L.Problem()
+    p.rows, p.vocab, p.row_stride, p.dtype, p.reduction = L.NOALLOC_MAX_ROWS + 1, 1024, 1024, \
+        L.BF16, L.REDUCTION_MEAN
+    p.target, p.ignore_index = FAKE, -100
+    out = L.Outputs()
+    out.loss = FAKE
+    assert L.raw_call("ce_forward_fused_inplace_noalloc", ctypes.byref(p), FAKE,
+                      ctypes.byref(out), None) == L.ERR_TOO_LARGE
+    assert lib.vsce_strerror(L.ERR_TOO_LARGE) == b"more rows than the static workspace holds"
+    # argument errors still come first
+    p.vocab = 0
+    assert L.raw_call("ce_forward_fused_inplace_noalloc", ctypes.byref(p), FAKE,
+                      ctypes.byref(out), None) == L.ERR_INVALID
+    # the static array holds the workspace of the largest accepted problem
+    assert L.vsce_workspace_bytes(L.NOALLOC_MAX_ROWS) < 2 << 20

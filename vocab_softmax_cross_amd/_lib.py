@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(PKG, "libvsce.so")
 F32, BF16, F16 = 0, 1, 2
 REDUCTION_NONE, REDUCTION_MEAN, REDUCTION_SUM = 0, 1, 2
 REDUCTIONS = {"none": REDUCTION_NONE, "mean": REDUCTION_MEAN, "sum": REDUCTION_SUM}
-OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_LAUNCH = 0, -1, -2, -3
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_TOO_LARGE = 0, -1, -2, -3, -4
+NOALLOC_MAX_ROWS = 65536
 STATUS_BAD_TARGET = 1
 STATS_STRIDE = 4
 PARTIAL_STRIDE = 8
@@ -27,6 +28,7 @@ WS_W, WS_SUM_W, WS_N_VALID, WS_N_INVALID, WS_STATUS, WS_HEADER_BYTES = 0, 8, 16,
 WS_INV_W, WS_INV_N_VALID = 40, 44
 
 EXPORTS = ("vsce_workspace_bytes", "ce_forward_fused_inplace", "ce_forward_fused_inplace_timed",
+           "ce_forward_fused_inplace_noalloc",
            "ce_forward_stats", "ce_forward_stats_partial", "ce_merge_stats",
            "ce_backward_from_stats", "ce_scale_grad", "vsce_gemm_bf16_nt", "vsce_gemm_bf16",
            "vsce_flce_workspace_bytes", "flce_forward_backward", "vsce_strerror", "vsce_version")
@@ -128,6 +130,8 @@ def load() -> ctypes.CDLL:
     lib.ce_forward_fused_inplace_timed.argtypes = [P(Problem), c_void_p, P(Outputs), c_void_p,
                                                    c_void_p, c_void_p, c_void_p]
     lib.ce_forward_fused_inplace_timed.restype = ctypes.c_int
+    lib.ce_forward_fused_inplace_noalloc.argtypes = [P(Problem), c_void_p, P(Outputs), c_void_p]
+    lib.ce_forward_fused_inplace_noalloc.restype = ctypes.c_int
     lib.ce_forward_stats.argtypes = [P(Problem), c_void_p, c_void_p, P(Outputs), c_void_p, c_void_p]
     lib.ce_forward_stats.restype = ctypes.c_int
     lib.ce_forward_stats_partial.argtypes = [P(Problem), c_void_p, c_void_p, c_void_p]
@@ -185,6 +189,12 @@ def ce_forward_fused_inplace_timed(problem: Problem, logits_inout: int, outputs:
                                    workspace: int, stream: int, begin: int, end: int) -> int:
     return _check("ce_forward_fused_inplace_timed", load().ce_forward_fused_inplace_timed(
         ctypes.byref(problem), logits_inout, ctypes.byref(outputs), workspace, stream, begin, end))
+
+
+def ce_forward_fused_inplace_noalloc(problem: Problem, logits_inout: int, outputs: Outputs,
+                                     stream: int) -> int:
+    return _check("ce_forward_fused_inplace_noalloc", load().ce_forward_fused_inplace_noalloc(
+        ctypes.byref(problem), logits_inout, ctypes.byref(outputs), stream))
 
 
 def ce_forward_stats(problem: Problem, logits: int, stats: int, outputs: Outputs,

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 #include "vsce.h"
@@ -232,6 +234,40 @@ int launch_scale(const Prob& p, RowArgs a, hipStream_t s) {
   return stream_any(kStreamScale, p, a, s);
 }
 
+// ---------------------------------------------------------------- static workspace
+// The workspace of ce_forward_fused_inplace_noalloc: one array per device, in
+// the library's device code object, sized for kStaticMaxRows rows.  In host
+// code `scratch` names a host-side stand-in, not device memory: host code
+// only ever uses the device address hipGetSymbolAddress gives for it, looked
+// up once per device (with that device current) and kept.
+namespace {
+
+constexpr int64_t kStaticMaxRows = VSCE_NOALLOC_MAX_ROWS;
+constexpr int64_t kStaticBytes =
+    VSCE_WS_HEADER_BYTES + 3 * ((4 * kStaticMaxRows + kAlign - 1) / kAlign * kAlign) +
+    (16 * kStaticMaxRows + kAlign - 1) / kAlign * kAlign;
+
+__device__ __align__(256) unsigned char scratch[kStaticBytes];
+
+constexpr int kMaxDevices = 64;
+
+// This device's copy of `scratch`, or null if the lookup fails.
+void* static_scratch() {
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
+
+}  // namespace
+
 }  // namespace vsce
 
 using namespace vsce;
@@ -266,6 +302,22 @@ int ce_forward_fused_inplace_timed(const vsce_problem* problem, void* logits_ino
   if (rc != VSCE_OK) return rc;
   return forward_common(p, row_args(p, logits_inout, out, workspace), out, workspace, true,
                         stream, begin, end);
+}
+
+int ce_forward_fused_inplace_noalloc(const vsce_problem* problem, void* logits_inout,
+                                     const vsce_outputs* out, hipStream_t stream) {
+  static_assert(kStaticBytes >= VSCE_WS_HEADER_BYTES, "static workspace");
+  Prob p;
+  int rc = check_problem(problem, logits_inout, p);
+  if (rc == VSCE_OK && !whole_rows(p)) rc = VSCE_ERR_INVALID;
+  if (rc == VSCE_OK) rc = check_outputs(out);
+  if (rc != VSCE_OK) return rc;
+  if (p.rows > kStaticMaxRows) return VSCE_ERR_TOO_LARGE;
+  // The layout of a workspace of vsce_workspace_bytes(rows) bytes, inside
+  // the array sized for kStaticMaxRows (every offset grows with rows).
+  void* ws = static_scratch();
+  if (ws == nullptr) return VSCE_ERR_LAUNCH;
+  return forward_common(p, row_args(p, logits_inout, out, ws), out, ws, true, stream);
 }
 
 int ce_forward_stats(const vsce_problem* problem, const void* logits, float* stats,
@@ -375,6 +427,7 @@ const char* vsce_strerror(int code) {
     case VSCE_ERR_INVALID: return "invalid argument";
     case VSCE_ERR_UNSUPPORTED: return "unsupported combination";
     case VSCE_ERR_LAUNCH: return "kernel launch failed";
+    case VSCE_ERR_TOO_LARGE: return "more rows than the static workspace holds";
     default: return "unknown error";
   }
 }
