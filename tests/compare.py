@@ -5,17 +5,20 @@ the buffer type of the oracle's exact value rounded once to that type
 (``strict``), or, where the gradient is a difference of nearly equal terms
 (label smoothing, fp32 buffers), within the error of evaluating that
 difference in fp32 (``floor``):
-    |g - g64| <= 2^-24 (|xt_c - lse| + log2 V + 8 + 8 s + 4 |x_c| / s) k_c
+    |g - g64| <= 2^-24 (|xt_c - lse| + log2 V + 8 + C_c) k_c
                  (p_c |sigma A + Z| + sigma eta |w_c| + sigma (1 - eps) w_y [c == y])
-with xt the (soft-capped) logits, s the cap (0 without; then the s terms
-drop), k_c the cap's slope 1 - tanh^2(x_c / s) (1 without), and
-Z = sigma_z 2 lambda lse the z-loss coefficient (0 without).  The 8 s term is
-the fp32 capped value's absolute error (a few units of 2^-24 s from exp,
-reciprocal and products), which enters exp(xt - m) through both xt_c and the
-capped maximum.  The 4 |x_c| / s term is the conditioning of the slope
-4 q / (1 + q)^2, q = exp(-2 |x_c| / s): the fp32 exponent argument carries a
-relative error of about 2^-23, so q (and the slope) carries one of about
-2 |x_c| / s * 2^-23 -- measured at up to 0.91 of this term on a fine grid.
+with xt the (soft-capped) logits, k_c the cap's slope 1 - tanh^2(x_c / s)
+(1 without a cap), Z = sigma_z 2 lambda lse the z-loss coefficient (0
+without), and C_c = 0 without a cap, else
+    C_c = |xt_c| + |mt| + 4 |x_c| / s        (mt = the capped row maximum):
+ - |xt_c| + |mt|: every exponent takes the difference of two capped logits,
+   each an fp32 value computed from x; its rounding alone is up to
+   2^-24 |xt| (half an ulp), in any fp32 evaluation (stored logits, uncapped,
+   are exact and need no such term);
+ - 4 |x_c| / s: the conditioning of the slope 4 q / (1 + q)^2,
+   q = exp(-2 |x_c| / s), where the cap saturates: an fp32 exponent argument
+   carries a relative error of about 2^-23, so q (and the slope) carries one
+   of about 2 |x_c| / s * 2^-23.
 The strict fraction must be 1 for bf16/fp16 buffers without label smoothing;
 the floored fraction must be 1 everywhere.
 """
@@ -83,7 +86,7 @@ def grad_report(g: np.ndarray, g64: np.ndarray, dtype: str, x: np.ndarray, targe
         if softcap > 0:
             xt = softcap * np.tanh(x[r] / softcap)
             slope = 1.0 / np.cosh(x[r] / softcap) ** 2
-            cap_terms = 8 * softcap + 4 * np.abs(x[r]) / softcap
+            cap_terms = np.abs(xt) + abs(m) + 4 * np.abs(x[r]) / softcap
         else:
             xt, slope, cap_terms = x[r], 1.0, 0.0
         p = np.exp(xt - lse)
@@ -102,6 +105,12 @@ def grad_report(g: np.ndarray, g64: np.ndarray, dtype: str, x: np.ndarray, targe
     units = np.where(both_nan, 0.0, units)
     return GradReport(int(g.size), int((~strict).sum()), int((~floor_ok).sum()),
                       float(np.nanmax(units)) if units.size else 0.0)
+
+
+# Relative error allowed in a capped logit the library reports (the maximum
+# and target logit of the split statistics and shard records), in units of
+# 2^-24: s tanh(x / s) evaluated in fp32 to a few units relative.
+CAPPED_VALUE_UNITS = 8
 
 
 def rel_err(a, b) -> np.ndarray:

@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.compare import assert_loss_close, grad_report, rel_err
+from tests.compare import CAPPED_VALUE_UNITS, assert_loss_close, grad_report, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -156,9 +156,10 @@ def check(wl, out, ref, x_host, tgt, w, strict_bf16=None):
     if out["stats"] is not None:
         valid = ref["cls"] == 0
         s, r = out["stats"][valid], ref["stats"][valid]
-        if cap > 0:  # capped values: the fp32 cap is good to a few units of 2^-24 s
+        if cap > 0:  # capped values: the fp32 cap is good to a few units of 2^-24, relative
             for k in (0, 2):
-                assert np.all(np.abs(s[:, k] - r[:, k]) <= 2.0 ** -24 * (8 * cap + np.abs(r[:, k])))
+                assert np.all(np.abs(s[:, k] - r[:, k])
+                              <= CAPPED_VALUE_UNITS * 2.0 ** -24 * np.abs(r[:, k])), k
         else:
             np.testing.assert_array_equal(s[:, 0], r[:, 0])
             np.testing.assert_array_equal(s[:, 2], r[:, 2])
@@ -166,9 +167,10 @@ def check(wl, out, ref, x_host, tgt, w, strict_bf16=None):
         if wl.label_smoothing > 0:
             xa = np.abs(W.as_f64(x_host[torch.from_numpy(np.where(valid)[0])]))
             if cap > 0:
-                xa = np.abs(cap * np.tanh(xa / cap)) + 8 * cap
+                xa = np.abs(cap * np.tanh(xa / cap))
             wa = np.ones(wl.V) if w is None else np.abs(w.astype(np.float64))
-            bound = 64 * 2.0 ** -24 * (xa @ wa)
+            # fp32 summation, plus each capped term's own relative error
+            bound = (64 + (CAPPED_VALUE_UNITS if cap > 0 else 0)) * 2.0 ** -24 * (xa @ wa)
             assert np.all(np.abs(s[:, 3] - r[:, 3]) <= bound)
         else:
             assert np.all(s[:, 3] == 0.0)
@@ -337,6 +339,58 @@ def test_softcap_z_loss_llm_head_full_size():
     check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0, rows, **kw), xh, tgt, w)
 
 
+@pytest.mark.parametrize("V,softcap,z_loss", [(128256, 30.0, 0.0), (128256, 3.0, 1e-4),
+                                              (32000, 30.0, 1e-4), (32000, 3.0, 0.0)])
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_softcap_strict_bf16_without_smoothing(V, softcap, z_loss, mode):
+    """bf16 rows without label smoothing, soft-capped: every gradient element
+    within 1 ulp of the exact value rounded once (the strict bar, no floor).
+    A cap of 3 puts most logits (sigma 2) outside the polynomial's range, so
+    both forms of the cap are exercised."""
+    wl = _small("llm_head", 48, V, label_smoothing=0.0)
+    kw = dict(softcap=softcap, z_loss=z_loss)
+    out, xh, tgt, w = run(wl, mode, "mean", 1.0, accuracy=True, **kw)
+    check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0, **kw), xh, tgt, w, strict_bf16=True)
+
+
+@pytest.mark.parametrize("softcap", [1.0, 7.0, 30.0, 1000.0])
+def test_softcap_value_on_a_grid(softcap):
+    """The capped logit s tanh(x / s) the library computes, read back through
+    the split statistics (x[y] of each row is one grid point, 8192 points over
+    |x| <= 12 s): within a few units of 2^-24 relative, on both sides of the
+    polynomial's range."""
+    dev = _dev()
+    BT, V = 8192, 64
+    xs = np.linspace(-12 * softcap, 12 * softcap, BT).astype(np.float32)
+    x = torch.zeros((BT, V), dtype=torch.float32)
+    x[:, 0] = torch.from_numpy(xs)
+    t = torch.zeros(BT, dtype=torch.int64)
+    res = vf.forward_stats(x.to(dev), t.to(dev), softcap=softcap, reduction="none")
+    st = res["stats"].cpu().numpy().astype(np.float64)
+    exact = softcap * np.tanh(xs.astype(np.float64) / softcap)
+    units = np.abs(st[:, 2] - exact) / np.maximum(np.abs(exact), 1e-30) / 2.0 ** -24
+    central = np.abs(xs) <= 0.55 * softcap
+    print(f"  capped value: central max {units[central].max():.2f}, outside max "
+          f"{units[~central].max():.2f} units of 2^-24", flush=True)
+    assert units[central].max() <= 4 and units[~central].max() <= CAPPED_VALUE_UNITS
+
+
+@pytest.mark.parametrize("variant", ["weights", "softcap_z_loss"])
+def test_short_rows_weighted_or_capped(variant):
+    """The 512-thread shape that serves rows of 2049-4096 vectors (bf16
+    V = 32000) with class weights and with a soft-cap plus z-loss, and an fp32
+    row of the same shape (V = 16000) with class weights."""
+    kw = dict(softcap=30.0, z_loss=1e-4) if variant == "softcap_z_loss" else {}
+    base = "weighted" if variant == "weights" else "llm_head"
+    for dtype, V in (("bf16", 32000), ("f32", 16000)):
+        if variant != "weights" and dtype == "f32":
+            continue
+        wl = _small(base, 40, V, dtype=dtype, ignore_frac=0.1, label_smoothing=0.1)
+        red = "sum" if variant == "weights" else "mean"
+        out, xh, tgt, w = run(wl, "fused", red, 0.5, accuracy=True, **kw)
+        check(wl, out, reference(wl, xh, tgt, w, red, 0.5, **kw), xh, tgt, w)
+
+
 # ---------------------------------------------------------------- vocab-parallel shards
 # TransformerEngine PR #2325 (dist_process_group): each rank holds a slice of
 # the vocabulary, the per-row record (max, sum, target logit, scaled_x_sum) is
@@ -390,7 +444,7 @@ def check_parts(wl, out, x_host, tgt, w, edges, softcap):
         first = out["parts"][s_][:, 5].view(np.int32)
         np.testing.assert_array_equal(first[valid], ref[valid, 5].astype(np.int64))
         np.testing.assert_array_equal(got[valid, 4], ref[valid, 4])
-        tol = 2.0 ** -24 * (8 * softcap + np.abs(ref[valid][:, [0, 2]])) if softcap else 0.0
+        tol = CAPPED_VALUE_UNITS * 2.0 ** -24 * np.abs(ref[valid][:, [0, 2]]) if softcap else 0.0
         assert np.all(np.abs(got[valid][:, [0, 2]] - ref[valid][:, [0, 2]]) <= tol)
         assert np.all(rel_err(got[valid, 1], ref[valid, 1]) <= 1e-5)
         assert np.all(got[~valid] == 0)

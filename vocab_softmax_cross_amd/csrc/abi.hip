@@ -78,6 +78,25 @@ int check_problem(const vsce_problem* pb, const void* logits, Prob& p) {
   return VSCE_OK;
 }
 
+// The constants of the soft-cap s (all zero when s = 0: no cap).
+SoftCap soft_cap_constants(float s) {
+  SoftCap c = {};
+  if (s > 0.0f) {
+    constexpr double log2e = 1.4426950408889634;
+    c.s = s;
+    c.k = static_cast<float>(-2.0 * log2e / s);
+    c.sa = static_cast<float>(kCapSqrtA / s);
+    c.ct = static_cast<float>(1.0 / (log2e * s));
+    c.x0 = kCapCentral * s;
+    c.qs = -0.25f * s;
+    c.c0 = kCapC0;
+    c.c1 = kCapC1;
+    c.c2 = kCapC2;
+    c.c3 = kCapC3;
+  }
+  return c;
+}
+
 // The problem's fields every per-row kernel reads.  The kernels index the
 // weights by this buffer's columns, so a shard sees its slice of them.
 void problem_args(const Prob& p, RowArgs& a) {
@@ -90,8 +109,7 @@ void problem_args(const Prob& p, RowArgs& a) {
   a.ignore_index = p.ignore_index;
   a.eps = p.eps;
   a.eta = p.eta;
-  a.cap = p.cap;
-  a.cap_k = p.cap > 0.0f ? static_cast<float>(-2.0 * 1.4426950408889634 / p.cap) : 0.0f;
+  a.cap_c = soft_cap_constants(p.cap);
   a.zl = p.zl;
   a.mean = (p.red == VSCE_REDUCTION_MEAN);
   a.rows = p.rows;

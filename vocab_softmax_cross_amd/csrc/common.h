@@ -16,6 +16,7 @@
 namespace vsce {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kWave = 64;
 
 // Workspace header; field offsets are part of the C ABI (VSCE_WS_*).
@@ -215,36 +216,113 @@ __device__ __forceinline__ T fresh_args() {
 
 // ---------------------------------------------------------------- soft-capping
 // Logit soft-capping x -> s tanh(x / s) and its slope 1 - tanh^2(x / s), each
-// with one hardware exp and one reciprocal.
+// with a relative error of a few units of 2^-24 for every x (u = x / s).  The
+// kernels read the capped logit in base-2 units, l2(x) = log2(e) s tanh(u),
+// since every use is an exponent of 2 (or a sum that is scaled back once).
 //
-// value(x) (the sums of the statistics pass, the maximum, the target logit):
-//   s tanh(x / s) = s - 2 s / (1 + e),   e = exp(2 x / s),
-// one fma after the reciprocal and no sign handling: e = +inf gives s, e = 0
-// gives -s.  The result is accurate to a few units of 2^-24 s.
+// Central range |u| <= kCapCentral: tanh(u) / u = 1 + w Q(w), w = u^2, with Q
+// the cubic that minimizes the largest relative error of 1 + w Q(w) on that
+// range (Remez exchange: 0.62 units of 2^-24).  So
+//   l2(x) = x P(w'),  P = log2(e) (1 + w Q(w)) = C0 + C1 w' + C2 w'^2 + C3 w'^3 + w'^4,
+// in the variable w' = a w, a = (log2(e) c3)^(1/4) for Q's cubic coefficient
+// c3, which makes P's leading coefficient exactly 1 (its first Horner step is
+// then w' + C3, one constant: a VALU instruction of this chip reads at most
+// one scalar or literal operand).  w' = (x sqrt(a) / s)^2.  The slope is
+// 1 - t^2 with t = l2(x) / (log2(e) s) (t <= 0.5: nothing cancels).  In fp32
+// on a grid of 2e5 points per cap (caps 1 to 1e3): at most 2.4 units for the
+// capped logit and 2.3 for the slope.  No exp and no reciprocal, which covers
+// most logits for any practical cap.
 //
-// value(x, slope) (the gradient pass, which also needs the slope) works from
-// q = exp(-2 |x| / s) in [0, 1], taken as q4 = 4 q = 2^(-2 |x| log2(e) / s + 2):
-//   tanh(|x| / s) = (1 - q) / (1 + q),   1 - tanh^2(x / s) = 4 q / (1 + q)^2,
-// so s tanh(|x| / s) = (s - (s / 4) q4) r and the slope is q4 r^2 with
-// r = 1 / (1 + q4 / 4).  q keeps its relative accuracy for every x, so the
-// slope does too (no 1 - t^2 cancellation where the cap saturates).  The two
-// forms of the capped value differ by a few units of 2^-24 s.
-// A NaN logit stays NaN; +-inf caps to +-s with slope 0.
-struct SoftCap {
-  float s;  // the cap, > 0
-  float k;  // -2 log2(e) / s
+// Outside it, from q = exp(-2 |u|), taken as q4 = 4 q = 2^(-2 |x| log2(e) / s + 2):
+//   s tanh(|u|) = (s - (s / 4) q4) r,   slope = q4 r^2,   r = 1 / (1 + q4 / 4),
+// a relative error of at most about 5 units for the value (at the range's
+// edge, where 1 - q cancels a little) and about 4 |u| + 5 for the slope (the
+// exponent argument's own rounding, scaled by its size, dominates far out).
+//
+// l2(x) and central_l2(x) give the same bits for a central x, so the
+// statistics pass and the gradient pass see the same capped logits whichever
+// form each takes.  A NaN logit stays NaN; +-inf caps to +-s with slope 0.
+constexpr float kCapCentral = 0.55f;
+constexpr double kCapSqrtA = 0.62643577936533333060;  // sqrt(a)
+constexpr float kCapC0 = 1.44269502f;                  // log2(e)
+constexpr float kCapC1 = -1.22544873f;
+constexpr float kCapC2 = 1.2479471f;
+constexpr float kCapC3 = -1.25745797f;
 
-  __device__ __forceinline__ float value(float x) const {
-    const float e = __builtin_amdgcn_exp2f(-k * x);
-    return __builtin_fmaf(-2.0f * s, __builtin_amdgcn_rcpf(1.0f + e), s);
+struct SoftCap {
+  float s;      // the cap, > 0
+  float k;      // -2 log2(e) / s
+  float sa;     // sqrt(a) / s: w' = (x sa)^2
+  float ct;     // 1 / (log2(e) s): t = l2(x) ct
+  float x0;     // kCapCentral * s: where the central range ends
+  float qs;     // -s / 4
+  // P's coefficients, passed as kernel arguments: each Horner step then reads
+  // one scalar register instead of a constant copied into a vector register.
+  float c0, c1, c2, c3;
+
+  // P(w'(x)) for a central x: l2(x) = x P.
+  __device__ __forceinline__ float central_p(float x) const {
+    const float up = x * sa;
+    const float wp = up * up;
+    float q = __builtin_fmaf(up, up, c3);
+    q = __builtin_fmaf(q, wp, c2);
+    q = __builtin_fmaf(q, wp, c1);
+    return __builtin_fmaf(q, wp, c0);
   }
-  __device__ __forceinline__ float value(float x, float& slope) const {
+  // The central range's formulas alone: for |x| <= x0 (a caller that knows
+  // every logit it passes lies there; NaN gives NaN).
+  __device__ __forceinline__ float central_l2(float x, float& slope) const {
+    const float xl = x * central_p(x);
+    const float t = xl * ct;
+    slope = __builtin_fmaf(-t, t, 1.0f);
+    return xl;
+  }
+  __device__ __forceinline__ float central_l2(float x) const { return x * central_p(x); }
+  // Any x, in base-2 units: both forms, then a select (no branch per
+  // element: the exec-mask juggling of one costs registers the resident row
+  // needs).
+  __device__ __forceinline__ float l2(float x, float& slope) const {
+    float sc;
+    const float xc = central_l2(x, sc);
     const float q4 = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fabsf(x), k, 2.0f));
     const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(q4, 0.25f, 1.0f));
-    slope = q4 * r * r;
-    return __builtin_copysignf(__builtin_fmaf(-0.25f * s, q4, s) * r, x);
+    const bool c = __builtin_fabsf(x) <= x0;
+    slope = c ? sc : q4 * r * r;
+    return c ? xc : __builtin_copysignf(__builtin_fmaf(qs, q4, s) * r, x) * kLog2e;
+  }
+  __device__ __forceinline__ float l2(float x) const {
+    const float xc = central_l2(x);
+    const float q4 = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fabsf(x), k, 2.0f));
+    const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(q4, 0.25f, 1.0f));
+    const float xr = __builtin_copysignf(__builtin_fmaf(qs, q4, s) * r, x) * kLog2e;
+    return __builtin_fabsf(x) <= x0 ? xc : xr;
+  }
+  // The capped logit s tanh(x / s) itself (for per-row values: the maximum,
+  // the target logit, the statistics).
+  __device__ __forceinline__ float value(float x) const {
+    if (__builtin_fabsf(x) <= x0) return central_l2(x) * kLn2;
+    const float q4 = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fabsf(x), k, 2.0f));
+    const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(q4, 0.25f, 1.0f));
+    return __builtin_copysignf(__builtin_fmaf(qs, q4, s) * r, x);
+  }
+  __device__ __forceinline__ float value(float x, float& slope) const {
+    float xt = central_l2(x, slope) * kLn2;
+    if (!(__builtin_fabsf(x) <= x0)) {
+      const float q4 = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fabsf(x), k, 2.0f));
+      const float r = __builtin_amdgcn_rcpf(__builtin_fmaf(q4, 0.25f, 1.0f));
+      slope = q4 * r * r;
+      xt = __builtin_copysignf(__builtin_fmaf(qs, q4, s) * r, x);
+    }
+    return xt;
   }
 };
+
+// The soft-cap of a kernel's arguments (its field cap_c: the constants of
+// a SoftCap, filled on the host by soft_cap_constants()).
+template <class Args>
+__device__ __forceinline__ SoftCap soft_cap(const Args& a) {
+  return a.cap_c;
+}
 
 // ---------------------------------------------------------------- XCD-aware order
 // The chip hands consecutive workgroups of a launch to its 8 XCDs in turn

@@ -95,7 +95,7 @@ void fused_resident_kernel(const RowArgs a) {
   };
   const int64_t y = a.target[n];
   const int cls = row_class(y, a.Vt, a.ignore_index);
-  const SoftCap cap{a.cap, a.cap_k};
+  const SoftCap cap = soft_cap(a);
 
   if (cls != kValid) {  // uniform over the workgroup: zero gradient, no read
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
@@ -219,8 +219,9 @@ void fused_resident_kernel(const RowArgs a) {
     static_for<NOV>([&](auto k) { r[k] = buf_load16(rsrc, lane_off(k), k * SLOT_BYTES); });
   }
 
-  // ---- pass 1: row maximum
+  // ---- pass 1: row maximum (and, with a soft-cap, each lane's largest |x|)
   float mx = -__builtin_inff();
+  float amax = 0.0f;
   auto max_vec = [&](const uint4 v) {
     const auto w = words(v);
 #pragma unroll
@@ -228,7 +229,10 @@ void fused_resident_kernel(const RowArgs a) {
       float f[EPW];
       D::word_fresh(w.w[q], f);
 #pragma unroll
-      for (int e = 0; e < EPW; ++e) mx = fmaxf(mx, f[e]);
+      for (int e = 0; e < EPW; ++e) {
+        mx = fmaxf(mx, f[e]);
+        if constexpr (CAP) amax = fmaxf(amax, __builtin_fabsf(f[e]));
+      }
     }
   };
   static_for<NREG>([&](auto k) {
@@ -267,13 +271,19 @@ void fused_resident_kernel(const RowArgs a) {
     xy_sh = xv;
   }
   if constexpr (NOV > 0) mx = fmaxf(mx, ov_m[tid / kWave]);  // this wavefront's lane 0 wrote it
+  // A wavefront whose logits all lie in the soft-cap's central range takes
+  // its polynomial alone in passes 2 and 3 (no per-element choice).  fmaxf
+  // drops NaN, which the polynomial turns into NaN like the general path.
+  const bool central = CAP && __ballot(amax > cap.x0) == 0ull;
   const float M = block_max<NT>(mx, red_max);          // of the stored logits
-  const float Mc = CAP ? uniform(cap.value(M)) : M;    // of the logits the loss reads
-  const float ML = Mc * kLog2e;
+  // The shift of the exponents, in base-2 units, and the maximum of the logits
+  // the loss reads (capped ones are read as l2(x) = log2(e) s tanh(x / s)).
+  const float ML = CAP ? uniform(cap.l2(M)) : M * kLog2e;
+  const float Mc = CAP ? ML * kLn2 : M;
 
   // ---- pass 2: sums below the maximum, ties, first index, logit sum
   RowSums rs = {0.0f, 0.0f, 0, 0x7fffffff};
-  auto accumulate = [&](auto careful, const uint4 v, int j) {
+  auto accumulate = [&](auto careful, auto cen, const uint4 v) {
     const auto w = words(v);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -281,14 +291,24 @@ void fused_resident_kernel(const RowArgs a) {
       D::word_fresh(w.w[q], f);
 #pragma unroll
       for (int e = 0; e < EPW; ++e) {
-        const int i = q * EPW + e;  // element within the vector
-        const float fc = CAP ? cap.value(f[e]) : f[e];
-        const float ex = exp_shifted(fc, ML);
+        // ex = exp(x - M) of the (capped) logits; fc joins the logit sum (in
+        // base-2 units when capped: scaled back once per row)
+        float ex, fc;
+        if constexpr (!CAP) {
+          fc = f[e];
+          ex = exp_shifted(fc, ML);
+        } else if constexpr (decltype(cen)::value) {
+          const float P = cap.central_p(f[e]);  // l2(x) = x P
+          ex = __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], P, -ML));
+          fc = f[e] * P;
+        } else {
+          fc = cap.l2(f[e]);
+          ex = __builtin_amdgcn_exp2f(fc - ML);
+        }
         if constexpr (decltype(careful)::value) {
           const bool eq = (f[e] == M);
           rs.s += eq ? 0.0f : ex;
           rs.cnt += eq ? 1 : 0;
-          if (eq) rs.first = min(rs.first, j * VEC + i);
         } else {
           rs.s += ex;
         }
@@ -296,18 +316,53 @@ void fused_resident_kernel(const RowArgs a) {
       }
     }
   };
-  auto sum_pass = [&](auto careful) {
+  auto sum_pass = [&](auto careful, auto cen) {
     static_for<NREG>([&](auto k) {
-      if (in_row(k)) accumulate(careful, r[k], k * NT + tid);
+      if (in_row(k)) accumulate(careful, cen, r[k]);
     });
     static_for<NLDS>([&](auto k) {
-      if (in_row(NREG + k)) accumulate(careful, xl[k * NT + tid], (NREG + k) * NT + tid);
+      if (in_row(NREG + k)) accumulate(careful, cen, xl[k * NT + tid]);
     });
   };
-  // Wavefront-uniform choice: only wavefronts that hold the maximum need the
-  // compare per element.
-  if (__ballot(mx == M) != 0ull) sum_pass(std::true_type{});
-  else sum_pass(std::false_type{});
+  // Wavefront-uniform choices: only wavefronts that hold the maximum need the
+  // compare per element, and a wavefront whose logits all lie in the
+  // soft-cap's central range takes the polynomial alone.
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (__ballot(mx == M) != 0ull) {
+    if (CAP && central) sum_pass(T_{}, T_{});
+    else sum_pass(T_{}, F_{});
+    // The first index of M: only lanes that hold it look for it, over their
+    // own vectors from the last back to the first, so the last match found
+    // is the smallest index.
+    if (rs.cnt > 0) {
+      int first = 0x7fffffff;
+      auto scan = [&](const uint4 v, int k) {
+        const auto w = words(v);
+        const int j = k * NT + fresh_tid();
+#pragma unroll
+        for (int q = 3; q >= 0; --q) {
+          float f[EPW];
+          D::word_fresh(w.w[q], f);
+#pragma unroll
+          for (int e = EPW - 1; e >= 0; --e)
+            if (f[e] == M) first = j * VEC + q * EPW + e;
+        }
+      };
+      static_for<NLDS>([&](auto kk) {
+        constexpr int k = NLDS - 1 - decltype(kk)::value;
+        if (in_row(NREG + k)) scan(xl[k * NT + tid], NREG + k);
+      });
+      static_for<NREG>([&](auto kk) {
+        constexpr int k = NREG - 1 - decltype(kk)::value;
+        if (in_row(k)) scan(r[k], k);
+      });
+      rs.first = first;
+    }
+  } else {
+    if (CAP && central) sum_pass(F_{}, T_{});
+    else sum_pass(F_{}, F_{});
+  }
   if constexpr (NOV > 0) {  // the wavefront's overflow share, at the row maximum, on lane 0
     if ((tid & (kWave - 1)) == 0) {
       const int wv = tid / kWave;
@@ -333,7 +388,12 @@ void fused_resident_kernel(const RowArgs a) {
   {
   const RowArgs& a = ra;
   const float xy_stored = uniform(xy_sh);  // posted before the pass-1 barrier
-  const float xy = CAP ? uniform(cap.value(xy_stored)) : xy_stored;
+  float xy = xy_stored, slope_y = 1.0f;
+  if constexpr (CAP) {
+    xy = uniform(cap.l2(xy_stored, slope_y)) * kLn2;
+    slope_y = uniform(slope_y);
+    rs.S *= kLn2;  // the capped logit sum, summed in base-2 units
+  }
   const float sum_w = uniform(static_cast<float>(a.ws->sum_w));
   const float wy = uniform(WEIGHTED ? a.weight[y] : 1.0f);
   const float lg = uniform(log1pf(dp));  // lse - m, once per row
@@ -355,16 +415,15 @@ void fused_resident_kernel(const RowArgs a) {
   const float sigma = uniform(a.mean ? a.ws->inv_W : 1.0f);
   RowTerms t = row_terms(Mc, dp, lg, xy, wy, sum_w, a.eps, a.eta, sigma, a.zl, z_sigma(a));
   if constexpr (CAP) {
-    float slope_y;
-    cap.value(xy_stored, slope_y);
     t.dxy *= slope_y;  // the owner stores the finished value
+    t.ML = ML;         // the shift pass 2 took, in base-2 units
   }
   t.ML = uniform(t.ML);
   t.K = uniform(t.K);
   t.B = uniform(t.B);
   t.dxy = uniform(t.dxy);
   float Sw = 0.0f;  // this thread's share of sum w x (class weights)
-  auto grad_vec = [&](const uint4 v, int k) {
+  auto grad_vec = [&](auto cen, const uint4 v, int k) {
     const int j = k * NT + tid;
     auto w = words(v);
 #pragma unroll
@@ -377,9 +436,10 @@ void fused_resident_kernel(const RowArgs a) {
         const float b = WEIGHTED ? t.B * wc : t.B;
         if constexpr (CAP) {
           float slope;
-          const float fc = cap.value(f[e], slope);
-          if constexpr (WEIGHTED) Sw = __builtin_fmaf(wc, fc, Sw);
-          f[e] = __builtin_fmaf(exp_shifted(fc, t.ML), t.K, -b) * slope;
+          const float xl =
+              decltype(cen)::value ? cap.central_l2(f[e], slope) : cap.l2(f[e], slope);
+          if constexpr (WEIGHTED) Sw = __builtin_fmaf(wc, xl, Sw);  // base-2 units
+          f[e] = __builtin_fmaf(__builtin_amdgcn_exp2f(xl - t.ML), t.K, -b) * slope;
         } else {
           if constexpr (WEIGHTED) Sw = __builtin_fmaf(wc, f[e], Sw);
           f[e] = __builtin_fmaf(exp_shifted(f[e], t.ML), t.K, -b);
@@ -406,16 +466,20 @@ void fused_resident_kernel(const RowArgs a) {
     buf_store16(rsrc, voff, static_cast<uint32_t>(k) * SLOT_BYTES,
                 make_uint4(w.w[0], w.w[1], w.w[2], w.w[3]));
   };
-  static_for<NREG>([&](auto k) {
-    if (in_row(k)) grad_vec(r[k], k);
-  });
-  static_for<NLDS>([&](auto k) {
-    if (in_row(NREG + k)) grad_vec(xl[k * NT + tid], NREG + k);
-  });
+  auto grad_pass = [&](auto cen) {
+    static_for<NREG>([&](auto k) {
+      if (in_row(k)) grad_vec(cen, r[k], k);
+    });
+    static_for<NLDS>([&](auto k) {
+      if (in_row(NREG + k)) grad_vec(cen, xl[k * NT + tid], NREG + k);
+    });
+  };
+  if (CAP && central) grad_pass(std::true_type{});
+  else grad_pass(std::false_type{});
   if constexpr (WEIGHTED) {  // summed in the order pass 2 sums the unweighted S
     const RowSums sw = block_sums<NT>(RowSums{0.0f, Sw, 0, 0x7fffffff}, red_sum3);
     if (tid == 0 && a.eps > 0.0f) {
-      const float l = l0 - a.eta * sw.S;
+      const float l = l0 - a.eta * (CAP ? sw.S * kLn2 : sw.S);
       a.loss_rows[n] = l;
       if (a.loss_rows2) a.loss_rows2[n] = l;
     }

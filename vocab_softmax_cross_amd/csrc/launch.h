@@ -6,11 +6,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
 #include "vsce.h"
 
 namespace vsce {
-
-struct WsHeader;
 
 // A validated problem with the derived quantities the launchers need.
 struct Prob {
@@ -47,8 +46,7 @@ struct RowArgs {
   int64_t ignore_index;
   float eps;
   float eta;
-  float cap;            // soft-cap s (the CAP kernels only)
-  float cap_k;          // -2 log2(e) / s
+  SoftCap cap_c;        // the soft-cap's constants (the CAP kernels only)
   float zl;             // z-loss lambda (0: off)
   int mean;             // sigma = 1 / W (mean) else 1
   float* loss_rows;     // [rows] per-row loss (never null)
@@ -70,6 +68,8 @@ struct RowArgs {
 int check_problem(const vsce_problem* pb, const void* logits, Prob& p);
 // The problem's fields every per-row kernel reads.
 void problem_args(const Prob& p, RowArgs& a);
+// The constants of a soft-cap s (zeros for s = 0).
+SoftCap soft_cap_constants(float s);
 // Byte offset, in a workspace of vsce_workspace_bytes(rows), of its [rows]
 // float4 statistics area (the fused mode's rows that are read twice).
 int64_t stats_scratch_offset(int64_t rows);

@@ -93,7 +93,7 @@ __device__ inline void finish_stats(const RowArgs& a, const char* row, float m, 
   constexpr int E = G::E;
   const int tid = threadIdx.x;
   const int64_t ng = a.nvec;
-  const SoftCap cap{a.cap, a.cap_k};
+  const SoftCap cap = soft_cap(a);
   auto capped = [&](float v) { return CAP ? cap.value(v) : v; };
   const float M = block_max<NT>(m, red_max);     // of the stored logits
   const float Mc = capped(M);                    // of the logits the loss reads
@@ -166,7 +166,7 @@ __device__ inline void stream_stats(const RowArgs& a, const char* row, float& M_
   constexpr int E = G::E;
   const int tid = threadIdx.x;
   const int64_t ng = a.nvec;
-  const SoftCap cap{a.cap, a.cap_k};
+  const SoftCap cap = soft_cap(a);
   auto capped = [&](float v) { return CAP ? cap.value(v) : v; };
   float m = -__builtin_inff(), s = 0.0f, S = 0.0f;
 
@@ -218,7 +218,7 @@ __device__ inline void stream_grad(const RowArgs& a, const char* src, char* dst,
   using G = Grp<DT, VECP>;
   constexpr int E = G::E;
   const int tid = threadIdx.x;
-  const SoftCap cap{a.cap, a.cap_k};
+  const SoftCap cap = soft_cap(a);
   const int64_t gy = y >= 0 ? y / E : -1;  // y < 0: no element here owns the target
   const int iy = static_cast<int>(y >= 0 ? y % E : 0);
   for (int64_t g0 = g_begin; g0 < g_end; g0 += static_cast<int64_t>(NT) * U) {
@@ -274,7 +274,7 @@ template <bool CAP>
 __device__ inline float cap_slope(const RowArgs& a, float x) {
   if constexpr (!CAP) return 1.0f;
   float slope;
-  SoftCap{a.cap, a.cap_k}.value(x, slope);
+  soft_cap(a).value(x, slope);
   return slope;
 }
 
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(NT) void stats_kernel(const RowArgs a) {
       float xy = 0.0f;
       if (yl >= 0 && yl < a.V) {
         const float xs = D::load1(row, yl);
-        xy = CAP ? SoftCap{a.cap, a.cap_k}.value(xs) : xs;
+        xy = CAP ? soft_cap(a).value(xs) : xs;
       }
       float4* pr = reinterpret_cast<float4*>(a.partial + n * VSCE_PARTIAL_STRIDE);
       pr[0] = make_float4(M, dp, xy, a.eps > 0.0f ? S : 0.0f);
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(NT) void stats_kernel(const RowArgs a) {
   }
   if (threadIdx.x == 0) {
     const float xs = D::load1(row, y);
-    const float xy = CAP ? SoftCap{a.cap, a.cap_k}.value(xs) : xs;
+    const float xy = CAP ? soft_cap(a).value(xs) : xs;
     const float sum_w = static_cast<float>(a.ws->sum_w);
     const float lg = log1pf(dp);
     const float zrow = row_z(M, lg, a.zl);
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(NT) void fused_ring_kernel(const RowArgs a) {
   auto fetch = [&](int k) {
     buf_load16_lds(rsrc, slot(k), static_cast<uint32_t>(vec(k)) * 16u, 0);
   };
-  const SoftCap cap{a.cap, a.cap_k};
+  const SoftCap cap = soft_cap(a);
   auto capped = [&](float v) { return CAP ? cap.value(v) : v; };
 
   // ---- pass 1: online (max, sum, logit sum) per lane
