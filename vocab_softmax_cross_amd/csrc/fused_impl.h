@@ -188,8 +188,13 @@ void fused_resident_kernel(const RowArgs a) {
     static_for<NOV>([&](auto k) {
       if (ov_col(k, t1) < nvec) ov[k] = buf_load16(rsrc, vo1, k * SLOT_BYTES);
     });
+    // One overflow vector at a time, its column from a fresh thread id: the
+    // six columns and the unpacked elements of two vectors need not be held
+    // beside the 44 registers of loads in flight.
     static_for<NOV>([&](auto k) {
-      if (ov_col(k, t1) < nvec) online(ov[k], ov_col(k, t1));
+      const int tk = fresh_tid();
+      if (ov_col(k, tk) < nvec) online(ov[k], ov_col(k, tk));
+      __builtin_amdgcn_sched_barrier(0);
     });
 #pragma unroll
     for (int d = kWave / 2; d >= 1; d /= 2) {  // fixed order
