@@ -736,15 +736,12 @@ def test_deterministic_repeat():
 
 # ---------------------------------------------------------------- autograd and host syncs
 
-@pytest.mark.parametrize("mode", ["fused", "split"])
-@pytest.mark.parametrize("reduction,go", [("mean", 1.0), ("sum", 0.37), ("none", 0.37)])
-@pytest.mark.parametrize("variant", ["plain", "smoothing", "weights"])
-def test_no_host_sync(mode, reduction, go, variant):
-    """Forward and backward under torch's sync debug mode "error" (the
-    pages' no-host-sync test, here for mean too)."""
+def _no_sync_case(wl, mode, reduction, go):
+    """Forward and backward through the autograd entry point under torch's
+    sync debug mode "error", then the loss and gradient against the oracle."""
     dev = _dev()
-    wl = _small("llm_head", 64, 8000, weighted=(variant == "weights"),
-                label_smoothing=0.1 if variant != "plain" else 0.0)
+    _note(f"no-sync {wl.name} BT={wl.BT} V={wl.V} mode={mode} red={reduction} go={go} "
+          f"weighted={wl.weighted} eps={wl.label_smoothing}")
     tgt = W.targets(wl)
     xh = W.logits(wl, tgt)
     w = W.class_weights(wl)
@@ -767,6 +764,27 @@ def test_no_host_sync(mode, reduction, go, variant):
     rep = grad_report(x.grad.float().cpu().numpy(), ref.grad, wl.dtype, W.as_f64(xh), tgt,
                       ref.stats, ref.cls, ref.scale, wl.label_smoothing, w, ref.norm.sum_w)
     assert rep.floor_fail == 0, rep
+
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+@pytest.mark.parametrize("reduction,go", [("mean", 1.0), ("sum", 0.37), ("none", 0.37)])
+@pytest.mark.parametrize("variant", ["plain", "smoothing", "weights"])
+def test_no_host_sync(mode, reduction, go, variant):
+    """Forward and backward under torch's sync debug mode "error" (the
+    pages' no-host-sync test, here for mean too)."""
+    wl = _small("llm_head", 64, 8000, weighted=(variant == "weights"),
+                label_smoothing=0.1 if variant != "plain" else 0.0)
+    _no_sync_case(wl, mode, reduction, go)
+
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+@pytest.mark.parametrize("reduction,go", [("none", 0.5), ("sum", 0.5), ("mean", 0.37)])
+def test_no_host_sync_weighted_workload(mode, reduction, go):
+    """The same at the weighted workload's row length (V = 151936 bf16, class
+    weights, smoothing 0.1, 5% ignored rows), with grad_output != 1: the
+    weighted one-row-per-CU kernel, the split pair and the in-place scale
+    (Liger-Kernel PR #1622, Testing Done: no host sync with class weights)."""
+    _no_sync_case(W.with_rows(W.WORKLOADS["weighted"], 48), mode, reduction, go)
 
 
 def test_fused_second_backward_raises():
@@ -831,6 +849,63 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(static_x, eager_g)
         assert torch.equal(res["loss"], eager_l)
+        _ = (pristine.float() * 2).sum()  # unrelated eager work between replays
+
+
+@pytest.mark.parametrize("reduction", ["none", "sum"])
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_graph_capture_weighted_step(mode, reduction):
+    """A whole step of the weighted workload's rows (V = 151936 bf16, class
+    weights, smoothing 0.1) captured in a HIP graph: the fused forward and the
+    in-place grad_output scale at 0.5, or the statistics forward and the
+    in-place backward.  Every replay, with eager work and synchronizations in
+    between, equals the eager step bit for bit."""
+    dev = _dev()
+    wl = W.with_rows(W.WORKLOADS["weighted"], 64)
+    tgt = W.targets(wl)
+    w = W.class_weights(wl)
+    xh = W.logits(wl, tgt)
+    t = torch.from_numpy(tgt).to(dev)
+    wt = torch.from_numpy(w).to(dev)
+    eps = wl.label_smoothing
+    go = _go_tensor(0.5, reduction, wl.BT, dev)
+    pristine = xh.to(dev)
+
+    def step(x, ws):
+        if mode == "fused":
+            res = vf.forward_fused_inplace(x, t, wt, -100, eps, reduction, row_loss=True,
+                                           workspace=ws)
+            vf.scale_grad(x, go, reduction)
+        else:
+            res = vf.forward_stats(x, t, wt, -100, eps, reduction, row_loss=True, workspace=ws)
+            vf.backward_from_stats(x, t, res["stats"], go, ws, wt, -100, eps, reduction, out=x)
+        return res
+
+    x = pristine.clone()
+    eager = step(x, vf.workspace_for(wl.BT, dev))
+    torch.cuda.synchronize()
+    eager_g, eager_l, eager_r = x.clone(), eager["loss"].clone(), eager["row_loss"].clone()
+    ref = oracle.cross_entropy(W.as_f64(xh), tgt, w, -100, eps, reduction, 1.0, None,
+                               want_grad=False)
+    assert_loss_close(eager_l.cpu().numpy().astype(np.float64), ref.loss)
+
+    static_x = pristine.clone()
+    ws = vf.workspace_for(wl.BT, dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(static_x, ws)  # warm-up
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        res = step(static_x, ws)
+    for _ in range(3):
+        static_x.copy_(pristine)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(static_x, eager_g)
+        assert torch.equal(res["loss"], eager_l) and torch.equal(res["row_loss"], eager_r)
         _ = (pristine.float() * 2).sum()  # unrelated eager work between replays
 
 
