@@ -631,7 +631,11 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": stored_traffic(wl.name), "traffic_unit": "bytes/launch",
                      "kernel": "fused_resident_kernel", "bytes_per_launch": kernel_bytes,
-                     "mean_launch_ms": round(mean_kernel_s * 1e3, 4)},
+                     "mean_launch_ms": round(mean_kernel_s * 1e3, 4),
+                     "scope": "the row kernel alone: HIP events around its launch",
+                     "step_frac": round(step_bytes * K / wall / 1e9 / HBM_PEAK_GBPS, 4),
+                     "step_scope": "the whole step by the wall clock: normalizers, row kernel, "
+                                   "loss reduction, grad_output scale"},
         "modes": extra,
         "copy_ceiling": copy_ceiling,
         "peak_memory": peak_memory,

@@ -10,7 +10,7 @@
  * load this file.  It shares no code, header, table or constant with the HIP
  * library, and the library never calls it.
  *
- * Every function here is pinned by the CPU tests (tests/test_oracle_*.py)
+ * Every function here is pinned by the CPU tests (tests/test_oracle.py)
  * against library routines, closed forms, invariants, brute force at 50
  * digits and the accuracy table printed on the pages; none is "parity
  * unpinned".
