@@ -844,6 +844,7 @@ def test_graph_capture_replays_match_eager():
         res = vf.forward_fused_inplace(static_x, t, label_smoothing=0.1, workspace=ws)
     for _ in range(3):
         static_x.copy_(pristine)
+        res["loss"].fill_(float("nan"))  # each replay must write its own reduced loss
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
@@ -901,6 +902,8 @@ def test_graph_capture_weighted_step(mode, reduction):
         res = step(static_x, ws)
     for _ in range(3):
         static_x.copy_(pristine)
+        res["loss"].fill_(float("nan"))  # each replay must write its own outputs
+        res["row_loss"].fill_(float("nan"))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
