@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--flce-only", action="store_true",
                     help="run only the FLCE measurement (a short run for profiling) and print "
                          "its JSON line")
+    ap.add_argument("--only-workload", choices=("confidence", "weighted"),
+                    help="run only the row kernel on that workload's full size (a short run for "
+                         "profiling) and print its JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle time budget for the cpu_baseline sample")
     return ap.parse_args()
@@ -214,7 +217,7 @@ def long_rows_mode(L, W, hip, dev, stream, K):
     return res
 
 
-def workload_modes(L, W, hip, dev, stream, K):
+def workload_modes(L, W, hip, dev, stream, K, names=("confidence", "weighted")):
     """The fused row kernel on the other workloads' full sizes: the
     confidence workload (4096 x 32000 bf16, targets at p = 0.9 / 0.99 / 0.999)
     and the weighted one (16384 x 151936 bf16, class weights, smoothing 0.1,
@@ -225,7 +228,7 @@ def workload_modes(L, W, hip, dev, stream, K):
     import numpy as np
     import torch
     res = {}
-    for name in ("confidence", "weighted"):
+    for name in names:
         wl = W.WORKLOADS[name]
         tgt = W.targets(wl)
         w = W.class_weights(wl)
@@ -384,6 +387,11 @@ def main():
         res, _ = flce_mode(L, W, Hip(), dev, torch.cuda.current_stream(dev).cuda_stream,
                            args.steps)
         print(json.dumps({"flce": res}), flush=True)
+        return
+    if args.only_workload:
+        res = workload_modes(L, W, Hip(), dev, torch.cuda.current_stream(dev).cuda_stream,
+                             args.steps, names=(args.only_workload,))
+        print(json.dumps(res), flush=True)
         return
     wl = W.WORKLOADS[args.workload]
     K, Wu = args.steps, args.warmup

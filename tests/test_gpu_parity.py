@@ -531,6 +531,44 @@ def test_every_resident_shape(V):
     check(wl, out, reference(wl, xh, tgt, w, "mean", 1.0), xh, tgt, w)
 
 
+# ---------------------------------------------------------------- one row per CU, many rows
+# Rows of 16321-32768 vectors with class weights or a soft-cap (bf16 V up to
+# 262144), and unweighted ones past the overflow shapes, take the shapes that
+# hold one row per CU (1024 threads, 16 or 24 register slots and LDS).  These
+# cases give every CU several rows in turn, with ignored rows first, last and
+# in runs, and check every row loss and every gradient element.
+
+def _targets_with_ignored_runs(wl):
+    t = W.targets(wl)
+    BT = wl.BT
+    t[:3] = -100                     # the first rows
+    t[BT - 4:] = -100                # the last rows
+    t[BT // 3:BT // 3 + 70] = -100   # a run of 70
+    t[BT // 2] = t[BT // 2 + 1]      # two rows with the same target
+    return t
+
+
+@pytest.mark.parametrize("case,reduction,go", [
+    ("weighted_bf16", "sum", 0.5), ("weighted_bf16", "none", 0.5), ("weighted_f32", "none", 0.5),
+    ("softcap_bf16", "mean", 1.0), ("weighted_softcap_bf16", "mean", 0.5),
+    ("long_bf16", "mean", 1.0)])
+def test_one_row_per_cu_shapes_many_rows(case, reduction, go):
+    """Every row loss and every gradient element of 600-700 rows."""
+    cases = {  # (workload, BT, V, dtype, features)
+        "weighted_bf16": ("weighted", 640, 151936, "bf16", {}),
+        "weighted_f32": ("weighted", 600, 70000, "f32", {}),
+        "softcap_bf16": ("llm_head", 600, 140000, "bf16", dict(softcap=30.0, z_loss=1e-4)),
+        "weighted_softcap_bf16": ("weighted", 600, 160000, "bf16",
+                                  dict(softcap=15.0, z_loss=1e-3)),
+        "long_bf16": ("llm_head", 700, 200000, "bf16", {}),
+    }
+    name, BT, V, dtype, kw = cases[case]
+    wl = _small(name, BT, V, dtype=dtype)
+    tgt = _targets_with_ignored_runs(wl)
+    out, xh, tgt, w = run(wl, "fused", reduction, go, accuracy=True, tgt=tgt, **kw)
+    check(wl, out, reference(wl, xh, tgt, w, reduction, go, **kw), xh, tgt, w)
+
+
 # ---------------------------------------------------------------- rows longer than the chip
 # Fused rows past the largest on-chip shape (32768 vectors), and rows off
 # 16-byte vectors, are read twice: by default the statistics kernel and the

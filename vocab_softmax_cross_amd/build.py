@@ -56,12 +56,6 @@ SCRATCH_ALLOWED = {
     (1024, 11, 5, 0, True, True):
         "class weights and a soft-cap on the two-rows-per-CU shape: the weights in flight "
         "and the cap's slope beside the 44 row registers",
-    (512, 8, 0, 0, True, True):
-        "class weights and a soft-cap on rows of 2049-4096 vectors at 8 waves per SIMD "
-        "(64 registers): the weights in flight beside the 32 row registers",
-    (1024, 24, 8, 0, True, True):
-        "class weights and a soft-cap on rows of 20481-32768 vectors (one row per CU, 128 "
-        "registers): the weights in flight beside the 96 row registers",
 }
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -369,6 +369,13 @@ __device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint
   const u32x4_t w = {v.x, v.y, v.z, v.w};
   __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, kNT);
 }
+// 16 bytes per lane with the default cache policy: data that every row
+// reads again (class weights), kept in L2.
+__device__ inline uint4 buf_load16_cached(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                          uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 // 16 bytes per lane straight into LDS; lane i of the wavefront lands at
 // lds_wave + 16 i, so `lds_wave` must be the same for the whole wavefront.
 // POLICY: kNT for a stream read once; 0 (default) for data other workgroups

@@ -337,10 +337,10 @@ void fused_resident_kernel(const RowArgs a) {
   if (__ballot(mx == M) != 0ull) {
     if (CAP && central) sum_pass(T_{}, T_{});
     else sum_pass(T_{}, F_{});
-    // The first index of M: only lanes that hold it look for it, over their
-    // own vectors from the last back to the first, so the last match found
-    // is the smallest index.
-    if (rs.cnt > 0) {
+    // The first index of M (for the accuracy output only): only lanes that
+    // hold it look for it, over their own vectors from the last back to the
+    // first, so the last match found is the smallest index.
+    if (rs.cnt > 0 && a.acc_rows != nullptr) {
       int first = 0x7fffffff;
       auto scan = [&](const uint4 v, int k) {
         const auto w = words(v);
@@ -428,16 +428,32 @@ void fused_resident_kernel(const RowArgs a) {
   t.B = uniform(t.B);
   t.dxy = uniform(t.dxy);
   float Sw = 0.0f;  // this thread's share of sum w x (class weights)
+  // The class weights of a vector's VEC columns: 16 bytes (4 weights) per
+  // load, through a buffer resource over the weights (kept in L2: every row
+  // reads them).
+  const auto wrsrc = make_rsrc(a.weight, WEIGHTED ? static_cast<uint32_t>(a.V * 4) : 0u);
+  constexpr int NWV = WEIGHTED ? VEC / 4 : 1;
   auto grad_vec = [&](auto cen, const uint4 v, int k) {
-    const int j = k * NT + tid;
     auto w = words(v);
+    uint4 wv[NWV];  // weights of vector j = k NT + tid: columns j VEC .. j VEC + VEC - 1
+    if constexpr (WEIGHTED) {
+      static_for<NWV>([&](auto h) {
+        wv[h] = buf_load16_cached(wrsrc, static_cast<uint32_t>(tid) * (VEC * 4u) + h * 16u,
+                                  static_cast<uint32_t>(k) * (NT * VEC * 4u));
+      });
+    }
+    auto weight_of = [&](int i) {  // the weight of column j VEC + i, i < VEC
+      const uint4 q4 = wv[i / 4];
+      const int c = i % 4;
+      return __uint_as_float(c == 0 ? q4.x : c == 1 ? q4.y : c == 2 ? q4.z : q4.w);
+    };
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float f[EPW];
       D::word_fresh(w.w[q], f);
 #pragma unroll
       for (int e = 0; e < EPW; ++e) {
-        const float wc = WEIGHTED ? a.weight[j * VEC + q * EPW + e] : 1.0f;
+        const float wc = WEIGHTED ? weight_of(q * EPW + e) : 1.0f;
         const float b = WEIGHTED ? t.B * wc : t.B;
         if constexpr (CAP) {
           float slope;
@@ -552,6 +568,7 @@ using Shapes = std::tuple<Shape<64, 4, 0, 4>,       // rows up to 256 vectors
 
 template <int DT, bool W, bool CAP, class SH>
 int launch_shape(const Prob& p, const RowArgs& a, hipStream_t s) {
+  if (p.rows <= 0) return VSCE_OK;
   hipLaunchKernelGGL(
       (fused_resident_kernel<DT, SH::NT, SH::NREG, SH::NLDS, SH::LDS_CAP, SH::NOV, W, CAP,
                              SH::WPE>),
