@@ -551,9 +551,13 @@ def _targets_with_ignored_runs(wl):
 @pytest.mark.parametrize("case,reduction,go", [
     ("weighted_bf16", "sum", 0.5), ("weighted_bf16", "none", 0.5), ("weighted_f32", "none", 0.5),
     ("softcap_bf16", "mean", 1.0), ("weighted_softcap_bf16", "mean", 0.5),
-    ("long_bf16", "mean", 1.0)])
+    ("long_bf16", "mean", 1.0), ("long_weighted_bf16", "sum", 0.5),
+    ("long_confident_bf16", "mean", 1.0), ("long_f16", "none", 0.37)])
 def test_one_row_per_cu_shapes_many_rows(case, reduction, go):
-    """Every row loss and every gradient element of 600-700 rows."""
+    """Every row loss and every gradient element of 600-700 rows.  The rows of
+    more than 20480 vectors without a soft-cap take the online statistics
+    pass (long_*), here also in the confident regime (targets at softmax
+    0.9 / 0.99 / 0.999, no smoothing: every element within 1 ulp)."""
     cases = {  # (workload, BT, V, dtype, features)
         "weighted_bf16": ("weighted", 640, 151936, "bf16", {}),
         "weighted_f32": ("weighted", 600, 70000, "f32", {}),
@@ -561,12 +565,43 @@ def test_one_row_per_cu_shapes_many_rows(case, reduction, go):
         "weighted_softcap_bf16": ("weighted", 600, 160000, "bf16",
                                   dict(softcap=15.0, z_loss=1e-3)),
         "long_bf16": ("llm_head", 700, 200000, "bf16", {}),
+        "long_weighted_bf16": ("weighted", 600, 200000, "bf16", {}),
+        "long_confident_bf16": ("confidence", 600, 200000, "bf16", {}),
+        "long_f16": ("llm_head", 600, 250000, "f16", {}),
     }
     name, BT, V, dtype, kw = cases[case]
     wl = _small(name, BT, V, dtype=dtype)
-    tgt = _targets_with_ignored_runs(wl)
+    tgt = W.targets(wl) if name == "confidence" else _targets_with_ignored_runs(wl)
     out, xh, tgt, w = run(wl, "fused", reduction, go, accuracy=True, tgt=tgt, **kw)
-    check(wl, out, reference(wl, xh, tgt, w, reduction, go, **kw), xh, tgt, w)
+    ref = reference(wl, xh, tgt, w, reduction, go, **kw)
+    check(wl, out, ref, xh, tgt, w)
+    if name == "confidence":
+        rows = np.arange(wl.BT)
+        gy = out["grad"][rows, tgt]
+        ry = ref["grad"][rows, tgt]
+        assert np.max(rel_err(gy, ry)) <= 0.005
+
+
+def test_one_row_per_cu_nan_propagates():
+    """A NaN logit reaches its row's loss and gradient only, on the online
+    statistics pass (bf16 V = 200000) and the two-pass one (V = 151936)."""
+    dev = _dev()
+    for V in (200000, 151936):
+        wl = _small("llm_head", 6, V)
+        tgt = W.targets(wl)
+        tgt[:] = np.arange(6) * 7 + 3
+        xh = W.logits(wl, tgt)
+        xh[2, V - 5] = float("nan")
+        xh[4, 0] = float("nan")
+        x = xh.to(dev)
+        t = torch.from_numpy(tgt).to(dev)
+        res = vf.forward_fused_inplace(x, t, reduction="none")
+        torch.cuda.synchronize()
+        loss = res["loss"].cpu()
+        assert math.isnan(loss[2]) and math.isnan(loss[4]), V
+        assert torch.isfinite(loss[[0, 1, 3, 5]]).all(), V
+        assert torch.isnan(x[2]).all() and torch.isnan(x[4]).all(), V
+        assert torch.isfinite(x[[0, 1, 3, 5]]).all(), V
 
 
 # ---------------------------------------------------------------- rows longer than the chip

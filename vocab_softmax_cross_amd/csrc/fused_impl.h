@@ -225,6 +225,22 @@ void fused_resident_kernel(const RowArgs a) {
   }
 
   // ---- pass 1: row maximum (and, with a soft-cap, each lane's largest |x|)
+  // With one row per CU (and uncapped logits), passes 1 and 2 are one online
+  // pass instead (ONLINE): each register slot is folded in as its load lands,
+  // so the statistics' arithmetic overlaps the rest of the row's read, where
+  // two passes would start only once the whole row had arrived and leave the
+  // CU's memory idle while they run.  Per lane: the maximum om so far, the
+  // sum osum of exp(x - om) over elements below it and the count oc at it,
+  // rescaled once whenever a vector raises om (the elements then at the old
+  // maximum join the sum); merged over the wavefront and the workgroup in a
+  // fixed order, with the same rescaling.  (The overflow pass's scheme.)
+  // Measured faster on the 24-slot shape only (rows of 20481-32768 vectors);
+  // on the 16-slot one the gradient pass grew by what the statistics saved.
+  constexpr bool ONLINE = !CAP && NOV == 0 && NT == 1024 && NREG >= 24;
+  __shared__ float4 red_on[ONLINE ? NW : 1];
+  float lane_m = -__builtin_inff();  // ONLINE: this lane's maximum
+  float M_on = 0.0f;
+  RowSums rs_on = {0.0f, 0.0f, 0, 0x7fffffff};
   float mx = -__builtin_inff();
   float amax = 0.0f;
   auto max_vec = [&](const uint4 v) {
@@ -240,14 +256,50 @@ void fused_resident_kernel(const RowArgs a) {
       }
     }
   };
-  static_for<NREG>([&](auto k) {
-    if (in_row(k)) max_vec(r[k]);
-  });
+  float om = -__builtin_inff(), osum = 0.0f, oS = 0.0f;
+  int oc = 0;
+  auto online_vec = [&](const uint4 v) {
+    float f[VEC];
+    D::unpack(v, f);
+    float bm = f[0];
+#pragma unroll
+    for (int e = 1; e < VEC; ++e) bm = fmaxf(bm, f[e]);
+    const float nm = fmaxf(om, bm);
+    const bool up = nm > om;  // select, not branch: the lanes stay together
+    const float sc = __builtin_amdgcn_exp2f((om - nm) * kLog2e);
+    osum = up ? (osum + static_cast<float>(oc)) * sc : osum;
+    oc = up ? 0 : oc;
+    om = nm;
+    const float mL = om * kLog2e;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const bool eq = f[e] == om;
+      osum += eq ? 0.0f : exp_shifted(f[e], mL);
+      oc += eq ? 1 : 0;
+      if constexpr (!WEIGHTED) oS += f[e];  // weighted: summed in pass 3
+    }
+  };
+  if constexpr (ONLINE) {
+    // One slot at a time (the scheduler would otherwise unpack several
+    // slots' elements at once beside the row's registers).
+    static_for<NREG>([&](auto k) {
+      if (in_row(k)) online_vec(r[k]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  } else {
+    static_for<NREG>([&](auto k) {
+      if (in_row(k)) max_vec(r[k]);
+    });
+  }
   if constexpr (NLDS > 0) {
     // Each lane reads back only the LDS slots its own wavefront loaded.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     static_for<NLDS>([&](auto k) {
-      if (in_row(NREG + k)) max_vec(xl[k * NT + tid]);
+      if (in_row(NREG + k)) {
+        if constexpr (ONLINE) online_vec(xl[k * NT + tid]);
+        else max_vec(xl[k * NT + tid]);
+      }
+      if constexpr (ONLINE) __builtin_amdgcn_sched_barrier(0);
     });
   }
   // The lane that holds column y posts x[y] to LDS (read by every wavefront
@@ -276,11 +328,49 @@ void fused_resident_kernel(const RowArgs a) {
     xy_sh = xv;
   }
   if constexpr (NOV > 0) mx = fmaxf(mx, ov_m[tid / kWave]);  // this wavefront's lane 0 wrote it
+  if constexpr (ONLINE) {
+    lane_m = om;
+    // (maximum, sum below it, count at it, logit sum) merged over the
+    // wavefront's lanes in a fixed order; every lane gets the result.
+    auto merge_wave = [&](float& m, float& sm, int& c, float& S) {
+#pragma unroll
+      for (int d = kWave / 2; d >= 1; d /= 2) {
+        const float m2 = __shfl_xor(m, d), s2 = __shfl_xor(sm, d), S2 = __shfl_xor(S, d);
+        const int c2 = __shfl_xor(c, d);
+        const float mm = fmaxf(m, m2);
+        const float s1 = m == mm ? sm
+                                 : (sm + static_cast<float>(c)) *
+                                       __builtin_amdgcn_exp2f((m - mm) * kLog2e);
+        const float s2m = m2 == mm ? s2
+                                   : (s2 + static_cast<float>(c2)) *
+                                         __builtin_amdgcn_exp2f((m2 - mm) * kLog2e);
+        c = (m == mm ? c : 0) + (m2 == mm ? c2 : 0);
+        m = mm;
+        sm = s1 + s2m;
+        S += S2;
+      }
+    };
+    merge_wave(om, osum, oc, oS);
+    if ((tid & (kWave - 1)) == 0)
+      red_on[tid / kWave] = make_float4(om, osum, __int_as_float(oc), oS);
+    lds_barrier();
+    // The wavefronts' states: lane w of every wavefront takes wavefront w's
+    // (the other lanes an empty state), merged again the same way.
+    const int l = tid & (kWave - 1);
+    const float4 q = red_on[l < NW ? l : 0];
+    float m = l < NW ? q.x : -__builtin_inff();
+    float sm = l < NW ? q.y : 0.0f;
+    int c = l < NW ? __float_as_int(q.z) : 0;
+    float S = l < NW ? q.w : 0.0f;
+    merge_wave(m, sm, c, S);
+    M_on = uniform(m);
+    rs_on = {uniform(sm), uniform(S), uniform(c), 0x7fffffff};
+  }
   // A wavefront whose logits all lie in the soft-cap's central range takes
   // its polynomial alone in passes 2 and 3 (no per-element choice).  fmaxf
   // drops NaN, which the polynomial turns into NaN like the general path.
   const bool central = CAP && __ballot(amax > cap.x0) == 0ull;
-  const float M = block_max<NT>(mx, red_max);          // of the stored logits
+  const float M = ONLINE ? M_on : block_max<NT>(mx, red_max);  // of the stored logits
   // The shift of the exponents, in base-2 units, and the maximum of the logits
   // the loss reads (capped ones are read as l2(x) = log2(e) s tanh(x / s)).
   const float ML = CAP ? uniform(cap.l2(M)) : M * kLog2e;
@@ -334,7 +424,9 @@ void fused_resident_kernel(const RowArgs a) {
   // soft-cap's central range takes the polynomial alone.
   using T_ = std::true_type;
   using F_ = std::false_type;
-  if (__ballot(mx == M) != 0ull) {
+  if constexpr (ONLINE) {
+    rs = rs_on;
+  } else if (__ballot(mx == M) != 0ull) {
     if (CAP && central) sum_pass(T_{}, T_{});
     else sum_pass(T_{}, F_{});
     // The first index of M (for the accuracy output only): only lanes that
@@ -383,7 +475,38 @@ void fused_resident_kernel(const RowArgs a) {
       rs.S += ov_S[wv];
     }
   }
-  rs = block_sums<NT>(rs, red_sum);
+  if constexpr (ONLINE) {
+    // The first index of M (for the accuracy output only), by the lanes that
+    // hold it, as pass 2 finds it.
+    if (a.acc_rows != nullptr) {
+      int first = 0x7fffffff;
+      if (lane_m == M) {
+        auto scan = [&](const uint4 v, int k) {
+          const auto w = words(v);
+          const int j = k * NT + fresh_tid();
+#pragma unroll
+          for (int q = 3; q >= 0; --q) {
+            float f[EPW];
+            D::word_fresh(w.w[q], f);
+#pragma unroll
+            for (int e = EPW - 1; e >= 0; --e)
+              if (f[e] == M) first = j * VEC + q * EPW + e;
+          }
+        };
+        static_for<NLDS>([&](auto kk) {
+          constexpr int k = NLDS - 1 - decltype(kk)::value;
+          if (in_row(NREG + k)) scan(xl[k * NT + tid], NREG + k);
+        });
+        static_for<NREG>([&](auto kk) {
+          constexpr int k = NREG - 1 - decltype(kk)::value;
+          if (in_row(k)) scan(r[k], k);
+        });
+      }
+      rs.first = block_sums<NT>(RowSums{0.0f, 0.0f, 0, first}, red_sum).first;
+    }
+  } else {
+    rs = block_sums<NT>(rs, red_sum);
+  }
 
   const float dp = rs.s + static_cast<float>(rs.cnt - 1);  // d' = d - 1
   // What only the row's end needs (normalizers, outputs, z-loss) is read from
