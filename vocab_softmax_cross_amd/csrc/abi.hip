@@ -89,10 +89,12 @@ SoftCap soft_cap_constants(float s) {
     c.ct = static_cast<float>(1.0 / (log2e * s));
     c.x0 = kCapCentral * s;
     c.qs = -0.25f * s;
+    const double a2 = (kCapSqrtA / s) * (kCapSqrtA / s);
     c.c0 = kCapC0;
-    c.c1 = kCapC1;
-    c.c2 = kCapC2;
-    c.c3 = kCapC3;
+    c.c1 = static_cast<float>(static_cast<double>(kCapC1) * a2);
+    c.c2 = static_cast<float>(static_cast<double>(kCapC2) * a2 * a2);
+    c.c3 = static_cast<float>(static_cast<double>(kCapC3) * a2 * a2 * a2);
+    c.c4 = static_cast<float>(a2 * a2 * a2 * a2);
   }
   return c;
 }

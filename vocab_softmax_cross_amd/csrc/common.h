@@ -223,15 +223,17 @@ __device__ __forceinline__ T fresh_args() {
 // Central range |u| <= kCapCentral: tanh(u) / u = 1 + w Q(w), w = u^2, with Q
 // the cubic that minimizes the largest relative error of 1 + w Q(w) on that
 // range (Remez exchange: 0.62 units of 2^-24).  So
-//   l2(x) = x P(w'),  P = log2(e) (1 + w Q(w)) = C0 + C1 w' + C2 w'^2 + C3 w'^3 + w'^4,
-// in the variable w' = a w, a = (log2(e) c3)^(1/4) for Q's cubic coefficient
-// c3, which makes P's leading coefficient exactly 1 (its first Horner step is
-// then w' + C3, one constant: a VALU instruction of this chip reads at most
-// one scalar or literal operand).  w' = (x sqrt(a) / s)^2.  The slope is
-// 1 - t^2 with t = l2(x) / (log2(e) s) (t <= 0.5: nothing cancels).  In fp32
-// on a grid of 2e5 points per cap (caps 1 to 1e3): at most 2.4 units for the
-// capped logit and 2.3 for the slope.  No exp and no reciprocal, which covers
-// most logits for any practical cap.
+//   l2(x) = x P,  P = log2(e) (1 + w Q(w)) = C0 + C1 w' + C2 w'^2 + C3 w'^3 + w'^4,
+// written in the variable w' = a w, a = (log2(e) c3)^(1/4) for Q's cubic
+// coefficient c3 (the constants below), and evaluated in x^2 itself:
+//   P = D0 + D1 x^2 + D2 x^4 + D3 x^6 + D4 x^8,  Di = Ci (a / s^2)^i  (C4 = 1),
+// the Di taken once per launch in fp64 and rounded to fp32, so that an element
+// costs x^2 and four fused multiply-adds (D4, the one constant beside the
+// first step's scalar, sits in a vector register).  The slope is 1 - t^2 with
+// t = l2(x) / (log2(e) s) (t <= 0.5: nothing cancels).  In fp32 (emulated on
+// the host, one rounding per operation) on a grid of 2e5 points per cap, caps
+// 1 to 1e3: at most 2.7 units for the capped logit and 2.9 for the slope.  No
+// exp and no reciprocal, which covers most logits for any practical cap.
 //
 // Outside it, from q = exp(-2 |u|), taken as q4 = 4 q = 2^(-2 |x| log2(e) / s + 2):
 //   s tanh(|u|) = (s - (s / 4) q4) r,   slope = q4 r^2,   r = 1 / (1 + q4 / 4),
@@ -252,22 +254,22 @@ constexpr float kCapC3 = -1.25745797f;
 struct SoftCap {
   float s;      // the cap, > 0
   float k;      // -2 log2(e) / s
-  float sa;     // sqrt(a) / s: w' = (x sa)^2
+  float sa;     // sqrt(a) / s
   float ct;     // 1 / (log2(e) s): t = l2(x) ct
   float x0;     // kCapCentral * s: where the central range ends
   float qs;     // -s / 4
-  // P's coefficients, passed as kernel arguments: each Horner step then reads
-  // one scalar register instead of a constant copied into a vector register.
-  float c0, c1, c2, c3;
+  // P's coefficients D0..D4 in x^2, passed as kernel arguments: each Horner
+  // step then reads one scalar register instead of a constant copied into a
+  // vector register.
+  float c0, c1, c2, c3, c4;
 
   // P(w'(x)) for a central x: l2(x) = x P.
   __device__ __forceinline__ float central_p(float x) const {
-    const float up = x * sa;
-    const float wp = up * up;
-    float q = __builtin_fmaf(up, up, c3);
-    q = __builtin_fmaf(q, wp, c2);
-    q = __builtin_fmaf(q, wp, c1);
-    return __builtin_fmaf(q, wp, c0);
+    const float w = x * x;
+    float q = __builtin_fmaf(w, c4, c3);
+    q = __builtin_fmaf(q, w, c2);
+    q = __builtin_fmaf(q, w, c1);
+    return __builtin_fmaf(q, w, c0);
   }
   // The central range's formulas alone: for |x| <= x0 (a caller that knows
   // every logit it passes lies there; NaN gives NaN).
