@@ -85,11 +85,10 @@ SoftCap soft_cap_constants(float s) {
     constexpr double log2e = 1.4426950408889634;
     c.s = s;
     c.k = static_cast<float>(-2.0 * log2e / s);
-    c.sa = static_cast<float>(kCapSqrtA / s);
     c.ct = static_cast<float>(1.0 / (log2e * s));
     c.x0 = kCapCentral * s;
     c.qs = -0.25f * s;
-    const double a2 = (kCapSqrtA / s) * (kCapSqrtA / s);
+    const double a2 = (kCapSqrtA / s) * (kCapSqrtA / s);  // a / s^2: w' = a2 x^2
     c.c0 = kCapC0;
     c.c1 = static_cast<float>(static_cast<double>(kCapC1) * a2);
     c.c2 = static_cast<float>(static_cast<double>(kCapC2) * a2 * a2);

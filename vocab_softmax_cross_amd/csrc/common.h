@@ -254,7 +254,6 @@ constexpr float kCapC3 = -1.25745797f;
 struct SoftCap {
   float s;      // the cap, > 0
   float k;      // -2 log2(e) / s
-  float sa;     // sqrt(a) / s
   float ct;     // 1 / (log2(e) s): t = l2(x) ct
   float x0;     // kCapCentral * s: where the central range ends
   float qs;     // -s / 4
@@ -263,7 +262,7 @@ struct SoftCap {
   // vector register.
   float c0, c1, c2, c3, c4;
 
-  // P(w'(x)) for a central x: l2(x) = x P.
+  // P for a central x, as a polynomial in x^2: l2(x) = x P.
   __device__ __forceinline__ float central_p(float x) const {
     const float w = x * x;
     float q = __builtin_fmaf(w, c4, c3);
