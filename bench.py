@@ -362,6 +362,47 @@ def flce_mode(L, W, hip, dev, stream, K, sample_rows=0):
     return res, sample
 
 
+def graph_steps(L, wl, ring, refill, problems, outs, ws, go, dt, dev, K, Wu):
+    """The headline step captured in a HIP graph: K fused steps (forward in
+    place + grad_output scale), each on its own ring buffer, recorded once
+    through torch's graph capture and replayed after the ring is refilled.
+    Reported beside the eager step (the headline): the difference is the
+    host launch overhead between the step's four kernels."""
+    import numpy as np
+    import torch
+
+    n = len(ring)
+
+    def steps(stream, first, count):
+        for i in range(first, first + count):
+            b = ring[i % n]
+            L.ce_forward_fused_inplace(problems[i % n], b.data_ptr(), outs, ws.data_ptr(), stream)
+            L.ce_scale_grad(b.data_ptr(), wl.BT, wl.V, wl.V, dt, go.data_ptr(), 0, 1, stream)
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    refill()
+    with torch.cuda.stream(side):
+        steps(side.cuda_stream, 0, Wu)  # warm-up outside the capture
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps(torch.cuda.current_stream(dev).cuda_stream, 0, K)
+    walls = []
+    for _ in range(3):
+        refill()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+    del graph
+    wall = float(np.median(walls))
+    return {"steps_per_graph": K, "ms_per_step": round(wall / K * 1e3, 4),
+            "rows_per_s": round(wl.BT * K / wall, 1),
+            "replays_ms_per_step": [round(w / K * 1e3, 4) for w in walls]}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -504,6 +545,8 @@ def main():
     if not args.no_extra_modes:
         go37 = torch.full((1,), 0.37, dtype=torch.float32, device=dev)
         w37 = timed(fused_step, go37)
+        extra["fused_graph"] = graph_steps(L, wl, ring, refill, problems, outs, ws, go_one, dt,
+                                           dev, K, Wu)
         wsp = timed(split_step, go_one)
         # the scale pass reads and writes every row
         extra["fused_go0.37"] = {"ms_per_step": round(w37 / K * 1e3, 4),
