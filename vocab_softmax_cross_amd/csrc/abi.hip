@@ -88,12 +88,11 @@ SoftCap soft_cap_constants(float s) {
     c.ct = static_cast<float>(1.0 / (log2e * s));
     c.x0 = kCapCentral * s;
     c.qs = -0.25f * s;
-    const double a2 = (kCapSqrtA / s) * (kCapSqrtA / s);  // a / s^2: w' = a2 x^2
-    c.c0 = kCapC0;
-    c.c1 = static_cast<float>(static_cast<double>(kCapC1) * a2);
-    c.c2 = static_cast<float>(static_cast<double>(kCapC2) * a2 * a2);
-    c.c3 = static_cast<float>(static_cast<double>(kCapC3) * a2 * a2 * a2);
-    c.c4 = static_cast<float>(a2 * a2 * a2 * a2);
+    const double is2 = 1.0 / (static_cast<double>(s) * s);  // 1 / s^2
+    c.c0 = static_cast<float>(kCapP0);
+    c.c1 = static_cast<float>(kCapP1 * is2);
+    c.c2 = static_cast<float>(kCapP2 * is2 * is2);
+    c.c3 = static_cast<float>(kCapP3 * is2 * is2 * is2);
   }
   return c;
 }

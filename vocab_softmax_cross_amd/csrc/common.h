@@ -221,19 +221,17 @@ __device__ __forceinline__ T fresh_args() {
 // since every use is an exponent of 2 (or a sum that is scaled back once).
 //
 // Central range |u| <= kCapCentral: tanh(u) / u = 1 + w Q(w), w = u^2, with Q
-// the cubic that minimizes the largest relative error of 1 + w Q(w) on that
-// range (Remez exchange: 0.62 units of 2^-24).  So
-//   l2(x) = x P,  P = log2(e) (1 + w Q(w)) = C0 + C1 w' + C2 w'^2 + C3 w'^3 + w'^4,
-// written in the variable w' = a w, a = (log2(e) c3)^(1/4) for Q's cubic
-// coefficient c3 (the constants below), and evaluated in x^2 itself:
-//   P = D0 + D1 x^2 + D2 x^4 + D3 x^6 + D4 x^8,  Di = Ci (a / s^2)^i  (C4 = 1),
+// the quadratic that minimizes the largest relative error of 1 + w Q(w) on
+// that range (Remez exchange: 0.68 units of 2^-24).  So
+//   l2(x) = x P,  P = log2(e) (1 + w Q(w)) = P0 + P1 w + P2 w^2 + P3 w^3
+// (the constants below), evaluated in x^2 itself:
+//   P = D0 + D1 x^2 + D2 x^4 + D3 x^6,  Di = Pi / s^(2i),
 // the Di taken once per launch in fp64 and rounded to fp32, so that an element
-// costs x^2 and four fused multiply-adds (D4, the one constant beside the
-// first step's scalar, sits in a vector register).  The slope is 1 - t^2 with
-// t = l2(x) / (log2(e) s) (t <= 0.5: nothing cancels).  In fp32 (emulated on
+// costs x^2 and three fused multiply-adds.  The slope is 1 - t^2 with
+// t = l2(x) / (log2(e) s) (t <= 0.34: nothing cancels).  In fp32 (emulated on
 // the host, one rounding per operation) on a grid of 2e5 points per cap, caps
-// 1 to 1e3: at most 2.7 units for the capped logit and 2.9 for the slope.  No
-// exp and no reciprocal, which covers most logits for any practical cap.
+// 1 to 1e3: at most 2.6 units for the capped logit and 1.3 for the slope.  No
+// exp and no reciprocal; at a cap of 30 the range holds every |x| <= 10.5.
 //
 // Outside it, from q = exp(-2 |u|), taken as q4 = 4 q = 2^(-2 |x| log2(e) / s + 2):
 //   s tanh(|u|) = (s - (s / 4) q4) r,   slope = q4 r^2,   r = 1 / (1 + q4 / 4),
@@ -244,12 +242,11 @@ __device__ __forceinline__ T fresh_args() {
 // l2(x) and central_l2(x) give the same bits for a central x, so the
 // statistics pass and the gradient pass see the same capped logits whichever
 // form each takes.  A NaN logit stays NaN; +-inf caps to +-s with slope 0.
-constexpr float kCapCentral = 0.55f;
-constexpr double kCapSqrtA = 0.62643577936533333060;  // sqrt(a)
-constexpr float kCapC0 = 1.44269502f;                  // log2(e)
-constexpr float kCapC1 = -1.22544873f;
-constexpr float kCapC2 = 1.2479471f;
-constexpr float kCapC3 = -1.25745797f;
+constexpr float kCapCentral = 0.35f;
+constexpr double kCapP0 = 1.4426950408889634;     // log2(e)
+constexpr double kCapP1 = -0.48088867846443684;
+constexpr double kCapP2 = 0.19187592127303182;
+constexpr double kCapP3 = -0.07090630044946303;
 
 struct SoftCap {
   float s;      // the cap, > 0
@@ -257,18 +254,16 @@ struct SoftCap {
   float ct;     // 1 / (log2(e) s): t = l2(x) ct
   float x0;     // kCapCentral * s: where the central range ends
   float qs;     // -s / 4
-  // P's coefficients D0..D4 in x^2, passed as kernel arguments: each Horner
+  // P's coefficients D0..D3 in x^2, passed as kernel arguments: each Horner
   // step then reads one scalar register instead of a constant copied into a
   // vector register.
-  float c0, c1, c2, c3, c4;
+  float c0, c1, c2, c3;
 
   // P for a central x, as a polynomial in x^2: l2(x) = x P.
   __device__ __forceinline__ float central_p(float x) const {
     const float w = x * x;
-    float q = __builtin_fmaf(w, c4, c3);
-    q = __builtin_fmaf(q, w, c2);
-    q = __builtin_fmaf(q, w, c1);
-    return __builtin_fmaf(q, w, c0);
+    const float q = __builtin_fmaf(w, c3, c2);
+    return __builtin_fmaf(__builtin_fmaf(q, w, c1), w, c0);
   }
   // The central range's formulas alone: for |x| <= x0 (a caller that knows
   // every logit it passes lies there; NaN gives NaN).
