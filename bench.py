@@ -545,8 +545,12 @@ def main():
     if not args.no_extra_modes:
         go37 = torch.full((1,), 0.37, dtype=torch.float32, device=dev)
         w37 = timed(fused_step, go37)
-        extra["fused_graph"] = graph_steps(L, wl, ring, refill, problems, outs, ws, go_one, dt,
-                                           dev, K, Wu)
+        try:  # a context mode: a capture failure is reported, not fatal to the line
+            extra["fused_graph"] = graph_steps(L, wl, ring, refill, problems, outs, ws, go_one,
+                                               dt, dev, K, Wu)
+        except RuntimeError as e:
+            torch.cuda.synchronize()
+            extra["fused_graph"] = {"error": str(e)[:200]}
         wsp = timed(split_step, go_one)
         # the scale pass reads and writes every row
         extra["fused_go0.37"] = {"ms_per_step": round(w37 / K * 1e3, 4),
