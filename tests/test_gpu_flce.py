@@ -13,7 +13,8 @@ The chain of checks:
   (the cross-entropy tests' bars), the gradient products against fp64
   products of the bf16 G;
 * end to end against oracle.flce (fp64, no intermediate rounding), within the
-  first-order effect of rounding z to bf16;
+  first-order effect of rounding z to bf16, on small problems and at the
+  benchmark's hidden size and vocabulary (H = 4096, V = 128256, 1000 rows);
 * chunked runs against the unchunked one.
 """
 import numpy as np
@@ -295,23 +296,41 @@ def test_flce_end_to_end_against_the_fp64_oracle(softcap, z_loss, reduction):
     bf16 (|dl| <= sum_c |dl/dz_c| |dz_c| <= 2 max_c |dz_c|), the gradients
     within a bound of the same origin."""
     h, W, t, cw = _problem(12, 200, 512, 2048, weighted=True)
-    eps = 0.05
     _note(f"flce end to end softcap={softcap} z_loss={z_loss} red={reduction}")
+    go = torch.linspace(0.5, 1.5, 200, device=h.device) if reduction == "none" else \
+        torch.tensor(0.7, device=h.device)
+    _end_to_end(h, W, t, cw, 0.05, reduction, softcap, z_loss, go)
+
+
+def test_flce_at_the_full_hidden_size_and_vocabulary():
+    """The FLCE at the hidden size and vocabulary of the pages' FLCE benchmark
+    (H = 4096, V = 128256, bf16; Liger-Kernel PR #1622, host-blocking table),
+    on 1000 rows (three full 256-row tiles and a ragged fourth, 5% ignored),
+    smoothing 0.1, mean, through the same kernels bench.py times: every row
+    loss and every element of dL/dh and dL/dW against the fp64 oracle, within
+    the bounds of the small cases (z's product then runs K = 4096, dh's
+    K = 128256)."""
+    h, W, t, _ = _problem(31, 1000, 4096, 128256, ignore_frac=0.05)
+    _note("flce end to end at H=4096 V=128256, 1000 rows")
+    _end_to_end(h, W, t, None, 0.1, "mean", 0.0, 0.0, torch.tensor(1.0, device=h.device))
+
+
+def _end_to_end(h, W, t, cw, eps, reduction, softcap, z_loss, go):
     dev = h.device
-    go = torch.linspace(0.5, 1.5, 200, device=dev) if reduction == "none" else \
-        torch.tensor(0.7, device=dev)
+    BT, H = h.shape
     out = vf.flce_forward_backward(h, W, torch.from_numpy(t).to(dev),
-                                   torch.from_numpy(cw).to(dev), -100, eps, reduction, softcap,
-                                   z_loss, grad_output=go, row_loss=True, accuracy=True,
-                                   return_z_loss=True)
+                                   None if cw is None else torch.from_numpy(cw).to(dev), -100,
+                                   eps, reduction, softcap, z_loss, grad_output=go,
+                                   row_loss=True, accuracy=True, return_z_loss=True)
     torch.cuda.synchronize()
     h64, W64 = _f64(h), _f64(W)
-    ref = oracle.flce(h64, W64, t, cw.astype(np.float64), -100, eps, reduction,
-                      go.cpu().numpy().astype(np.float64) if reduction == "none" else 0.7,
-                      softcap, z_loss)
+    cw64 = None if cw is None else cw.astype(np.float64)
+    go_host = go.cpu().numpy().astype(np.float64)
+    ref = oracle.flce(h64, W64, t, cw64, -100, eps, reduction,
+                      go_host if reduction == "none" else float(go_host), softcap, z_loss)
     z = ref.logits
-    dz = 0.5 * _ulp_bf16(np.abs(z)) + 512 * U32 * (np.abs(h64) @ np.abs(W64).T)
-    lse_term = 2.0 * z_loss * (np.abs(z).max(axis=1) + np.log(2048.0)) + 2.0
+    dz = 0.5 * _ulp_bf16(np.abs(z)) + H * U32 * (np.abs(h64) @ np.abs(W64).T)
+    lse_term = 2.0 * z_loss * (np.abs(z).max(axis=1) + np.log(float(W.shape[0]))) + 2.0
     row_tol = lse_term * 1.5 * dz.max(axis=1) + 1e-5 * np.abs(ref.ce.row_loss)
     valid = t != -100
     got = out["row_loss"].cpu().numpy().astype(np.float64)
@@ -319,9 +338,8 @@ def test_flce_end_to_end_against_the_fp64_oracle(softcap, z_loss, reduction):
     assert np.all(got[~valid] == 0.0)
     # dL/dh and dL/dW, element by element, within the first-order effect of
     # the bf16 logits and the bf16 G (_grad_bounds).
-    go_rows = go.cpu().numpy().astype(np.float64) if reduction == "none" else np.full(200, 0.7)
-    bh, bw = _grad_bounds(ref, h64, W64, dz, t, cw.astype(np.float64), eps, softcap, z_loss,
-                          go_rows)
+    go_rows = go_host if reduction == "none" else np.full(BT, float(go_host))
+    bh, bw = _grad_bounds(ref, h64, W64, dz, t, cw64, eps, softcap, z_loss, go_rows)
     gh = _f64(out["grad_hidden"])
     gw = out["grad_weight"].cpu().numpy().astype(np.float64)
     eh, ew = np.abs(gh - ref.grad_hidden), np.abs(gw - ref.grad_weight)
